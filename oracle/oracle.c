@@ -1,0 +1,217 @@
+/*
+ * CPU oracle for the IndexCache sparse-attention path -- TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, obviously correct C. Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg load this library; the product path never
+ * does. It shares no code, header or table with the HIP library.
+ *
+ * What it computes (every step is the plain definition, in fp64):
+ *   O0  decoders for OCP fp8 e4m3fn and bf16 bytes;
+ *   O1  lightning-indexer scores     I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[base_t+s,:])
+ *       ("Hy4 IndexCache cross-layer index reuse", Jargon: "Indexer", "DSA");
+ *   O2  top-k selection: the k' = min(k, n_t) positions with the largest
+ *       score, lower position first among equal scores ("Jargon: Top-k
+ *       selection"); a full sort is the library step;
+ *   O3  sparse MLA with a per-head softmax sink over the selected latent rows
+ *       (GitHub issue "rtx6kpro #90", bullets on the learnable per-head sink
+ *       and on the 576-wide MLA row: 512 latent + 64 RoPE), two-pass softmax.
+ * The layer-stack rule (O4: shared layers reuse the index of the last
+ * preceding full layer, issue #90 "Indexer:" bullet) lives in __init__.py.
+ *
+ * Readings where the pages are silent are listed with each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- O0 ---- */
+
+/* OCP 8-bit float E4M3 ("fn" variant): 1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits. Exponent field 0 encodes subnormals m/8 * 2^-6. The
+ * all-ones exponent with all-ones mantissa (0x7F, 0xFF) is NaN; there is no
+ * infinity, so exponent 15 with mantissa 0..6 is an ordinary normal number. */
+double orc_fp8_e4m3fn_to_double(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 3) & 0xF;
+    int m = b & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* bf16 is the upper half of an IEEE binary32. */
+double orc_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+void orc_decode_fp8(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = orc_fp8_e4m3fn_to_double(src[i]);
+}
+
+void orc_decode_bf16(const uint16_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = orc_bf16_to_double(src[i]);
+}
+
+/* ---------------------------------------------------------------- O1 ---- */
+
+/* Indexer scores for T queries.
+ *   q_idx [T, H_I, D_I] fp8, w [T, H_I] fp32, k_idx [rows, D_I] fp8
+ *   query t sees cache rows base[t] .. base[t] + n[t] - 1 (position s is
+ *   sequence-local), out [T, ld] fp64, entries s >= n[t] are left untouched.
+ * Reading: one key vector per cached token, shared by all indexer heads, and a
+ * non-negative weight per (query, head); no further scale factors. */
+void orc_indexer_scores(int32_t T, int32_t H_I, int32_t D_I,
+                        const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                        const int64_t *base, const int32_t *n, double *out, int64_t ld)
+{
+    for (int32_t t = 0; t < T; ++t) {
+        double *qd = (double *)malloc(sizeof(double) * (size_t)H_I * D_I);
+        orc_decode_fp8(q_idx + (int64_t)t * H_I * D_I, qd, (int64_t)H_I * D_I);
+        int32_t nt = n[t];
+#pragma omp parallel for schedule(static)
+        for (int32_t s = 0; s < nt; ++s) {
+            double kd[1024];
+            const uint8_t *krow = k_idx + (base[t] + s) * (int64_t)D_I;
+            for (int32_t d = 0; d < D_I; ++d)
+                kd[d] = orc_fp8_e4m3fn_to_double(krow[d]);
+            double I = 0.0;
+            for (int32_t h = 0; h < H_I; ++h) {
+                double dot = 0.0;
+                for (int32_t d = 0; d < D_I; ++d)
+                    dot += qd[(int64_t)h * D_I + d] * kd[d];
+                if (dot > 0.0)
+                    I += (double)w[(int64_t)t * H_I + h] * dot;
+            }
+            out[(int64_t)t * ld + s] = I;
+        }
+        free(qd);
+    }
+}
+
+/* ---------------------------------------------------------------- O2 ---- */
+
+typedef struct {
+    float score;
+    int32_t pos;
+} orc_cand;
+
+/* larger score first; among equal scores the lower position first */
+static int orc_cmp_rank(const void *pa, const void *pb)
+{
+    const orc_cand *a = (const orc_cand *)pa, *b = (const orc_cand *)pb;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    return (a->pos > b->pos) - (a->pos < b->pos);
+}
+
+static int orc_cmp_i32(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/* Top-k over fp32 scores [T, ld]; query t considers positions 0 .. n[t]-1.
+ * idx [T, k]: the selected positions in ascending order, then -1 padding.
+ * When n[t] <= k every position is kept. Scores are compared as fp32 values,
+ * so -0 and +0 are equal. */
+void orc_topk(int32_t T, const float *scores, int64_t ld, const int32_t *n, int32_t k, int32_t *idx)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        int32_t nt = n[t];
+        int32_t *row = idx + (int64_t)t * k;
+        int32_t keep = nt < k ? nt : k;
+        if (nt <= k) {
+            for (int32_t i = 0; i < k; ++i)
+                row[i] = i < nt ? i : -1;
+            continue;
+        }
+        orc_cand *c = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)nt);
+        for (int32_t s = 0; s < nt; ++s) {
+            c[s].score = scores[(int64_t)t * ld + s];
+            c[s].pos = s;
+        }
+        qsort(c, (size_t)nt, sizeof(orc_cand), orc_cmp_rank);
+        for (int32_t i = 0; i < keep; ++i)
+            row[i] = c[i].pos;
+        qsort(row, (size_t)keep, sizeof(int32_t), orc_cmp_i32);
+        for (int32_t i = keep; i < k; ++i)
+            row[i] = -1;
+        free(c);
+    }
+}
+
+/* ---------------------------------------------------------------- O3 ---- */
+
+/* Sparse MLA with a per-head sink, for T queries and H heads.
+ *   q [T, H, D_qk] bf16, kv [rows, D_qk] bf16 (the latent row; its first D_v
+ *   entries are the value), idx [T, k] sequence-local positions (-1 = empty),
+ *   sink [H] fp32, out [T, H, D_v] fp64.
+ * For each (t, h), over the valid entries j of idx[t]:
+ *   s_j = scale * <q[t,h,:], kv[base_t + idx_j, :]>
+ *   m   = max(sink_h, max_j s_j)
+ *   out = sum_j exp(s_j - m) kv[base_t+idx_j, :D_v] / (exp(sink_h - m) + sum_j exp(s_j - m))
+ * Readings: the sink is a logit in the units of the scaled scores, it only
+ * enlarges the denominator and carries no value; the scale covers the whole
+ * 576-wide dot (latent and RoPE parts); the value is the leading D_v entries of
+ * the same latent row (absorbed-MLA form). An empty selection gives zeros. */
+void orc_sparse_mla(int32_t T, int32_t H, int32_t D_qk, int32_t D_v,
+                    const uint16_t *q, const uint16_t *kv, const int64_t *base,
+                    const int32_t *idx, int32_t k, const float *sink, double scale, double *out)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            const int32_t *row = idx + (int64_t)t * k;
+            double *qd = (double *)malloc(sizeof(double) * (size_t)D_qk);
+            double *s = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+            double *o = out + ((int64_t)t * H + h) * D_v;
+            orc_decode_bf16(q + ((int64_t)t * H + h) * D_qk, qd, D_qk);
+            /* pass 1: scores and their maximum (the sink takes part in it) */
+            double m = (double)sink[h];
+            for (int32_t j = 0; j < k; ++j) {
+                if (row[j] < 0)
+                    continue;
+                const uint16_t *kr = kv + (base[t] + row[j]) * (int64_t)D_qk;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D_qk; ++d)
+                    dot += qd[d] * orc_bf16_to_double(kr[d]);
+                s[j] = scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+            /* pass 2: normalised weighted sum of the value rows */
+            double den = exp((double)sink[h] - m);
+            for (int32_t v = 0; v < D_v; ++v)
+                o[v] = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                if (row[j] < 0)
+                    continue;
+                const uint16_t *kr = kv + (base[t] + row[j]) * (int64_t)D_qk;
+                double p = exp(s[j] - m);
+                den += p;
+                for (int32_t v = 0; v < D_v; ++v)
+                    o[v] += p * orc_bf16_to_double(kr[v]);
+            }
+            for (int32_t v = 0; v < D_v; ++v)
+                o[v] /= den;
+            free(qd);
+            free(s);
+        }
+    }
+}
