@@ -1,0 +1,365 @@
+// C ABI of libic.so: host-side validation, workspace layout and dispatch to
+// the HIP kernels. Semantics of every entry point are documented in ic.h.
+#include "ic.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+#define IC_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ic_status fail(ic_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ic_status ok()
+{
+    g_last_error[0] = '\0';
+    return IC_OK;
+}
+
+ic_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(IC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int32_t kMaxT = 65535;          // grid dimension limit for the query axis
+constexpr int64_t kMaxN = (int64_t)1 << 30;
+
+ic_status check_queries(const ic_queries *qs)
+{
+    if (!qs)
+        return fail(IC_ERR_NULL, "queries descriptor is NULL");
+    if (qs->T < 0 || qs->T > kMaxT)
+        return fail(IC_ERR_SHAPE, "T=%d outside [0, %d]", qs->T, kMaxT);
+    if (qs->T > 0 && (!qs->base || !qs->n_valid))
+        return fail(IC_ERR_NULL, "queries base/n_valid is NULL");
+    if (qs->max_n < 0 || qs->max_n > kMaxN)
+        return fail(IC_ERR_SHAPE, "max_n=%lld outside [0, 2^30]", (long long)qs->max_n);
+    if (qs->rows < 0)
+        return fail(IC_ERR_SHAPE, "rows=%lld is negative", (long long)qs->rows);
+    if (qs->max_n > qs->rows && qs->T > 0)
+        return fail(IC_ERR_SHAPE, "max_n=%lld exceeds rows=%lld", (long long)qs->max_n, (long long)qs->rows);
+    if (qs->T > 0 && (!aligned16(qs->base) || !aligned16(qs->n_valid)))
+        return fail(IC_ERR_ALIGN, "queries base/n_valid not 16-byte aligned");
+    return IC_OK;
+}
+
+ic_status check_indexer(const uint8_t *q_idx, const float *w, const uint8_t *k_idx, const ic_queries *qs,
+                        int32_t H_I, int32_t D_I, const float *scores, int64_t ld)
+{
+    if (ic_status s = check_queries(qs))
+        return s;
+    if (qs->T == 0)
+        return IC_OK;
+    if (!q_idx || !w || !k_idx || !scores)
+        return fail(IC_ERR_NULL, "indexer: q_idx, w, k_idx and scores are required");
+    if (H_I < 1 || H_I > 64)
+        return fail(IC_ERR_UNSUPPORTED, "indexer: H_I=%d outside [1, 64]", H_I);
+    if (D_I != 32 && D_I != 64 && D_I != 128)
+        return fail(IC_ERR_UNSUPPORTED, "indexer: D_I=%d not in {32, 64, 128}", D_I);
+    if (ld < qs->max_n || ld % 4 != 0)
+        return fail(IC_ERR_SHAPE, "indexer: ld=%lld must be >= max_n=%lld and a multiple of 4", (long long)ld,
+                    (long long)qs->max_n);
+    if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(scores))
+        return fail(IC_ERR_ALIGN, "indexer: device pointers must be 16-byte aligned");
+    return IC_OK;
+}
+
+ic_status check_topk(const float *scores, int64_t ld, const ic_queries *qs, int32_t k, const int32_t *idx,
+                     const void *ws, size_t ws_bytes)
+{
+    if (ic_status s = check_queries(qs))
+        return s;
+    if (k < 1 || k > (1 << 20))
+        return fail(IC_ERR_SHAPE, "topk: k=%d outside [1, 2^20]", k);
+    if (qs->T == 0)
+        return IC_OK;
+    if (!scores || !idx)
+        return fail(IC_ERR_NULL, "topk: scores and idx are required");
+    if (ld < qs->max_n || ld % 4 != 0)
+        return fail(IC_ERR_SHAPE, "topk: ld=%lld must be >= max_n and a multiple of 4", (long long)ld);
+    if (!aligned16(scores) || !aligned16(idx))
+        return fail(IC_ERR_ALIGN, "topk: device pointers must be 16-byte aligned");
+    const size_t need = ic::topk_workspace_bytes(qs->T, qs->max_n, k);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(IC_ERR_WORKSPACE, "topk: workspace of %zu bytes required, %zu given", need, ws_bytes);
+    if (need > 0 && !aligned16(ws))
+        return fail(IC_ERR_ALIGN, "topk: workspace not 16-byte aligned");
+    return IC_OK;
+}
+
+ic_status check_dims_mla(const ic_dims *d)
+{
+    if (!d)
+        return fail(IC_ERR_NULL, "dims descriptor is NULL");
+    if (d->k < 1 || d->k > (1 << 20))
+        return fail(IC_ERR_SHAPE, "k=%d outside [1, 2^20]", d->k);
+    if (d->H < 1 || d->H > 4096)
+        return fail(IC_ERR_SHAPE, "H=%d outside [1, 4096]", d->H);
+    if (!ic::sparse_mla_supported(d->D_qk, d->D_v))
+        return fail(IC_ERR_UNSUPPORTED, "sparse MLA: (D_qk, D_v)=(%d, %d) not built; built: (576, 512), (80, 64)",
+                    d->D_qk, d->D_v);
+    if (d->out_dtype != IC_OUT_BF16 && d->out_dtype != IC_OUT_F32)
+        return fail(IC_ERR_SHAPE, "out_dtype=%d unknown", d->out_dtype);
+    return IC_OK;
+}
+
+ic_status check_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs, const int32_t *idx,
+                    const float *sink, const ic_dims *d, const void *out, const void *ws, size_t ws_bytes)
+{
+    if (ic_status s = check_queries(qs))
+        return s;
+    if (ic_status s = check_dims_mla(d))
+        return s;
+    if (qs->T == 0)
+        return IC_OK;
+    if (!q || !kv || !idx || !sink || !out)
+        return fail(IC_ERR_NULL, "sparse MLA: q, kv, idx, sink and out are required");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(idx) || !aligned16(sink) || !aligned16(out))
+        return fail(IC_ERR_ALIGN, "sparse MLA: device pointers must be 16-byte aligned");
+    const ic::MlaPlan plan = ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v);
+    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
+        return fail(IC_ERR_WORKSPACE, "sparse MLA: workspace of %zu bytes required, %zu given", plan.ws_bytes,
+                    ws_bytes);
+    if (plan.ws_bytes > 0 && !aligned16(ws))
+        return fail(IC_ERR_ALIGN, "sparse MLA: workspace not 16-byte aligned");
+    return IC_OK;
+}
+
+ic_status check_reuse_map(int32_t n_layers, const int32_t *m)
+{
+    if (n_layers < 1)
+        return fail(IC_ERR_SHAPE, "n_layers=%d must be >= 1", n_layers);
+    if (!m)
+        return fail(IC_ERR_NULL, "reuse_map is NULL");
+    if (m[0] != 0)
+        return fail(IC_ERR_REUSE_MAP, "layer 0 must be a full layer (reuse_map[0]=%d)", m[0]);
+    for (int32_t l = 1; l < n_layers; ++l) {
+        const int32_t s = m[l];
+        if (s == l)
+            continue;
+        if (s < 0 || s > l)
+            return fail(IC_ERR_REUSE_MAP, "layer %d: source %d is not an earlier layer", l, s);
+        if (m[s] != s)
+            return fail(IC_ERR_REUSE_MAP, "layer %d: source %d is itself a shared layer", l, s);
+    }
+    return IC_OK;
+}
+
+int64_t score_ld(const ic_queries *qs) { return (int64_t)round_up((size_t)(qs->max_n > 0 ? qs->max_n : 1), 4); }
+
+// layer-stack workspace: [scores][top-k][sparse MLA], each 256-byte aligned
+struct StackLayout {
+    size_t scores_off, topk_off, mla_off, total;
+    int64_t ld;
+};
+
+StackLayout stack_layout(const ic_queries *qs, const ic_dims *d)
+{
+    StackLayout L;
+    L.ld = score_ld(qs);
+    L.scores_off = 0;
+    L.topk_off = round_up((size_t)qs->T * L.ld * sizeof(float), 256);
+    L.mla_off = L.topk_off + round_up(ic::topk_workspace_bytes(qs->T, qs->max_n, d->k), 256);
+    L.total = L.mla_off + round_up(ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v).ws_bytes, 256);
+    return L;
+}
+
+}  // namespace
+
+IC_EXPORT const char *ic_status_str(ic_status s)
+{
+    switch (s) {
+    case IC_OK: return "IC_OK";
+    case IC_ERR_NULL: return "IC_ERR_NULL";
+    case IC_ERR_SHAPE: return "IC_ERR_SHAPE";
+    case IC_ERR_UNSUPPORTED: return "IC_ERR_UNSUPPORTED";
+    case IC_ERR_ALIGN: return "IC_ERR_ALIGN";
+    case IC_ERR_WORKSPACE: return "IC_ERR_WORKSPACE";
+    case IC_ERR_REUSE_MAP: return "IC_ERR_REUSE_MAP";
+    case IC_ERR_HIP: return "IC_ERR_HIP";
+    default: return "IC_ERR_UNKNOWN";
+    }
+}
+
+IC_EXPORT const char *ic_last_error(void) { return g_last_error; }
+
+IC_EXPORT ic_status ic_indexer_score(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                     const ic_queries *qs, int32_t H_I, int32_t D_I, float *scores, int64_t ld,
+                                     void *stream)
+{
+    if (ic_status s = check_indexer(q_idx, w, k_idx, qs, H_I, D_I, scores, ld))
+        return s;
+    if (qs->T == 0 || qs->max_n == 0)
+        return ok();
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return hip_status(ic::launch_indexer_decode(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I,
+                                                D_I, scores, ld, st),
+                      "indexer launch");
+}
+
+IC_EXPORT size_t ic_topk_workspace_size(const ic_queries *qs, int32_t k)
+{
+    if (!qs || qs->T < 0)
+        return 0;
+    return ic::topk_workspace_bytes(qs->T, qs->max_n, k);
+}
+
+IC_EXPORT ic_status ic_topk(const float *scores, int64_t ld, const ic_queries *qs, int32_t k, int32_t *idx,
+                            void *ws, size_t ws_bytes, void *stream)
+{
+    if (ic_status s = check_topk(scores, ld, qs, k, idx, ws, ws_bytes))
+        return s;
+    if (qs->T == 0)
+        return ok();
+    return hip_status(ic::launch_topk(scores, ld, qs->n_valid, qs->T, qs->max_n, k, idx, ws,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                      "top-k launch");
+}
+
+IC_EXPORT size_t ic_sparse_mla_workspace_size(const ic_queries *qs, const ic_dims *d)
+{
+    if (!qs || !d || qs->T < 0 || d->H < 1 || d->k < 1)
+        return 0;
+    return ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v).ws_bytes;
+}
+
+IC_EXPORT ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs, const int32_t *idx,
+                                  const float *sink, float scale, const ic_dims *d, void *out, void *ws,
+                                  size_t ws_bytes, void *stream)
+{
+    if (ic_status s = check_mla(q, kv, qs, idx, sink, d, out, ws, ws_bytes))
+        return s;
+    if (qs->T == 0)
+        return ok();
+    const ic::MlaPlan plan = ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v);
+    return hip_status(ic::launch_sparse_mla(q, kv, qs->base, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, sink, scale,
+                                            out, d->out_dtype == IC_OUT_F32, plan, ws,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                      "sparse MLA launch");
+}
+
+IC_EXPORT ic_status ic_reuse_map_last_full(int32_t n_layers, const uint8_t *is_full, int32_t *reuse_map)
+{
+    if (n_layers < 1)
+        return fail(IC_ERR_SHAPE, "n_layers=%d must be >= 1", n_layers);
+    if (!is_full || !reuse_map)
+        return fail(IC_ERR_NULL, "is_full and reuse_map are required");
+    if (!is_full[0])
+        return fail(IC_ERR_REUSE_MAP, "layer 0 must be a full layer");
+    int32_t last = 0;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (is_full[l])
+            last = l;
+        reuse_map[l] = last;
+    }
+    return ok();
+}
+
+IC_EXPORT size_t ic_layer_stack_workspace_size(const ic_queries *qs, const ic_dims *d)
+{
+    if (!qs || !d || qs->T < 0 || d->H < 1 || d->k < 1 || qs->max_n < 0)
+        return 0;
+    return stack_layout(qs, d).total;
+}
+
+IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, const int32_t *reuse_map,
+                                   const ic_queries *qs, const ic_dims *d, float scale, int32_t *index_cache,
+                                   int32_t *indexer_passes, void *ws, size_t ws_bytes, void *stream)
+{
+    if (ic_status s = check_reuse_map(n_layers, reuse_map))
+        return s;
+    if (!layers)
+        return fail(IC_ERR_NULL, "layers is NULL");
+    if (ic_status s = check_queries(qs))
+        return s;
+    if (ic_status s = check_dims_mla(d))
+        return s;
+    int32_t n_full = 0;
+    for (int32_t l = 0; l < n_layers; ++l)
+        n_full += reuse_map[l] == l;
+    if (qs->T > 0) {
+        if (!index_cache)
+            return fail(IC_ERR_NULL, "index_cache is NULL");
+        if (!aligned16(index_cache))
+            return fail(IC_ERR_ALIGN, "index_cache not 16-byte aligned");
+        const StackLayout L = stack_layout(qs, d);
+        if (!ws || ws_bytes < L.total)
+            return fail(IC_ERR_WORKSPACE, "layer stack: workspace of %zu bytes required, %zu given", L.total,
+                        ws_bytes);
+        if (!aligned16(ws))
+            return fail(IC_ERR_ALIGN, "layer stack: workspace not 16-byte aligned");
+        for (int32_t l = 0; l < n_layers; ++l) {
+            const ic_layer &y = layers[l];
+            if (reuse_map[l] == l) {
+                if (ic_status s = check_indexer(y.q_idx, y.w, y.k_idx, qs, d->H_I, d->D_I,
+                                                reinterpret_cast<float *>(ws), L.ld)) {
+                    char msg[512];
+                    snprintf(msg, sizeof msg, "%s", g_last_error);
+                    return fail(s, "layer %d: %s", l, msg);
+                }
+            }
+            if (ic_status s = check_mla(y.q, y.kv, qs, index_cache, y.sink, d, y.out,
+                                        static_cast<char *>(ws) + L.mla_off, ws_bytes - L.mla_off)) {
+                char msg[512];
+                snprintf(msg, sizeof msg, "%s", g_last_error);
+                return fail(s, "layer %d: %s", l, msg);
+            }
+        }
+    }
+    if (indexer_passes)
+        *indexer_passes = n_full;
+    if (qs->T == 0)
+        return ok();
+
+    const StackLayout L = stack_layout(qs, d);
+    float *scores = reinterpret_cast<float *>(static_cast<char *>(ws) + L.scores_off);
+    void *topk_ws = static_cast<char *>(ws) + L.topk_off;
+    void *mla_ws = static_cast<char *>(ws) + L.mla_off;
+    const ic::MlaPlan plan = ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    std::vector<int32_t> slot(n_layers, -1);
+    int32_t next_slot = 0;
+    const size_t slot_elems = (size_t)qs->T * d->k;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const ic_layer &y = layers[l];
+        if (reuse_map[l] == l) {
+            slot[l] = next_slot++;
+            int32_t *idx = index_cache + slot[l] * slot_elems;
+            if (qs->max_n > 0) {
+                hipError_t e = ic::launch_indexer_decode(y.q_idx, y.w, y.k_idx, qs->base, qs->n_valid, qs->T,
+                                                         qs->max_n, d->H_I, d->D_I, scores, L.ld, st);
+                if (e != hipSuccess)
+                    return hip_status(e, "layer stack: indexer launch");
+            }
+            hipError_t e = ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx, topk_ws, st);
+            if (e != hipSuccess)
+                return hip_status(e, "layer stack: top-k launch");
+        }
+        const int32_t *idx = index_cache + slot[reuse_map[l]] * slot_elems;
+        hipError_t e = ic::launch_sparse_mla(y.q, y.kv, qs->base, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, y.sink,
+                                             scale, y.out, d->out_dtype == IC_OUT_F32, plan, mla_ws, st);
+        if (e != hipSuccess)
+            return hip_status(e, "layer stack: sparse MLA launch");
+    }
+    return ok();
+}

@@ -1,0 +1,43 @@
+// Internal launch interface between the C-ABI layer (ic_api.cpp) and the HIP
+// kernels. Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ic {
+
+// ---- indexer --------------------------------------------------------------
+// Decode form: each query streams its own key rows (no reuse across queries).
+hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                 const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                 int32_t H_I, int32_t D_I, float *scores, int64_t ld,
+                                 hipStream_t stream);
+// Prefill form: all queries read one sequence; key tiles are shared by a
+// group of queries through LDS.
+hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                  const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                  int32_t H_I, int32_t D_I, float *scores, int64_t ld,
+                                  hipStream_t stream);
+bool indexer_prefill_supported(int32_t H_I, int32_t D_I);
+
+// ---- top-k ------------------------------------------------------------------
+size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t k);
+hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
+                       int32_t k, int32_t *idx, void *ws, hipStream_t stream);
+
+// ---- sparse MLA -----------------------------------------------------------
+struct MlaPlan {
+    int32_t splits;          // k-splits per (query, head group)
+    int32_t rows_per_split;  // multiple of the row tile
+    size_t ws_bytes;         // partial results when splits > 1
+};
+bool sparse_mla_supported(int32_t D_qk, int32_t D_v);
+MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v);
+hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_t *base,
+                             const int32_t *idx, int32_t T, int32_t H, int32_t k, int32_t D_qk,
+                             int32_t D_v, const float *sink, float scale, void *out, int32_t out_f32,
+                             const MlaPlan &plan, void *ws, hipStream_t stream);
+
+}  // namespace ic

@@ -1,0 +1,244 @@
+"""ctypes binding of libic.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module turns
+torch tensors into pointers, fills the descriptor structs and passes torch's
+current HIP stream. Importing it loads the library and fails loudly when it
+is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libic.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run `python -m cross_layer_index_amd.build` "
+                      "(or __graft_entry__.build()) first")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+IC_OK, IC_ERR_NULL, IC_ERR_SHAPE, IC_ERR_UNSUPPORTED, IC_ERR_ALIGN, IC_ERR_WORKSPACE, IC_ERR_REUSE_MAP, \
+    IC_ERR_HIP = range(8)
+IC_OUT_BF16, IC_OUT_F32 = 0, 1
+
+_P = ctypes.c_void_p
+_i32, _i64, _sz, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+
+class ic_queries(ctypes.Structure):
+    _fields_ = [("base", _P), ("n_valid", _P), ("T", _i32), ("same_seq", _i32), ("max_n", _i64),
+                ("rows", _i64)]
+
+
+class ic_dims(ctypes.Structure):
+    _fields_ = [("H_I", _i32), ("D_I", _i32), ("k", _i32), ("H", _i32), ("D_qk", _i32), ("D_v", _i32),
+                ("out_dtype", _i32)]
+
+
+class ic_layer(ctypes.Structure):
+    _fields_ = [("q_idx", _P), ("w", _P), ("k_idx", _P), ("q", _P), ("kv", _P), ("sink", _P), ("out", _P)]
+
+
+_QP, _DP = ctypes.POINTER(ic_queries), ctypes.POINTER(ic_dims)
+_SIGS = {
+    "ic_indexer_score": ([_P, _P, _P, _QP, _i32, _i32, _P, _i64, _P], _i32),
+    "ic_topk_workspace_size": ([_QP, _i32], _sz),
+    "ic_topk": ([_P, _i64, _QP, _i32, _P, _P, _sz, _P], _i32),
+    "ic_sparse_mla_workspace_size": ([_QP, _DP], _sz),
+    "ic_sparse_mla": ([_P, _P, _QP, _P, _P, _f32, _DP, _P, _P, _sz, _P], _i32),
+    "ic_reuse_map_last_full": ([_i32, _P, _P], _i32),
+    "ic_layer_stack_workspace_size": ([_QP, _DP], _sz),
+    "ic_layer_stack": ([_i32, ctypes.POINTER(ic_layer), _P, _QP, _DP, _f32, _P, ctypes.POINTER(_i32), _P, _sz,
+                        _P], _i32),
+    "ic_status_str": ([_i32], ctypes.c_char_p),
+    "ic_last_error": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class ICError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_lib.ic_status_str(status).decode()}: {detail}")
+
+
+def _check(status: int):
+    if status != IC_OK:
+        raise ICError(status, _lib.ic_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+@dataclass
+class Queries:
+    """Which cache rows each query sees (see ic_queries in include/ic.h)."""
+    base: torch.Tensor      # int64 [T] on device
+    n_valid: torch.Tensor   # int32 [T] on device
+    max_n: int
+    rows: int
+    same_seq: bool = False
+
+    @property
+    def T(self) -> int:
+        return int(self.n_valid.numel())
+
+    def c(self) -> ic_queries:
+        _dev(self.base, torch.int64, "base")
+        _dev(self.n_valid, torch.int32, "n_valid")
+        return ic_queries(_ptr(self.base), _ptr(self.n_valid), self.T, int(self.same_seq), int(self.max_n),
+                          int(self.rows))
+
+
+def make_queries(base: torch.Tensor, n_valid: torch.Tensor, rows: int, same_seq=False, device="cuda") -> Queries:
+    nv = n_valid.to(torch.int32)
+    return Queries(base.to(device=device, dtype=torch.int64).contiguous(), nv.to(device).contiguous(),
+                   int(nv.max().item()) if nv.numel() else 0, int(rows), same_seq)
+
+
+def dims(H_I, D_I, k, H, D_qk, D_v, out_f32=False) -> ic_dims:
+    return ic_dims(H_I, D_I, k, H, D_qk, D_v, IC_OUT_F32 if out_f32 else IC_OUT_BF16)
+
+
+def score_ld(max_n: int) -> int:
+    return max(4, (int(max_n) + 3) // 4 * 4)
+
+
+def _u8(t, name):
+    if t is not None and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    return _dev(t, torch.uint8, name)
+
+
+def _bf16(t, name):
+    return _dev(t, torch.bfloat16, name)
+
+
+# ---------------------------------------------------------------- entries --
+def indexer_score(q_idx, w, k_idx, qs: Queries, scores: Optional[torch.Tensor] = None, stream=None):
+    """Indexer scores [T, ld] fp32 (ld = max_n rounded up to 4)."""
+    q_idx, k_idx = _u8(q_idx, "q_idx"), _u8(k_idx, "k_idx")
+    _dev(w, torch.float32, "w")
+    T, H_I, D_I = q_idx.shape
+    if scores is None:
+        scores = torch.empty((T, score_ld(qs.max_n)), dtype=torch.float32, device=q_idx.device)
+    _dev(scores, torch.float32, "scores")
+    qc = qs.c()
+    _check(_lib.ic_indexer_score(_ptr(q_idx), _ptr(w), _ptr(k_idx), ctypes.byref(qc), H_I, D_I, _ptr(scores),
+                                 scores.shape[1], _stream(stream)))
+    return scores
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (the library's counters expect zeros at first use)."""
+    return torch.zeros(max(256, (int(nbytes) + 255) // 256 * 256), dtype=torch.uint8, device=device)
+
+
+def topk(scores, qs: Queries, k: int, idx: Optional[torch.Tensor] = None, ws=None, stream=None):
+    _dev(scores, torch.float32, "scores")
+    qc = qs.c()
+    need = _lib.ic_topk_workspace_size(ctypes.byref(qc), k)
+    if ws is None:
+        ws = workspace(need, scores.device)
+    if idx is None:
+        idx = torch.empty((qs.T, k), dtype=torch.int32, device=scores.device)
+    _dev(idx, torch.int32, "idx")
+    _check(_lib.ic_topk(_ptr(scores), scores.shape[1], ctypes.byref(qc), k, _ptr(idx), _ptr(ws), ws.numel(),
+                        _stream(stream)))
+    return idx
+
+
+def sparse_mla(q, kv, qs: Queries, idx, sink, scale: float, D_v: int, out=None, out_f32=False, ws=None,
+               stream=None):
+    _bf16(q, "q")
+    _bf16(kv, "kv")
+    _dev(idx, torch.int32, "idx")
+    _dev(sink, torch.float32, "sink")
+    T, H, D_qk = q.shape
+    d = dims(0, 0, idx.shape[1], H, D_qk, D_v, out_f32)
+    qc = qs.c()
+    need = _lib.ic_sparse_mla_workspace_size(ctypes.byref(qc), ctypes.byref(d))
+    if ws is None:
+        ws = workspace(need, q.device)
+    if out is None:
+        out = torch.empty((T, H, D_v), dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    _dev(out, torch.float32 if out_f32 else torch.bfloat16, "out")
+    _check(_lib.ic_sparse_mla(_ptr(q), _ptr(kv), ctypes.byref(qc), _ptr(idx), _ptr(sink), float(scale),
+                              ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def reuse_map_last_full(is_full: Sequence[bool]) -> List[int]:
+    n = len(is_full)
+    f = (ctypes.c_uint8 * max(n, 1))(*[1 if x else 0 for x in is_full])
+    m = (ctypes.c_int32 * max(n, 1))()
+    _check(_lib.ic_reuse_map_last_full(n, f, m))
+    return list(m)[:n]
+
+
+class LayerStack:
+    """Holds the host-side descriptors of a layer stack so repeated calls (and
+    HIP-graph capture) marshal nothing."""
+
+    def __init__(self, layers, reuse_map: Sequence[int], qs: Queries, d: ic_dims, scale: float, device="cuda"):
+        self.n = len(layers)
+        self.layers = layers
+        self.qs = qs
+        self.qc = qs.c()
+        self.d = d
+        self.scale = float(scale)
+        self.rmap = (ctypes.c_int32 * self.n)(*reuse_map)
+        arr = (ic_layer * self.n)()
+        for l, y in enumerate(layers):
+            arr[l] = ic_layer(_ptr(_u8(y.get("q_idx"), "q_idx")), _ptr(_dev(y.get("w"), torch.float32, "w")),
+                              _ptr(_u8(y.get("k_idx"), "k_idx")), _ptr(_bf16(y["q"], "q")),
+                              _ptr(_bf16(y["kv"], "kv")), _ptr(_dev(y["sink"], torch.float32, "sink")),
+                              _ptr(y["out"]))
+        self.arr = arr
+        self.n_full = sum(1 for l in range(self.n) if reuse_map[l] == l)
+        self.index_cache = torch.empty((max(self.n_full, 1), qs.T, d.k), dtype=torch.int32, device=device)
+        need = _lib.ic_layer_stack_workspace_size(ctypes.byref(self.qc), ctypes.byref(self.d))
+        self.ws = workspace(need, device)
+        self.passes = _i32(-1)
+
+    def __call__(self, stream=None) -> int:
+        _check(_lib.ic_layer_stack(self.n, self.arr, self.rmap, ctypes.byref(self.qc), ctypes.byref(self.d),
+                                   self.scale, _ptr(self.index_cache), ctypes.byref(self.passes), _ptr(self.ws),
+                                   self.ws.numel(), _stream(stream)))
+        return self.passes.value
+
+
+def layer_stack(layers, reuse_map, qs: Queries, d: ic_dims, scale: float):
+    """One call of ic_layer_stack. ``layers``: list of dicts with keys q_idx, w,
+    k_idx (optional on shared layers), q, kv, sink, out. Returns
+    (index_cache, indexer_passes)."""
+    st = LayerStack(layers, reuse_map, qs, d, scale, device=layers[0]["q"].device)
+    passes = st()
+    return st.index_cache, passes

@@ -1,0 +1,175 @@
+/*
+ * ic.h -- C ABI of libic.so: DeepSeek-style sparse attention with IndexCache
+ * cross-layer index reuse, on MI355X (gfx950).
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *  [E]  explainer "Hy4 IndexCache cross-layer index reuse" (learnaivisually.com):
+ *       FAQ, TL;DR, Jargon ("Sparse index", "Indexer", "Top-k selection",
+ *       "DSA"), the scheme table, and "Where the saving actually lands".
+ *  [G]  GitHub issue "local-inference-lab/rtx6kpro #90": the MLA shape
+ *       (RoPE-64, head 576, top-k 2048; first paragraph), the learnable
+ *       per-head sink bullet, and the "Indexer:" bullet (shared layers reuse
+ *       the last preceding full layer's top-k; 21 full of 78).
+ *  [B]  catalogue record "Bai et al.: IndexCache cross-layer sparse-index
+ *       reuse" (summary and boundary fields).
+ *
+ * Conventions shared by every call
+ *  - All tensors are row-major and contiguous. Device pointers must be 16-byte
+ *    aligned. Element types: indexer q/k are OCP fp8 e4m3fn bytes; head
+ *    weights, scores and sinks are fp32; attention q and the latent KV cache
+ *    are bf16 bit patterns (uint16_t); index lists are int32 (-1 = empty
+ *    slot); cache offsets are int64.
+ *  - Every device buffer, workspace included, is allocated by the caller. The
+ *    library never allocates or frees device memory.
+ *  - Workspaces: zero-fill a workspace once, before its first use with this
+ *    library. Every call that returns IC_OK leaves the workspace's counter
+ *    area zero again, so one workspace can be reused by any sequence of calls
+ *    on one stream. Calls that overlap in time must use distinct workspaces.
+ *  - Every call enqueues kernels on `stream` (a hipStream_t; NULL = default
+ *    stream) and returns without synchronising; no call issues memsets or
+ *    host<->device copies, so calls may be captured into a HIP graph.
+ *  - Errors: arguments are validated on the host before any launch; on a
+ *    validation failure nothing is enqueued and the status says why
+ *    (ic_last_error() gives the detail, per thread). IC_ERR_HIP means a launch
+ *    failed. Faults inside kernels surface at the caller's next synchronisation.
+ *  - Values that live in device memory (n_valid, base, idx) cannot be checked
+ *    on the host. Contract: 0 <= n_valid[t] <= max_n, base[t] >= 0,
+ *    base[t] + n_valid[t] <= rows, and every idx entry is -1 or in
+ *    [0, n_valid[t]).
+ */
+#ifndef IC_H
+#define IC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ic_status;
+enum {
+    IC_OK = 0,
+    IC_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    IC_ERR_SHAPE = 2,       /* sizes are inconsistent or out of range          */
+    IC_ERR_UNSUPPORTED = 3, /* valid, but no kernel is built for this shape    */
+    IC_ERR_ALIGN = 4,       /* a device pointer or stride is misaligned        */
+    IC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
+    IC_ERR_REUSE_MAP = 6,   /* reuse map violates the full/shared rule          */
+    IC_ERR_HIP = 7          /* a HIP launch failed                             */
+};
+
+enum { IC_OUT_BF16 = 0, IC_OUT_F32 = 1 };
+
+/* Which cache rows each query sees. Query t sees the rows
+ * base[t] .. base[t] + n_valid[t] - 1 of the key and latent caches, and
+ * positions are sequence-local: position s means row base[t] + s.
+ * Decode: each query's cache is its own, n_valid[t] = its length.
+ * Causal prefill: all queries read one sequence (same_seq = 1, every base[t]
+ * equal) and n_valid[t] = position_t + 1 (a query sees itself). */
+typedef struct {
+    const int64_t *base;     /* device [T]                                     */
+    const int32_t *n_valid;  /* device [T]                                     */
+    int32_t T;               /* number of queries, >= 0                        */
+    int32_t same_seq;        /* nonzero: every query reads the same rows       */
+    int64_t max_n;           /* host: upper bound of n_valid[t]                */
+    int64_t rows;            /* host: rows in the key and latent caches        */
+} ic_queries;
+
+/* Shapes. Indexer: H_I heads of dim D_I (D_I in {32, 64, 128}, 1 <= H_I <= 64).
+ * Attention: H heads over rows of D_qk bf16 (latent + RoPE); the value is the
+ * leading D_v entries of the same row. Built (D_qk, D_v): (576, 512) -- the
+ * MLA shape of [G] -- and (80, 64). */
+typedef struct {
+    int32_t H_I, D_I;
+    int32_t k;               /* top-k, >= 1                                     */
+    int32_t H, D_qk, D_v;
+    int32_t out_dtype;       /* IC_OUT_BF16 or IC_OUT_F32                       */
+} ic_dims;
+
+/* Lightning-indexer scores ([E] Jargon "Indexer" and "DSA": a cheap pass that
+ * scores every cached position for a query):
+ *   scores[t, s] = sum_h w[t,h] * max(0, sum_d q_idx[t,h,d] * k_idx[base_t+s, d])
+ * for 0 <= s < n_valid[t]; entries s >= n_valid[t] of a row are not written.
+ *   q_idx  [T, H_I, D_I] fp8 e4m3fn     w      [T, H_I] fp32
+ *   k_idx  [rows, D_I]   fp8 e4m3fn     scores [T, ld] fp32, ld >= max_n, ld % 4 == 0
+ * Products accumulate in fp32 on the matrix cores; with integer-valued inputs
+ * whose partial sums stay below 2^24 the result is exact. */
+ic_status ic_indexer_score(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                           const ic_queries *qs, int32_t H_I, int32_t D_I,
+                           float *scores, int64_t ld, void *stream);
+
+/* Top-k selection ([E] Jargon "Top-k selection" and "Sparse index"; k = 2048
+ * in [G]): for each query, the min(k, n_valid[t]) positions s < n_valid[t]
+ * with the largest scores[t, s]; among equal scores the lower position wins,
+ * so exactly one set is correct. idx [T, k] int32 receives the set in
+ * ascending position order followed by -1 padding. Scores are compared as
+ * fp32 values (-0 equals +0); NaN scores are not allowed. */
+size_t ic_topk_workspace_size(const ic_queries *qs, int32_t k);
+ic_status ic_topk(const float *scores, int64_t ld, const ic_queries *qs, int32_t k,
+                  int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Sparse MLA with a per-head softmax sink ([E] Jargon "DSA": each query
+ * attends to its selected tokens only; [G]: 576-wide latent rows, learnable
+ * per-head sink acting as a bias in the softmax denominator). For each query
+ * t and head h, over the valid entries j of idx[t] (-1 entries are skipped):
+ *   s_j = scale * <q[t,h,:], kv[base_t + idx[t,j], :]>
+ *   out[t,h,:] = sum_j e^{s_j} kv[base_t + idx[t,j], :D_v] / (e^{sink_h} + sum_j e^{s_j})
+ *   q   [T, H, D_qk] bf16     kv  [rows, D_qk] bf16     idx [T, k] int32
+ *   sink [H] fp32 (a logit in the units of the scaled scores)
+ *   out [T, H, D_v] bf16 (round to nearest even) or fp32, per dims->out_dtype.
+ * An all-empty selection gives zeros. QK^T and PV run on bf16 matrix cores
+ * with fp32 accumulation and an fp32 online softmax; P is rounded to bf16. */
+size_t ic_sparse_mla_workspace_size(const ic_queries *qs, const ic_dims *d);
+ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs,
+                        const int32_t *idx, const float *sink, float scale, const ic_dims *d,
+                        void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* One attention layer's tensors for ic_layer_stack. q_idx, w and k_idx are
+ * read only on full layers and may be NULL on shared ones. */
+typedef struct {
+    const uint8_t *q_idx;
+    const float *w;
+    const uint8_t *k_idx;
+    const uint16_t *q;
+    const uint16_t *kv;
+    const float *sink;
+    void *out;
+} ic_layer;
+
+/* IndexCache reuse map ([G] "Indexer:" bullet; [E] FAQ and TL;DR: the index
+ * is computed once and later layers read it): reuse_map[l] = l when is_full[l]
+ * is nonzero, else the last full layer before l. Host arrays of n_layers
+ * entries. IC_ERR_REUSE_MAP when layer 0 is not full. */
+ic_status ic_reuse_map_last_full(int32_t n_layers, const uint8_t *is_full, int32_t *reuse_map);
+
+/* Layer stack ([E] "Where the saving actually lands": the per-layer indexer
+ * pass is what IndexCache removes; [G] "Indexer:" bullet). For l = 0..n_layers-1:
+ *   full layer   (reuse_map[l] == l): indexer -> top-k, stored in index_cache
+ *                slot = rank of l among the full layers;
+ *   shared layer (reuse_map[l] <  l): reads the slot of layer reuse_map[l],
+ *                which must be a full layer;
+ *   every layer: sparse MLA with its own q, kv, sink over that index into
+ *                layers[l].out.
+ *   layers      host [n_layers]        reuse_map host [n_layers]
+ *   index_cache device [n_full, T, k] int32 (kept: the caller may read it)
+ *   indexer_passes (host, may be NULL): receives the number of full layers.
+ * Validation of the map: reuse_map[0] == 0, and for l > 0 either
+ * reuse_map[l] == l or reuse_map[l] < l with reuse_map[reuse_map[l]] equal to
+ * reuse_map[l]. */
+size_t ic_layer_stack_workspace_size(const ic_queries *qs, const ic_dims *d);
+ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, const int32_t *reuse_map,
+                         const ic_queries *qs, const ic_dims *d, float scale,
+                         int32_t *index_cache, int32_t *indexer_passes,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status, and the detail of the last failure on the
+ * calling thread (empty string if none). Both return static storage. */
+const char *ic_status_str(ic_status s);
+const char *ic_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IC_H */

@@ -18,3 +18,19 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # name the case on the raw stream before it runs, so a run that dies
+    # inside a GPU call still says which case it was in
+    sys.__stderr__.write(f"[case] {nodeid}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device (run them with -m gpu on an MI355X)")
+    from cross_layer_index_amd import ic
+    return ic

