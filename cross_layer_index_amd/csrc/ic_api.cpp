@@ -213,7 +213,7 @@ IC_EXPORT ic_status ic_indexer_score(const uint8_t *q_idx, const float *w, const
         return ok();
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     return hip_status(ic::launch_indexer_decode(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I,
-                                                D_I, scores, ld, st),
+                                                D_I, scores, ld, nullptr, st),
                       "indexer launch");
 }
 
@@ -231,7 +231,7 @@ IC_EXPORT ic_status ic_topk(const float *scores, int64_t ld, const ic_queries *q
         return s;
     if (qs->T == 0)
         return ok();
-    return hip_status(ic::launch_topk(scores, ld, qs->n_valid, qs->T, qs->max_n, k, idx, ws,
+    return hip_status(ic::launch_topk(scores, ld, qs->n_valid, qs->T, qs->max_n, k, idx, ws, false,
                                       reinterpret_cast<hipStream_t>(stream)),
                       "top-k launch");
 }
@@ -347,11 +347,13 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
             int32_t *idx = index_cache + slot[l] * slot_elems;
             if (qs->max_n > 0) {
                 hipError_t e = ic::launch_indexer_decode(y.q_idx, y.w, y.k_idx, qs->base, qs->n_valid, qs->T,
-                                                         qs->max_n, d->H_I, d->D_I, scores, L.ld, st);
+                                                         qs->max_n, d->H_I, d->D_I, scores, L.ld,
+                                                         ic::topk_hist0(topk_ws), st);
                 if (e != hipSuccess)
                     return hip_status(e, "layer stack: indexer launch");
             }
-            hipError_t e = ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx, topk_ws, st);
+            hipError_t e = ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx, topk_ws,
+                                           qs->max_n > 0, st);
             if (e != hipSuccess)
                 return hip_status(e, "layer stack: top-k launch");
         }

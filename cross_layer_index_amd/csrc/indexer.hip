@@ -19,6 +19,7 @@
 //   Accumulator element r of lane l is (row 8*(r/4) + 4*(l/32) + r%4,
 //   column l % 32).
 #include "kernels.h"
+#include "radix_key.h"
 
 namespace ic {
 namespace {
@@ -72,9 +73,10 @@ template <int DI, int MT>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
     const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t H_I,
-    float *__restrict__ scores, int64_t ld, int64_t chunk)
+    float *__restrict__ scores, int64_t ld, int64_t chunk, uint32_t *__restrict__ hist0)
 {
     using G = IdxGeom<DI>;
+    __shared__ uint32_t hist[kHistBins0];
     const int t = blockIdx.y;
     const int64_t nt = n[t];
     const int64_t s_begin = (int64_t)blockIdx.x * chunk;
@@ -85,6 +87,11 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 5;
     const int j = lane & 31;
+    if (hist0) {
+        for (int i = threadIdx.x; i < kHistBins0; i += 256)
+            hist[i] = 0;
+        __syncthreads();
+    }
 
     // q fragments for all heads of this query, kept in registers
     v8i a[MT][G::KS];
@@ -135,16 +142,26 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
             }
             sum += __shfl_xor(sum, 32);
             const int64_t s = s0 + 32 * u + j;
-            if (g == 0 && s < s_end)
+            if (g == 0 && s < s_end) {
                 srow[s] = sum;
+                if (hist0)
+                    atomicAdd(&hist[ord_key(sum) >> kHistShift0], 1u);
+            }
         }
+    }
+    if (hist0) {
+        __syncthreads();
+        uint32_t *h = hist0 + ((int64_t)t * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins0;
+        for (int i = threadIdx.x; i < kHistBins0; i += 256)
+            if (hist[i])
+                atomicAdd(&h[i], hist[i]);
     }
 }
 
 template <int DI>
 hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                             const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
-                            int32_t H_I, float *scores, int64_t ld, hipStream_t stream)
+                            int32_t H_I, float *scores, int64_t ld, uint32_t *hist0, hipStream_t stream)
 {
     // aim for >= 2048 workgroups over the whole call, chunks of >= one WG step
     int64_t total = max_n * (int64_t)T;
@@ -157,10 +174,10 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
     dim3 grid((unsigned)nchunks, (unsigned)T);
     if (H_I <= 32)
         hipLaunchKernelGGL((indexer_decode_kernel<DI, 1>), grid, dim3(256), 0, stream, q_idx, w, k_idx,
-                           base, n, H_I, scores, ld, chunk);
+                           base, n, H_I, scores, ld, chunk, hist0);
     else
         hipLaunchKernelGGL((indexer_decode_kernel<DI, 2>), grid, dim3(256), 0, stream, q_idx, w, k_idx,
-                           base, n, H_I, scores, ld, chunk);
+                           base, n, H_I, scores, ld, chunk, hist0);
     return hipGetLastError();
 }
 
@@ -169,12 +186,12 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
 hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                                  const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
                                  int32_t H_I, int32_t D_I, float *scores, int64_t ld,
-                                 hipStream_t stream)
+                                 uint32_t *hist0, hipStream_t stream)
 {
     switch (D_I) {
-    case 32: return launch_decode_di<32>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, stream);
-    case 64: return launch_decode_di<64>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, stream);
-    case 128: return launch_decode_di<128>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, stream);
+    case 32: return launch_decode_di<32>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, hist0, stream);
+    case 64: return launch_decode_di<64>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, hist0, stream);
+    case 128: return launch_decode_di<128>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, hist0, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -10,10 +10,13 @@ namespace ic {
 
 // ---- indexer --------------------------------------------------------------
 // Decode form: each query streams its own key rows (no reuse across queries).
+// With `hist0` non-null, also adds each score's first radix digit (bits 31..21
+// of its order-preserving key) into hist0[t][copy][2048] (copy = workgroup
+// index mod kHistCopies) for the top-k that follows.
 hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                                  const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
                                  int32_t H_I, int32_t D_I, float *scores, int64_t ld,
-                                 hipStream_t stream);
+                                 uint32_t *hist0, hipStream_t stream);
 // Prefill form: all queries read one sequence; key tiles are shared by a
 // group of queries through LDS.
 hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
@@ -23,9 +26,13 @@ hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const ui
 bool indexer_prefill_supported(int32_t H_I, int32_t D_I);
 
 // ---- top-k ------------------------------------------------------------------
+// The workspace starts with the first-digit histograms [T][copies][2048]
+// (uint32, zero on entry and on return); topk_hist0() points at them.
 size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t k);
+uint32_t *topk_hist0(void *ws);
+// hist_ready: the histograms were filled while the scores were produced.
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
-                       int32_t k, int32_t *idx, void *ws, hipStream_t stream);
+                       int32_t k, int32_t *idx, void *ws, bool hist_ready, hipStream_t stream);
 
 // ---- sparse MLA -----------------------------------------------------------
 struct MlaPlan {

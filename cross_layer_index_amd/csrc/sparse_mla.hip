@@ -36,6 +36,7 @@ constexpr int kHeadsPerWG = 64;
 constexpr int kTile = 32;                 // gathered rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMInit = -1.0e30f;        // finite "minus infinity" for partials
+constexpr int kMaxRowsPerSplit = 2048;    // index entries one workgroup handles
 
 __device__ __forceinline__ f4 mfma_bf16_16x16x32(const bf16x8 &a, const bf16x8 &b, const f4 &c)
 {
@@ -66,22 +67,33 @@ struct MlaGeom {
     static constexpr int KROW = DQKP + 8;        // LDS row stride (bf16)
     static constexpr int NCH = DQK / 8;          // 16-byte chunks per row
     static constexpr int NTV = DV / 16;          // value column tiles
-    static constexpr int VROW = kTile + 8;       // transposed-V row stride (bf16)
+    static constexpr int VROW = kTile + 4;       // transposed-V row stride (bf16): 72 B keeps
+                                                 // the transposing writes conflict-free
     static_assert(DQK % 8 == 0 && DV % 16 == 0 && DV <= DQK, "shape");
+};
+
+// Rows of the KV cache a thread copies per tile: items of (row quad, 16-byte
+// chunk); the tile's loads are all issued before any is used.
+template <int DQK>
+struct Gather {
+    static constexpr int NCH = DQK / 8;
+    static constexpr int ITEMS = (kTile / 4) * NCH;
+    static constexpr int PER = (ITEMS + kMlaThreads - 1) / kMlaThreads;
 };
 
 // grid: (splits, ceil(H/64), T); block: 256.
 template <int DQK, int DV>
-__global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
+__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const int64_t *__restrict__ base,
     const int32_t *__restrict__ idx, int32_t k, int32_t H, const float *__restrict__ sink, float scale_log2,
     int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
     float *__restrict__ part_o, float *__restrict__ part_ml)
 {
     using G = MlaGeom<DQK, DV>;
+    using GA = Gather<DQK>;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * G::KROW];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * G::VROW];
-    __shared__ int32_t rowid[kTile];
+    __shared__ int32_t rowid[kMaxRowsPerSplit];
 
     const int split = blockIdx.x;
     const int t = blockIdx.z;
@@ -95,6 +107,14 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
     const int64_t b_t = base[t];
     const int j_begin = split * rows_per_split;
     const int j_end = min(k, j_begin + rows_per_split);
+    const int nrows = j_end - j_begin;
+    // a row every thread may always read: this query's own q row (used in place
+    // of empty index slots, whose data is then replaced by zeros)
+    const uint16_t *safe_row = q + (int64_t)t * H * DQK;
+
+    // the split's index list, kept in LDS
+    for (int i = tid; i < nrows; i += kMlaThreads)
+        rowid[i] = idx[(int64_t)t * k + j_begin + i];
 
     // q fragments: lane (head hc, group g) holds d = 32*ks + 8*g .. +8
     bf16x8 qf[G::KS];
@@ -114,6 +134,57 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
             *reinterpret_cast<uint4 *>(&Ks[r * G::KROW + DQK + 8 * ch]) = make_uint4(0, 0, 0, 0);
         }
     }
+    __syncthreads();
+
+    // row id of tile-local row j of the tile starting at list offset j0 (-1 = empty)
+    auto rid_of = [&](int j0, int j) -> int { return j0 + j < nrows ? rowid[j0 + j] : -1; };
+
+    uint4 pre[GA::PER][4];
+    auto prefetch = [&](int j0) {
+#pragma unroll
+        for (int it = 0; it < GA::PER; ++it) {
+            const int item = tid + it * kMlaThreads;
+            const int rq = item & 7;
+            const int ch = min(item >> 3, GA::NCH - 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rid = rid_of(j0, 4 * rq + r);
+                const uint16_t *p = rid >= 0 ? kv + (b_t + rid) * DQK : safe_row;
+                pre[it][r] = *reinterpret_cast<const uint4 *>(p + 8 * ch);
+            }
+        }
+    };
+    // write the prefetched tile: row-major K, transposed V (zeros for empty slots)
+    auto commit = [&](int j0) {
+#pragma unroll
+        for (int it = 0; it < GA::PER; ++it) {
+            const int item = tid + it * kMlaThreads;
+            if (item >= GA::ITEMS)
+                continue;
+            const int rq = item & 7;
+            const int ch = item >> 3;
+            uint4 v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v[r] = rid_of(j0, 4 * rq + r) >= 0 ? pre[it][r] : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(&Ks[(4 * rq + r) * G::KROW + 8 * ch]) = v[r];
+            }
+            if (8 * ch < DV) {
+                const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+                const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+                const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+                const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sh = (e & 1) * 16;
+                    const uint32_t a0 = (w0[e >> 1] >> sh) & 0xFFFFu, a1 = (w1[e >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t a2 = (w2[e >> 1] >> sh) & 0xFFFFu, a3 = (w3[e >> 1] >> sh) & 0xFFFFu;
+                    *reinterpret_cast<uint2 *>(&Vt[(8 * ch + e) * G::VROW + 4 * rq]) =
+                        make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+                }
+            }
+        }
+    };
 
     float m_run, l_run;
     if (splits == 1) {
@@ -128,40 +199,11 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
     for (int nt = 0; nt < G::NTV; ++nt)
         o[nt] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int tile0 = j_begin; tile0 < j_end; tile0 += kTile) {
+    if (nrows > 0)
+        prefetch(0);
+    for (int j0 = 0; j0 < nrows; j0 += kTile) {
         __syncthreads();                          // previous tile fully consumed
-        if (tid < kTile) {
-            const int j = tile0 + tid;
-            rowid[tid] = j < j_end ? idx[(int64_t)t * k + j] : -1;
-        }
-        __syncthreads();
-        // gather: item = (row quad rq, 16-byte chunk ch)
-        for (int item = tid; item < (kTile / 4) * G::NCH; item += kMlaThreads) {
-            const int rq = item / G::NCH;
-            const int ch = item - rq * G::NCH;
-            uint4 v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rid = rowid[4 * rq + r];
-                v[r] = rid >= 0 ? *reinterpret_cast<const uint4 *>(kv + (b_t + rid) * DQK + 8 * ch)
-                                : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(&Ks[(4 * rq + r) * G::KROW + 8 * ch]) = v[r];
-            }
-            if (8 * ch < DV) {
-                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&v[0]);
-                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&v[1]);
-                const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&v[2]);
-                const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&v[3]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int sh = (e & 1) * 16;
-                    const uint32_t a0 = (w0[e >> 1] >> sh) & 0xFFFFu, a1 = (w1[e >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t a2 = (w2[e >> 1] >> sh) & 0xFFFFu, a3 = (w3[e >> 1] >> sh) & 0xFFFFu;
-                    *reinterpret_cast<uint2 *>(&Vt[(8 * ch + e) * G::VROW + 4 * rq]) =
-                        make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-                }
-            }
-        }
+        commit(j0);
         __syncthreads();
 
         // S^T = K Q^T for this wave's 16 heads, rows 16*b + (0..15)
@@ -174,13 +216,15 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
                 st[b] = mfma_bf16_16x16x32(as_bf16x8(a), qf[ks], st[b]);
             }
         }
+        if (j0 + kTile < nrows)
+            prefetch(j0 + kTile);                 // in flight during softmax and PV
         float s[8];
         float mt = -INFINITY;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool ok = rowid[16 * b + 4 * g + r] >= 0;
+                const bool ok = rid_of(j0, 16 * b + 4 * g + r) >= 0;
                 s[4 * b + r] = ok ? st[b][r] * scale_log2 : -INFINITY;
                 mt = fmaxf(mt, s[4 * b + r]);
             }
@@ -204,6 +248,7 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             al[r] = __shfl(alpha, 4 * g + r);
+        const bool rescale = __any(alpha != 1.0f);
         const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         const bf16x8 pa = as_bf16x8(pw);
@@ -213,9 +258,11 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
             const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
             const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16);
             const bf16x8 vb = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+            if (rescale) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                o[nt][r] *= al[r];
+                for (int r = 0; r < 4; ++r)
+                    o[nt][r] *= al[r];
+            }
             o[nt] = mfma_bf16_16x16x32(pa, vb, o[nt]);
         }
     }
@@ -259,6 +306,8 @@ __global__ __launch_bounds__(kMlaThreads) void sparse_mla_kernel(
 }
 
 // grid: (H, T); block: 256. Merges the per-split partials and adds the sink.
+constexpr int kMaxSplits = 256;
+
 template <int DV>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml,
@@ -266,24 +315,55 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restric
                                                           int32_t splits, void *__restrict__ out,
                                                           int32_t out_f32)
 {
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float red[4];
     const int h = blockIdx.x;
     const int t = blockIdx.y;
+    const int tid = threadIdx.x;
     const float ms = sink[h] * kLog2e;
-    float m = ms;
-    for (int s = 0; s < splits; ++s)
+    // global maximum over the sink and the partial maxima
+    float m = tid == 0 ? ms : -INFINITY;
+    for (int s = tid; s < splits; s += 256)
         m = fmaxf(m, part_ml[(((int64_t)t * splits + s) * H + h) * 2]);
-    float den = exp2f(ms - m);
-    for (int s = 0; s < splits; ++s) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0)
+        red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    // per-split weights and the denominator
+    float dsum = tid == 0 ? exp2f(ms - m) : 0.0f;
+    for (int s = tid; s < splits; s += 256) {
         const int64_t pr = ((int64_t)t * splits + s) * H + h;
-        den += part_ml[pr * 2 + 1] * exp2f(part_ml[pr * 2] - m);
+        const float wv = exp2f(part_ml[pr * 2] - m);
+        wgt[s] = wv;
+        dsum += part_ml[pr * 2 + 1] * wv;
     }
-    const float inv = 1.0f / den;
-    for (int v = threadIdx.x; v < DV; v += blockDim.x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        dsum += __shfl_xor(dsum, off);
+    if ((tid & 63) == 0)
+        red[tid >> 6] = dsum;
+    __syncthreads();
+    const float inv = 1.0f / (red[0] + red[1] + red[2] + red[3]);
+    const int64_t stride = (int64_t)H * DV;
+    for (int v = tid; v < DV; v += 256) {
+        const float *p = part_o + ((int64_t)t * splits * H + h) * DV + v;
         float acc = 0.0f;
-        for (int s = 0; s < splits; ++s) {
-            const int64_t pr = ((int64_t)t * splits + s) * H + h;
-            acc += part_o[pr * DV + v] * exp2f(part_ml[pr * 2] - m);
+        int s = 0;
+        for (; s + 8 <= splits; s += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                x[u] = p[(int64_t)(s + u) * stride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                acc = fmaf(x[u], wgt[s + u], acc);
         }
+        for (; s < splits; ++s)
+            acc = fmaf(p[(int64_t)s * stride], wgt[s], acc);
         const int64_t oi = ((int64_t)t * H + h) * DV + v;
         if (out_f32)
             reinterpret_cast<float *>(out)[oi] = acc * inv;
@@ -326,11 +406,15 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     MlaPlan p;
     const int64_t hg = (H + kHeadsPerWG - 1) / kHeadsPerWG;
     const int64_t base_wgs = (int64_t)T * hg;
-    const int64_t max_splits = (k + 4 * kTile - 1) / (4 * kTile);   // >= 4 tiles per split
+    int64_t max_splits = (k + 4 * kTile - 1) / (4 * kTile);   // >= 4 tiles per split
+    if (max_splits > kMaxSplits)
+        max_splits = kMaxSplits;
     int64_t s = base_wgs > 0 ? (512 + base_wgs - 1) / base_wgs : 1;
     s = s < 1 ? 1 : s;
     s = s > max_splits ? max_splits : s;
     s = s < 1 ? 1 : s;
+    if (s < (k + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit)
+        s = (k + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit;
     int64_t rps = (k + s - 1) / s;
     rps = (rps + kTile - 1) / kTile * kTile;
     s = (k + rps - 1) / rps;

@@ -3,37 +3,55 @@
 // "rtx6kpro #90"): keep the k largest scores of positions 0..n_t-1, the lower
 // position winning among equal scores, emitted in ascending position order.
 //
-// Method: radix select on an order-preserving 32-bit image of the fp32 score
-// (three LDS-histogram passes of 11, 11 and 10 bits find the k-th largest key
-// `thr` and how many of the keys equal to it are kept, `need`), then one
-// ordered compaction in position order. A position is kept when its key is
-// above thr, or equal to thr and fewer than `need` equal keys precede it; its
-// output slot is (#kept keys above thr before it) + min(#equal keys before it,
-// need), which a block-wide prefix sum of packed (above, equal) counts gives.
+// Method: radix select over an order-preserving 32-bit image of the fp32
+// score, in three digits (bits 31..21, 20..10, 9..0). Each digit's histogram
+// finds the bin holding the k-th largest key; after the last digit the k-th
+// key `thr` is known, with `need` = how many keys equal to thr are kept. A
+// final ordered compaction walks the keys in position order: a key above thr
+// is kept, a key equal to thr is kept while fewer than `need` equal keys came
+// before it, and its output slot is (#kept keys above thr before it) +
+// min(#equal keys before it, need) -- a prefix sum of packed (above, equal)
+// counts.
+//
+// The first digit's histogram is built while the scores are produced (the
+// indexer kernel can add into it) or by topk_hist_kernel. Only keys whose
+// first digit is >= the threshold digit ("survivors", about k plus one bin)
+// take part in the later digits:
+//   * split path (few queries, long rows): P workgroups per query each copy
+//     their chunk's survivors, in position order, into their own slice of the
+//     workspace (topk_survivors_kernel); one workgroup per query then gathers
+//     them in order into LDS and finishes the selection there
+//     (topk_finish_kernel). The kernel boundary orders the two phases.
+//   * row path (many queries): one workgroup per query streams its row once
+//     more to collect survivors into LDS and finishes there.
+// If the survivors exceed the LDS list (heavy ties), the finishing workgroup
+// falls back to digit passes over the full row, which is always correct.
+// The first-digit histogram is kept in kHistCopies copies per query (adders
+// pick a copy by workgroup index, which spreads atomic traffic); the workspace
+// holds them zeroed on entry and the finishing workgroup zeroes them again.
 #include "kernels.h"
+#include "radix_key.h"
 
 namespace ic {
 namespace {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBins0 = kHistBins0;      // first digit: bits 31..21
+constexpr int kSplitThreads = 256;
+constexpr int kSplitChunk = kSplitThreads * 4;   // scores per split workgroup
+constexpr int kRowThreads = 1024;
+constexpr int kListCap = 8192;          // survivors held in LDS
+constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
 
-__device__ __forceinline__ uint32_t ord_key(float x)
+// Block-wide inclusive scan of one uint32 per thread.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *lds_waves, uint32_t *total)
 {
-    uint32_t u = __float_as_uint(x);
-    if (u == 0x80000000u)
-        u = 0u;                                   // -0 and +0 are one value
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Block-wide inclusive scan of one uint32 per thread (1024 threads).
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *lds_waves, uint32_t *total)
-{
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        uint32_t o = __shfl_up(v, off);
+        const uint32_t o = __shfl_up(v, off);
         if (lane >= off)
             v += o;
     }
@@ -41,127 +59,160 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *l
         lds_waves[wave] = v;
     __syncthreads();
     if (wave == 0) {
-        uint32_t x = lane < kTopkWaves ? lds_waves[lane] : 0u;
+        uint32_t x = lane < NW ? lds_waves[lane] : 0u;
 #pragma unroll
-        for (int off = 1; off < kTopkWaves; off <<= 1) {
-            uint32_t o = __shfl_up(x, off);
+        for (int off = 1; off < NW; off <<= 1) {
+            const uint32_t o = __shfl_up(x, off);
             if (lane >= off)
                 x += o;
         }
-        if (lane < kTopkWaves)
-            lds_waves[lane] = x;      // inclusive wave totals
+        if (lane < NW)
+            lds_waves[lane] = x;
     }
     __syncthreads();
     const uint32_t before = wave ? lds_waves[wave - 1] : 0u;
     if (total)
-        *total = lds_waves[kTopkWaves - 1];
+        *total = lds_waves[NW - 1];
     __syncthreads();
     return v + before;
 }
 
-// grid: T; block: 1024 threads. One workgroup selects one query's top-k.
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(const float *__restrict__ scores, int64_t ld,
-                                                                const int32_t *__restrict__ n, int32_t k,
-                                                                int32_t *__restrict__ idx)
+struct Shared {
+    uint32_t hist[kBins0];
+    uint32_t waves[16];
+    uint32_t digit, above;
+};
+
+// Given a histogram of `nb` bins (in LDS), find the digit of the bin holding
+// the need-th largest key; returns it with the count of keys in higher bins.
+template <int NT>
+__device__ __forceinline__ void find_digit(Shared &sh, int nb, uint32_t need, uint32_t &digit, uint32_t &above)
 {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wave_tot[kTopkWaves];
-    __shared__ uint32_t sel_digit, sel_above;
-
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int64_t nt = n[t];
-    int32_t *out = idx + (int64_t)t * k;
-    if (nt <= k) {
-        for (int i = tid; i < k; i += kTopkThreads)
-            out[i] = i < nt ? i : -1;
-        return;
-    }
-    const float *row = scores + (int64_t)t * ld;
-
-    uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nb = pass == 2 ? 1024 : 2048;
-        for (int i = tid; i < nb; i += kTopkThreads)
-            hist[i] = 0;
-        __syncthreads();
-        for (int64_t s = (int64_t)tid * 4; s < nt; s += (int64_t)kTopkThreads * 4) {
-            if (s + 3 < nt) {
-                const float4 v = *reinterpret_cast<const float4 *>(row + s);
-                const float vv[4] = {v.x, v.y, v.z, v.w};
+    constexpr int PER = kBins0 / NT;             // bins per thread (descending)
+    uint32_t c[PER];
+    uint32_t local = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t key = ord_key(vv[e]);
-                    if ((key & pmask) == prefix)
-                        atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-                }
-            } else {
-                for (int64_t e = s; e < nt; ++e) {
-                    const uint32_t key = ord_key(row[e]);
-                    if ((key & pmask) == prefix)
-                        atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-                }
+    for (int i = 0; i < PER; ++i) {
+        const int b = nb - 1 - (PER * (int)threadIdx.x + i);
+        c[i] = b >= 0 ? sh.hist[b] : 0u;
+        local += c[i];
+    }
+    const uint32_t incl = block_scan<NT>(local, sh.waves, nullptr);
+    uint32_t run = incl - local;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int b = nb - 1 - (PER * (int)threadIdx.x + i);
+        if (b >= 0 && run < need && run + c[i] >= need) {
+            sh.digit = (uint32_t)b;
+            sh.above = run;
+        }
+        run += c[i];
+    }
+    __syncthreads();
+    digit = sh.digit;
+    above = sh.above;
+    __syncthreads();
+}
+
+// Key sources: a row of fp32 scores (position = index) or an LDS list of
+// (key << 32 | position) entries in position order.
+struct RowSrc {
+    const float *row;
+    int64_t n;
+    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
+    {
+        if (i + 3 < n) {
+            const float4 v = *reinterpret_cast<const float4 *>(row + i);
+            key[0] = ord_key(v.x), key[1] = ord_key(v.y), key[2] = ord_key(v.z), key[3] = ord_key(v.w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pos[e] = i + e, ok[e] = true;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ok[e] = i + e < n;
+                key[e] = ok[e] ? ord_key(row[i + e]) : 0u;
+                pos[e] = i + e;
             }
         }
-        __syncthreads();
-        // bins in descending digit order: thread p owns digits nb-1-2p, nb-2-2p
-        uint32_t c0 = 0, c1 = 0;
-        if (2 * tid < nb) {
-            c0 = hist[nb - 1 - 2 * tid];
-            c1 = hist[nb - 2 - 2 * tid];
+    }
+};
+
+struct ListSrc {
+    const uint64_t *list;
+    int64_t n;
+    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ok[e] = i + e < n;
+            const uint64_t v = ok[e] ? list[i + e] : 0ull;
+            key[e] = (uint32_t)(v >> 32);
+            pos[e] = (int64_t)(uint32_t)v;
         }
-        const uint32_t incl = block_inclusive_scan(c0 + c1, wave_tot, nullptr);
-        const uint32_t excl = incl - c0 - c1;
-        if (2 * tid < nb) {
-            if (excl < need && excl + c0 >= need) {
-                sel_digit = nb - 1 - 2 * tid;
-                sel_above = excl;
-            } else if (excl + c0 < need && incl >= need) {
-                sel_digit = nb - 2 - 2 * tid;
-                sel_above = excl + c0;
-            }
+    }
+};
+
+// Digit passes `first`..2 over `src`, then the ordered compaction into out[0..k).
+template <int NT, class Src>
+__device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t prefix, uint32_t pmask,
+                              uint32_t need, int32_t k, int32_t *__restrict__ out)
+{
+    const int tid = threadIdx.x;
+    for (int pass = first; pass < 3; ++pass) {
+        const int shf = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        for (int i = tid; i < nb; i += NT)
+            sh.hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = (int64_t)tid * 4; i < src.n; i += (int64_t)NT * 4) {
+            uint32_t key[4];
+            int64_t pos[4];
+            bool ok[4];
+            src.get4(i, key, pos, ok);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ok[e] && (key[e] & pmask) == prefix)
+                    atomicAdd(&sh.hist[(key[e] >> shf) & (nb - 1)], 1u);
         }
         __syncthreads();
-        prefix |= sel_digit << sh;
-        pmask |= (uint32_t)(nb - 1) << sh;
-        need -= sel_above;
-        __syncthreads();
+        uint32_t digit, above;
+        find_digit<NT>(sh, nb, need, digit, above);
+        prefix |= digit << shf;
+        pmask |= (uint32_t)(nb - 1) << shf;
+        need -= above;
     }
     const uint32_t thr = prefix;
-
-    // ordered compaction, 4 consecutive positions per thread per chunk
     uint32_t run_gt = 0, run_eq = 0;
-    for (int64_t c0 = 0; c0 < nt; c0 += (int64_t)kTopkThreads * 4) {
-        const int64_t s = c0 + (int64_t)tid * 4;
+    for (int64_t c0 = 0; c0 < src.n; c0 += (int64_t)NT * 4) {
+        uint32_t key[4];
+        int64_t pos[4];
+        bool ok[4];
+        src.get4(c0 + (int64_t)tid * 4, key, pos, ok);
         uint32_t gt[4], eq[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            gt[e] = eq[e] = 0;
-            if (s + e < nt) {
-                const uint32_t key = ord_key(row[s + e]);
-                gt[e] = key > thr;
-                eq[e] = key == thr;
-            }
+            gt[e] = ok[e] && key[e] > thr;
+            eq[e] = ok[e] && key[e] == thr;
         }
         const uint32_t lg = gt[0] + gt[1] + gt[2] + gt[3];
         const uint32_t le = eq[0] + eq[1] + eq[2] + eq[3];
         uint32_t tot;
-        const uint32_t incl = block_inclusive_scan(lg | (le << 16), wave_tot, &tot);
+        const uint32_t incl = block_scan<NT>(lg | (le << 16), sh.waves, &tot);
         const uint32_t excl = incl - (lg | (le << 16));
         uint32_t gb = run_gt + (excl & 0xFFFFu);
         uint32_t eb = run_eq + (excl >> 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // slots are < k by construction; the bound check keeps a broken
-            // threshold from ever writing outside the row
+            // slots are < k by construction; the check keeps any inconsistent
+            // input (NaN scores) from writing outside the row
             if (gt[e]) {
                 const uint32_t slot = gb + min(eb, need);
                 if (slot < (uint32_t)k)
-                    out[slot] = (int32_t)(s + e);
+                    out[slot] = (int32_t)pos[e];
             } else if (eq[e] && eb < need) {
                 if (gb + eb < (uint32_t)k)
-                    out[gb + eb] = (int32_t)(s + e);
+                    out[gb + eb] = (int32_t)pos[e];
             }
             gb += gt[e];
             eb += eq[e];
@@ -169,21 +220,323 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(const float *__r
         run_gt += tot & 0xFFFFu;
         run_eq += tot >> 16;
         if (run_gt + min(run_eq, need) >= (uint32_t)k)
-            break;                                 // every kept position is placed
+            break;
     }
+}
+
+template <int NT>
+__device__ void write_all(int32_t *out, int64_t nt, int32_t k)
+{
+    for (int i = threadIdx.x; i < k; i += NT)
+        out[i] = i < nt ? i : -1;
+}
+
+// Sum the histogram copies of one query into LDS.
+template <int NT>
+__device__ void load_hist0(Shared &sh, const uint32_t *h)
+{
+    for (int i = threadIdx.x * 4; i < kBins0; i += NT * 4) {
+        uint4 acc = *reinterpret_cast<const uint4 *>(h + i);
+#pragma unroll
+        for (int c = 1; c < kHistCopies; ++c) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(h + c * kBins0 + i);
+            acc.x += v.x, acc.y += v.y, acc.z += v.z, acc.w += v.w;
+        }
+        *reinterpret_cast<uint4 *>(&sh.hist[i]) = acc;
+    }
+    __syncthreads();
+}
+
+template <int NT>
+__device__ void zero_hist0(uint32_t *h)
+{
+    for (int i = threadIdx.x * 4; i < kBins0 * kHistCopies; i += NT * 4)
+        *reinterpret_cast<uint4 *>(h + i) = make_uint4(0, 0, 0, 0);
+}
+
+// ---- first-digit histogram of a score row (standalone top-k) -------------
+// grid: (chunks, T); block: 256.
+__global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict__ scores, int64_t ld,
+                                                        const int32_t *__restrict__ n, int64_t chunk,
+                                                        uint32_t *__restrict__ hist0)
+{
+    __shared__ uint32_t h[kBins0];
+    const int t = blockIdx.y;
+    const int64_t nt = n[t];
+    const int64_t s0 = (int64_t)blockIdx.x * chunk;
+    if (s0 >= nt)
+        return;
+    const int64_t s1 = min(nt, s0 + chunk);
+    for (int i = threadIdx.x; i < kBins0; i += 256)
+        h[i] = 0;
+    __syncthreads();
+    const float *row = scores + (int64_t)t * ld;
+    for (int64_t i = s0 + (int64_t)threadIdx.x * 4; i < s1; i += 256 * 4) {
+        if (i + 3 < s1) {
+            const float4 v = *reinterpret_cast<const float4 *>(row + i);
+            atomicAdd(&h[ord_key(v.x) >> 21], 1u);
+            atomicAdd(&h[ord_key(v.y) >> 21], 1u);
+            atomicAdd(&h[ord_key(v.z) >> 21], 1u);
+            atomicAdd(&h[ord_key(v.w) >> 21], 1u);
+        } else {
+            for (int64_t e = i; e < s1; ++e)
+                atomicAdd(&h[ord_key(row[e]) >> 21], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t *g = hist0 + ((int64_t)t * kHistCopies + (blockIdx.x % kHistCopies)) * kBins0;
+    for (int i = threadIdx.x; i < kBins0; i += 256)
+        if (h[i])
+            atomicAdd(&g[i], h[i]);
+}
+
+// ---- split path -------------------------------------------------------------
+// Phase 1. grid: (P, T); block: 256; kSplitChunk scores per workgroup. Copies
+// the chunk's survivors (first digit >= the threshold digit), in position
+// order, into the workgroup's slice of `regions`, and their count to counts.
+__global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
+    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
+    const uint32_t *__restrict__ hist0, uint32_t *__restrict__ counts, uint64_t *__restrict__ regions)
+{
+    __shared__ Shared sh;
+    const int t = blockIdx.y;
+    const int w = blockIdx.x;
+    const int P = gridDim.x;
+    const int tid = threadIdx.x;
+    const int64_t nt = n[t];
+    if (nt <= k)
+        return;                                   // the finish kernel keeps everything
+    const float *row = scores + (int64_t)t * ld;
+    // this chunk's scores, issued before the histogram is read
+    const int64_t s = (int64_t)w * kSplitChunk + (int64_t)tid * 4;
+    uint32_t key[4];
+    int64_t pos[4];
+    bool ok[4];
+    RowSrc{row, nt}.get4(s, key, pos, ok);
+
+    uint32_t d0, above0;
+    load_hist0<kSplitThreads>(sh, hist0 + (int64_t)t * kHistCopies * kBins0);
+    find_digit<kSplitThreads>(sh, kBins0, (uint32_t)k, d0, above0);
+    uint32_t sv[4], ls = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sv[e] = ok[e] && (key[e] >> 21) >= d0;
+        ls += sv[e];
+    }
+    uint32_t tot;
+    uint32_t o = block_scan<kSplitThreads>(ls, sh.waves, &tot) - ls;
+    uint64_t *reg = regions + ((int64_t)t * P + w) * kSplitChunk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (sv[e])
+            reg[o++] = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
+    if (tid == 0)
+        counts[(int64_t)t * P + w] = tot;
+}
+
+// Phase 2. grid: T; block: 1024. Gathers the survivors of all P slices in
+// slice order (= position order) into LDS and finishes the selection; zeroes
+// the query's histogram copies.
+__global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
+    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
+    int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, const uint32_t *__restrict__ counts,
+    const uint64_t *__restrict__ regions, int32_t P)
+{
+    __shared__ Shared sh;
+    __shared__ uint64_t list[kListCap];
+    __shared__ uint32_t offs[kMaxSplit + 1];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nt = n[t];
+    int32_t *out = idx + (int64_t)t * k;
+    uint32_t *h0 = hist0 + (int64_t)t * kHistCopies * kBins0;
+    if (nt <= k) {
+        write_all<kRowThreads>(out, nt, k);
+        zero_hist0<kRowThreads>(h0);
+        return;
+    }
+    uint32_t d0, above0;
+    load_hist0<kRowThreads>(sh, h0);
+    find_digit<kRowThreads>(sh, kBins0, (uint32_t)k, d0, above0);
+    zero_hist0<kRowThreads>(h0);
+    // slice offsets
+    uint32_t total = 0;
+    for (int w0 = 0; w0 < P; w0 += kRowThreads) {
+        const int ww = w0 + tid;
+        const uint32_t c = ww < P ? counts[(int64_t)t * P + ww] : 0u;
+        uint32_t tot;
+        const uint32_t excl = block_scan<kRowThreads>(c, sh.waves, &tot) - c;
+        if (ww < P)
+            offs[ww] = total + excl;
+        total += tot;
+    }
+    if (tid == 0)
+        offs[P] = total;
+    __syncthreads();
+    const uint32_t need = (uint32_t)k - above0;
+    if (total <= (uint32_t)kListCap) {
+        for (uint32_t i = tid; i < total; i += kRowThreads) {
+            int lo = 0, hi = P;                   // last slice whose offset <= i
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (offs[mid] <= i)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            list[i] = regions[((int64_t)t * P + lo) * kSplitChunk + (i - offs[lo])];
+        }
+        __syncthreads();
+        finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+    } else {
+        finish_select<kRowThreads>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 1, d0 << 21, 0xFFE00000u, need, k,
+                                   out);
+    }
+}
+
+// ---- row path ---------------------------------------------------------------
+// grid: T; block: 1024. With `hist0` non-null the first digit's histogram is
+// taken from it (and zeroed); otherwise it is built here.
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__restrict__ scores, int64_t ld,
+                                                               const int32_t *__restrict__ n, int32_t k,
+                                                               int32_t *__restrict__ idx,
+                                                               uint32_t *__restrict__ hist0)
+{
+    __shared__ Shared sh;
+    __shared__ uint64_t list[kListCap];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nt = n[t];
+    int32_t *out = idx + (int64_t)t * k;
+    const float *row = scores + (int64_t)t * ld;
+    const RowSrc src{row, nt};
+    uint32_t *h0 = hist0 ? hist0 + (int64_t)t * kHistCopies * kBins0 : nullptr;
+
+    if (nt <= k) {
+        write_all<kRowThreads>(out, nt, k);
+        if (h0)
+            zero_hist0<kRowThreads>(h0);
+        return;
+    }
+    if (h0) {
+        load_hist0<kRowThreads>(sh, h0);
+        zero_hist0<kRowThreads>(h0);
+    } else {
+        for (int i = tid; i < kBins0; i += kRowThreads)
+            sh.hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = (int64_t)tid * 4; i < nt; i += (int64_t)kRowThreads * 4) {
+            uint32_t key[4];
+            int64_t pos[4];
+            bool ok[4];
+            src.get4(i, key, pos, ok);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ok[e])
+                    atomicAdd(&sh.hist[key[e] >> 21], 1u);
+        }
+        __syncthreads();
+    }
+    uint32_t d0, above0;
+    find_digit<kRowThreads>(sh, kBins0, (uint32_t)k, d0, above0);
+    const uint32_t need = (uint32_t)k - above0;
+    // collect survivors in position order
+    uint32_t total = 0;
+    for (int64_t c0 = 0; c0 < nt; c0 += (int64_t)kRowThreads * 4) {
+        uint32_t key[4];
+        int64_t pos[4];
+        bool ok[4];
+        src.get4(c0 + (int64_t)tid * 4, key, pos, ok);
+        uint32_t sv[4], ls = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = ok[e] && (key[e] >> 21) >= d0;
+            ls += sv[e];
+        }
+        uint32_t tot;
+        uint32_t o = total + block_scan<kRowThreads>(ls, sh.waves, &tot) - ls;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (sv[e]) {
+                if (o < (uint32_t)kListCap)
+                    list[o] = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
+                ++o;
+            }
+        }
+        total += tot;
+    }
+    __syncthreads();
+    if (total <= (uint32_t)kListCap)
+        finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+    else
+        finish_select<kRowThreads>(src, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+}
+
+struct TopkLayout {
+    bool split;
+    int64_t P;
+    size_t hist_off, counts_off, regions_off, total;
+};
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+TopkLayout topk_layout(int32_t T, int64_t max_n)
+{
+    TopkLayout L{};
+    L.P = (max_n + kSplitChunk - 1) / kSplitChunk;
+    if (L.P < 1)
+        L.P = 1;
+    // split when the queries alone cannot fill the chip and the survivor
+    // slices stay small
+    L.split = T < 256 && (int64_t)T * L.P * kSplitChunk <= ((int64_t)1 << 26) && L.P <= kMaxSplit;
+    L.hist_off = 0;
+    L.counts_off = up256((size_t)T * kHistCopies * kBins0 * 4);
+    if (L.split) {
+        L.regions_off = L.counts_off + up256((size_t)T * L.P * 4);
+        L.total = L.regions_off + up256((size_t)T * L.P * kSplitChunk * 8);
+    } else {
+        L.regions_off = L.counts_off;
+        L.total = L.counts_off;
+    }
+    return L;
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int32_t, int64_t, int32_t) { return 0; }
+size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t) { return topk_layout(T, max_n).total; }
 
-hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t,
-                       int32_t k, int32_t *idx, void *, hipStream_t stream)
+uint32_t *topk_hist0(void *ws) { return reinterpret_cast<uint32_t *>(ws); }
+
+hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n, int32_t k,
+                       int32_t *idx, void *ws, bool hist_ready, hipStream_t stream)
 {
     if (T == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kTopkThreads), 0, stream, scores, ld, n, k,
-                       idx);
+    const TopkLayout L = topk_layout(T, max_n);
+    char *base = static_cast<char *>(ws);
+    uint32_t *hist0 = reinterpret_cast<uint32_t *>(base + L.hist_off);
+    if (L.split) {
+        uint32_t *counts = reinterpret_cast<uint32_t *>(base + L.counts_off);
+        uint64_t *regions = reinterpret_cast<uint64_t *>(base + L.regions_off);
+        if (!hist_ready && max_n > 0) {
+            const int64_t chunk = 8192;
+            hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)((max_n + chunk - 1) / chunk), (unsigned)T),
+                               dim3(256), 0, stream, scores, ld, n, chunk, hist0);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        hipLaunchKernelGGL(topk_survivors_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0,
+                           stream, scores, ld, n, k, hist0, counts, regions);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k,
+                           idx, hist0, counts, regions, (int32_t)L.P);
+    } else {
+        hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
+                           hist_ready ? hist0 : nullptr);
+    }
     return hipGetLastError();
 }
 
