@@ -184,6 +184,23 @@ StackLayout stack_layout(const ic_queries *qs, const ic_dims *d)
     return L;
 }
 
+// Prefill (all queries on one sequence) uses the key-sharing GEMM form when it
+// is built for the shape; everything else streams keys per query.
+bool use_prefill_indexer(const ic_queries *qs, int32_t H_I, int32_t D_I)
+{
+    return qs->same_seq && qs->T > 1 && ic::indexer_prefill_supported(H_I, D_I);
+}
+
+hipError_t launch_indexer(const uint8_t *q_idx, const float *w, const uint8_t *k_idx, const ic_queries *qs,
+                          int32_t H_I, int32_t D_I, float *scores, int64_t ld, uint32_t *hist0, hipStream_t st)
+{
+    if (use_prefill_indexer(qs, H_I, D_I))
+        return ic::launch_indexer_prefill(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I, D_I, scores,
+                                          ld, st);
+    return ic::launch_indexer_decode(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I, D_I, scores, ld,
+                                     hist0, st);
+}
+
 }  // namespace
 
 IC_EXPORT const char *ic_status_str(ic_status s)
@@ -212,9 +229,7 @@ IC_EXPORT ic_status ic_indexer_score(const uint8_t *q_idx, const float *w, const
     if (qs->T == 0 || qs->max_n == 0)
         return ok();
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    return hip_status(ic::launch_indexer_decode(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I,
-                                                D_I, scores, ld, nullptr, st),
-                      "indexer launch");
+    return hip_status(launch_indexer(q_idx, w, k_idx, qs, H_I, D_I, scores, ld, nullptr, st), "indexer launch");
 }
 
 IC_EXPORT size_t ic_topk_workspace_size(const ic_queries *qs, int32_t k)
@@ -345,15 +360,16 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
         if (reuse_map[l] == l) {
             slot[l] = next_slot++;
             int32_t *idx = index_cache + slot[l] * slot_elems;
+            // the per-query key stream also fills the top-k's first-digit histogram
+            const bool fused_hist = qs->max_n > 0 && !use_prefill_indexer(qs, d->H_I, d->D_I);
             if (qs->max_n > 0) {
-                hipError_t e = ic::launch_indexer_decode(y.q_idx, y.w, y.k_idx, qs->base, qs->n_valid, qs->T,
-                                                         qs->max_n, d->H_I, d->D_I, scores, L.ld,
-                                                         ic::topk_hist0(topk_ws), st);
+                hipError_t e = launch_indexer(y.q_idx, y.w, y.k_idx, qs, d->H_I, d->D_I, scores, L.ld,
+                                              fused_hist ? ic::topk_hist0(topk_ws) : nullptr, st);
                 if (e != hipSuccess)
                     return hip_status(e, "layer stack: indexer launch");
             }
             hipError_t e = ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx, topk_ws,
-                                           qs->max_n > 0, st);
+                                           fused_hist, st);
             if (e != hipSuccess)
                 return hip_status(e, "layer stack: top-k launch");
         }

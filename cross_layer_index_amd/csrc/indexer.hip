@@ -181,6 +181,135 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
     return hipGetLastError();
 }
 
+// ---- prefill form ------------------------------------------------------------
+// All queries read one sequence (causal prefill: query t sees tokens
+// 0..n_t-1 of the shared cache), so a key tile staged in LDS serves a group of
+// 16 queries: 8 waves x 2 queries, each wave holding its queries' q fragments
+// and head weights in registers. Per 32-token group a wave reads the key
+// fragments from LDS once and runs 4 MFMAs per query. Key rows sit in LDS with
+// a 144-byte stride so the fragment reads (64 contiguous bytes per lane, lanes
+// on consecutive rows) hit distinct banks. The next tile is loaded into
+// registers while the current one is scored.
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kPfQW = 2;                                  // queries per wave
+constexpr int kPfQ = kPfWaves * kPfQW;                    // queries per workgroup
+constexpr int kPfTile = 256;                              // tokens per LDS tile
+constexpr int kPfRow = 144;                               // LDS bytes per key row
+constexpr int kPfDI = 128;
+constexpr int kPfLoads = kPfTile * kPfDI / 16 / kPfThreads;   // 16-byte loads per thread per tile
+
+__global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
+    const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
+    const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t T, float *__restrict__ scores,
+    int64_t ld, int64_t chunk)
+{
+    using G = IdxGeom<kPfDI>;
+    __shared__ __attribute__((aligned(16))) uint8_t keys[2][kPfTile * kPfRow];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;
+    const int j = lane & 31;
+    const int t_base = blockIdx.y * kPfQ;
+
+    // causal extent of the group: the largest n among its queries
+    int64_t nmax = 0;
+    for (int i = 0; i < kPfQ; ++i)
+        if (t_base + i < T)
+            nmax = max(nmax, (int64_t)n[t_base + i]);
+    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
+    if (s_begin >= nmax)
+        return;
+    const int64_t s_end = min(nmax, s_begin + chunk);
+    const uint8_t *krows = k_idx + base[t_base] * kPfDI;
+
+    int tq[kPfQW];
+    int64_t nq[kPfQW];
+    v8i a[kPfQW][2][G::KS];
+    float wr[kPfQW][2][16];
+#pragma unroll
+    for (int i = 0; i < kPfQW; ++i) {
+        tq[i] = t_base + wave * kPfQW + i;
+        const bool ok = tq[i] < T;
+        nq[i] = ok ? n[tq[i]] : 0;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int h = 32 * mt + j;
+            if (ok)
+                load_run<kPfDI>(q_idx + ((int64_t)tq[i] * 64 + h) * kPfDI + g * G::HALF, a[i][mt]);
+            else
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks)
+                    a[i][mt][ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hh = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+                wr[i][mt][r] = ok ? w[(int64_t)tq[i] * 64 + hh] : 0.0f;
+            }
+        }
+    }
+
+    // tile loads: chunk c of the tile = (row c / 8, 16-byte column c % 8)
+    uint4 pre[kPfLoads];
+    auto fetch = [&](int64_t tile) {
+#pragma unroll
+        for (int u = 0; u < kPfLoads; ++u) {
+            const int c = tid + u * kPfThreads;
+            int64_t row = tile + (c >> 3);
+            row = row < s_end ? row : s_end - 1;
+            pre[u] = *reinterpret_cast<const uint4 *>(krows + row * kPfDI + (c & 7) * 16);
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kPfLoads; ++u) {
+            const int c = tid + u * kPfThreads;
+            *reinterpret_cast<uint4 *>(&keys[buf][(c >> 3) * kPfRow + (c & 7) * 16]) = pre[u];
+        }
+    };
+
+    fetch(s_begin);
+    int buf = 0;
+    for (int64_t tile = s_begin; tile < s_end; tile += kPfTile, buf ^= 1) {
+        stage(buf);
+        __syncthreads();
+        if (tile + kPfTile < s_end)
+            fetch(tile + kPfTile);
+        const int groups = (int)min((int64_t)(kPfTile / 32), (s_end - tile + 31) / 32);
+        for (int grp = 0; grp < groups; ++grp) {
+            const uint8_t *kr = &keys[buf][(32 * grp + j) * kPfRow + g * G::HALF];
+            v8i b[G::KS];
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                const uint4 lo = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+                const uint4 hi = *reinterpret_cast<const uint4 *>(kr + 32 * ks + 16);
+                b[ks] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            const int64_t s = tile + 32 * grp + j;
+#pragma unroll
+            for (int i = 0; i < kPfQW; ++i) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < G::KS; ++ks)
+                        acc = mfma_fp8_32x32x64(a[i][mt][ks], b[ks], acc);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        sum = fmaf(wr[i][mt][r], fmaxf(acc[r], 0.0f), sum);
+                }
+                sum += __shfl_xor(sum, 32);
+                if (g == 0 && s < nq[i])
+                    scores[(int64_t)tq[i] * ld + s] = sum;
+            }
+        }
+        // no barrier here: buffer `buf` is next written two tiles on, after the
+        // barrier that follows the other buffer's staging
+    }
+}
+
 }  // namespace
 
 hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
@@ -194,6 +323,29 @@ hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uin
     case 128: return launch_decode_di<128>(q_idx, w, k_idx, base, n, T, max_n, H_I, scores, ld, hist0, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+bool indexer_prefill_supported(int32_t H_I, int32_t D_I) { return H_I == 64 && D_I == kPfDI; }
+
+hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                  const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                  int32_t H_I, int32_t D_I, float *scores, int64_t ld, hipStream_t stream)
+{
+    if (!indexer_prefill_supported(H_I, D_I))
+        return hipErrorInvalidValue;
+    if (T == 0 || max_n == 0)
+        return hipSuccess;
+    const int64_t groups = (T + kPfQ - 1) / kPfQ;
+    // token chunks: enough workgroups to fill the chip several times over
+    int64_t chunk = kPfTile;
+    while (chunk < max_n && groups * ((max_n + chunk - 1) / chunk) > 16384)
+        chunk *= 2;
+    const int64_t nchunks = (max_n + chunk - 1) / chunk;
+    if (groups > 65535)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)nchunks, (unsigned)groups), dim3(kPfThreads), 0,
+                       stream, q_idx, w, k_idx, base, n, T, scores, ld, chunk);
+    return hipGetLastError();
 }
 
 }  // namespace ic

@@ -37,6 +37,7 @@ constexpr int kTile = 32;                 // gathered rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMInit = -1.0e30f;        // finite "minus infinity" for partials
 constexpr int kMaxRowsPerSplit = 2048;    // index entries one workgroup handles
+constexpr float kSlack = 8.0f;            // lazy-rescale slack, log2 units
 
 __device__ __forceinline__ f4 mfma_bf16_16x16x32(const bf16x8 &a, const bf16x8 &b, const f4 &c)
 {
@@ -170,17 +171,18 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
                 *reinterpret_cast<uint4 *>(&Ks[(4 * rq + r) * G::KROW + 8 * ch]) = v[r];
             }
             if (8 * ch < DV) {
+                // element e of the 4 rows -> V^T[8*ch + e][4*rq .. 4*rq+3]; a byte
+                // permute packs two rows' 16-bit elements per dword
                 const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
                 const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
                 const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
                 const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int sh = (e & 1) * 16;
-                    const uint32_t a0 = (w0[e >> 1] >> sh) & 0xFFFFu, a1 = (w1[e >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t a2 = (w2[e >> 1] >> sh) & 0xFFFFu, a3 = (w3[e >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
                     *reinterpret_cast<uint2 *>(&Vt[(8 * ch + e) * G::VROW + 4 * rq]) =
-                        make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+                        make_uint2(__builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel),
+                                   __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel));
                 }
             }
         }
@@ -230,39 +232,47 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - m_new);
+        // Lazy rescaling: the reference point m_run only moves when a column's
+        // maximum exceeds it by more than kSlack (log2 units), so most tiles
+        // skip the O rescale; exponents stay <= 2^kSlack, exact in fp32/bf16 range.
+        const bool grow = mt > m_run + kSlack;
+        float al[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        const bool rescale = __any(grow);
+        if (rescale) {
+            const float m_new = grow ? mt : m_run;
+            const float alpha = exp2f(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                al[r] = __shfl(alpha, 4 * g + r);   // O rows are heads 4*g + r
+        }
         float p[8];
         float ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            p[i] = exp2f(s[i] - m_new);
+            p[i] = exp2f(s[i] - m_run);
             ps += p[i];
         }
         ps += __shfl_xor(ps, 16);
         ps += __shfl_xor(ps, 32);
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
-        // O rows are heads 4*g + r: fetch their rescale factors
-        float al[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            al[r] = __shfl(alpha, 4 * g + r);
-        const bool rescale = __any(alpha != 1.0f);
+        l_run += ps;
         const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         const bf16x8 pa = as_bf16x8(pw);
+        if (__builtin_amdgcn_readfirstlane(rescale)) {   // rare: a branch, not selects
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[nt][r] *= al[r];
+        }
 #pragma unroll
         for (int nt = 0; nt < G::NTV; ++nt) {
             const uint16_t *vr = &Vt[(16 * nt + c) * G::VROW + 4 * g];
             const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
             const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16);
             const bf16x8 vb = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-            if (rescale) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[nt][r] *= al[r];
-            }
             o[nt] = mfma_bf16_16x16x32(pa, vb, o[nt]);
         }
     }

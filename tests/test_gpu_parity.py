@@ -47,6 +47,10 @@ SMALL = {
     "edges": W.scaled(W.WORKLOADS["edge_lengths"], T=8, lengths=[0, 1, 31, 33, 255, 257, 700, 2049]),
     "hi40_di64": W.scaled(W.WORKLOADS["decode_128k"], H_I=40, D_I=64, T=3, lengths=[1000, 77, 1300]),
     "di32_hi64": W.scaled(W.WORKLOADS["decode_128k"], H_I=64, D_I=32, T=2, lengths=[513, 999]),
+    # causal prefill over one shared cache (the key-sharing kernel)
+    "prefill_tail": W.scaled(W.WORKLOADS["prefill_1m"], T=37, prefill_first_pos=2900, prefill_rows=3000),
+    "prefill_diag": W.scaled(W.WORKLOADS["prefill_1m"], T=300, prefill_first_pos=0, prefill_rows=300),
+    "prefill_long": W.scaled(W.WORKLOADS["prefill_1m"], T=20, prefill_first_pos=70000, prefill_rows=70100),
 }
 
 
