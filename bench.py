@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Throughput of the IndexCache sparse-attention hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: indexer -> top-k ->
-sparse MLA with sink, through ic_layer_stack. The default workload is one full
-decode layer at batch 1 over a 131,072-token cache (indexer 64x128 fp8, top-2048,
-MLA 128 heads over 576-wide bf16 latent rows). Inputs are resident in HBM
-before timing starts; R independently seeded input sets are rotated so that
-the working set (R x ~168 MB) does not fit in the 256 MB Infinity Cache.
+A step is one pass of the whole path over one batch, through ic_layer_stack:
+for every full layer indexer -> top-k -> stored index, for every layer sparse
+MLA with sink over its (own or inherited) index. The default workload is one
+full decode layer at batch 1 over a 131,072-token cache (indexer 64x128 fp8,
+top-2048, MLA 128 heads over 576-wide bf16 latent rows). Inputs are resident in
+HBM before timing starts; for the default workload R independently seeded input
+sets are rotated so that the working set (R x ~168 MB) does not fit in the
+256 MB Infinity Cache.
 
-Prints one JSON line (rank 0). Other workloads (--workload) are for reports;
-the default line is the headline figure.
+Prints one JSON line. The default line is the headline figure; --workload
+selects the other synthetic workloads for reports (the 78-layer stack line
+also carries the all-full-layers comparison).
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "decode query-layers/s at L=128K (index+topk+sparse MLA); % of HBM roofline"
 
 
 def algorithmic_bytes(n: int, k: int, H_I: int, D_I: int, H: int, D_qk: int, D_v: int, full: bool):
@@ -44,18 +48,40 @@ def indexer_bytes(n: int, H_I: int, D_I: int) -> int:
     return D_I * n + H_I * (D_I + 4)
 
 
+def indexer_flops(n: int, H_I: int, D_I: int) -> int:
+    return 2 * H_I * D_I * n
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    import glob
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "cross_layer_index_amd", "csrc", "indexer.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for m in re.finditer(r"<!-- traffic: (.*?) -->", open(path).read()):
+            f = dict(kv.split("=", 1) for kv in m.group(1).split())
+            if f.get("kernel") == kernel and f.get("workload") == workload and f.get("source_sha256") == digest:
+                return float(f["bytes_per_launch"])
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="decode_128k")
-    ap.add_argument("--sets", type=int, default=8, help="rotating input sets")
+    ap.add_argument("--workload", default="decode_128k",
+                    choices=["decode_128k", "ragged_64", "stack_78", "prefill_1m", "tiny_2layer"])
+    ap.add_argument("--sets", type=int, default=None, help="rotating input sets (default 8 for decode_128k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-steps", type=int, default=400, help="launches timed for the dominant kernel")
-    ap.add_argument("--only", choices=["all", "step", "indexer"], default="all",
-                    help="profiling aid: run only the stack steps or only the indexer launches")
+    ap.add_argument("--only", choices=["all", "step", "indexer", "copy"], default="all",
+                    help="profiling aid: run only the stack steps, only the dominant-kernel launches, or "
+                         "only a plain 256 MiB device copy (the calibration for HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -66,7 +92,6 @@ def main():
                                    "(the path shards by sequence, see the design notes)"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from cross_layer_index_amd import ic
@@ -74,40 +99,52 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "copy":
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.kernel_steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read_per_copy": src.numel() * 4, "copies": args.kernel_steps}))
+        return
     wl = W.WORKLOADS[args.workload]
-    R = max(1, args.sets)
+    R = args.sets if args.sets is not None else (8 if wl.name == "decode_128k" else 1)
     n = wl.n_valid()
+    nn = [int(x) for x in n.tolist()]
     qs = ic.make_queries(wl.base(), n, wl.rows(), wl.same_seq, device=dev)
     d = ic.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v)
     rmap = ic.reuse_map_last_full(wl.is_full())
+    small = wl.rows() * wl.D_qk * 2 * wl.n_layers < (1 << 30)
+    cpu_wanted = not args.no_cpu_baseline and args.only == "all"
 
-    # ---- inputs: set 0 from the CPU generator (what the oracle sees), the
-    # rest from the device generator with their own seeds
-    host0 = [W.layer_inputs(wl, l) for l in range(wl.n_layers)] if not args.no_cpu_baseline else None
+    # ---- inputs: set 0 of the small workloads from the CPU generator (what the
+    # oracle sees), everything else from the device generator
+    host0 = None
+    if cpu_wanted and small:
+        host0 = [W.layer_inputs(wl, l, with_indexer=(rmap[l] == l)) for l in range(wl.n_layers)]
     sets = []
     for i in range(R):
         wli = wl if i == 0 else W.scaled(wl, seed=wl.seed * 1000 + i)
         lays = []
         for l in range(wl.n_layers):
             full = rmap[l] == l
-            if i == 0 and host0 is not None:
+            if host0 is not None and i == 0:
                 x = host0[l]
                 li = W.LayerInputs(*[None if t is None else t.to(dev) for t in
                                      (x.q_idx, x.w, x.k_idx, x.q, x.kv, x.sink)])
             else:
-                li = W.layer_inputs(wli, l, device=dev, with_indexer=full)
+                li = W.layer_inputs(wli, l, device=dev, with_indexer=full or wl.name == "stack_78")
             out = torch.empty((wl.T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
             lays.append(dict(q_idx=li.q_idx, w=li.w, k_idx=li.k_idx, q=li.q, kv=li.kv, sink=li.sink, out=out))
         sets.append(ic.LayerStack(lays, rmap, qs, d, wl.scale, device=dev))
     torch.cuda.synchronize()
 
-    # ---- graphs: one step per set, plus a long chain of R*4 steps
     def capture(fns):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for f in fns:          # warm the capture stream once
+            for f in fns:          # run once on the capture stream first
                 f()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
@@ -117,106 +154,159 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    chain = 4 * R
-    step_fns = [sets[i % R] for i in range(chain)]
-    g_chain = capture(step_fns)
-    g_one = [capture([sets[i]]) for i in range(R)]
+    def runner(fns):
+        """Callable running K steps (rotating over fns), through HIP graphs
+        when a step is short enough for launch overhead to matter."""
+        t0 = time.perf_counter()
+        fns[0]()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > 0.05:
+            def run(K):
+                for i in range(K):
+                    fns[i % len(fns)]()
+            return run
+        chain = 4 * len(fns)
+        g_chain = capture([fns[i % len(fns)] for i in range(chain)])
+        g_one = [capture([f]) for f in fns]
 
-    def run_steps(K):
-        for _ in range(K // chain):
-            g_chain.replay()
-        for i in range(K % chain):
-            g_one[i % R].replay()
+        def run(K):
+            for _ in range(K // chain):
+                g_chain.replay()
+            for i in range(K % chain):
+                g_one[i % len(fns)].replay()
+        return run
 
+    def timed(run, K, W_):
+        run(W_)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        run(K)
+        e1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+
+    big = wl.name in ("stack_78", "prefill_1m")
+    steps = min(args.steps, 20) if big else args.steps
+    warm = min(args.warmup, 2) if big else args.warmup
     result = {}
     if args.only in ("all", "step"):
-        run_steps(args.warmup)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run_steps(args.steps)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        ms = el * 1e3 / args.steps
-        ql_per_step = wl.T * wl.n_layers
-        result.update(value=ql_per_step * args.steps / el, ms_per_step=ms)
+        run = runner(sets)
+        el, _ = timed(run, steps, warm)
+        result.update(value=wl.T * wl.n_layers * steps / el, ms_per_step=el * 1e3 / steps)
+        if wl.name == "stack_78":
+            ident = list(range(wl.n_layers))
+            allfull = [ic.LayerStack(s.layers, ident, qs, d, wl.scale, device=dev) for s in sets]
+            el2, _ = timed(runner(allfull), steps, warm)
+            result["all_full"] = {"value": wl.T * wl.n_layers * steps / el2, "ms_per_step": el2 * 1e3 / steps,
+                                  "indexer_passes": wl.n_layers}
+            result["indexcache_speedup"] = el2 / el
+            del allfull
 
     # ---- dominant kernel: the indexer, timed alone with events on its stream
-    idx_ms = None
+    k_ms = None
     if args.only in ("all", "indexer"):
-        scores = [torch.empty((wl.T, ic.score_ld(qs.max_n)), dtype=torch.float32, device=dev) for _ in range(R)]
         full0 = rmap.index(0)
+        scores = [torch.empty((wl.T, ic.score_ld(qs.max_n)), dtype=torch.float32, device=dev) for _ in range(R)]
 
         def idx_fn(i):
             y = sets[i].layers[full0]
             return lambda: ic.indexer_score(y["q_idx"], y["w"], y["k_idx"], qs, scores[i])
 
-        g_idx = capture([idx_fn(i % R) for i in range(chain)])
-        for _ in range(max(1, args.warmup // chain)):
-            g_idx.replay()
-        reps = max(1, args.kernel_steps // chain)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            g_idx.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        idx_ms = e0.elapsed_time(e1) / (reps * chain)
+        fns = [idx_fn(i) for i in range(R)]
+        ksteps = min(args.kernel_steps, 10) if big else args.kernel_steps
+        _, ev = timed(runner(fns), ksteps, min(warm, ksteps))
+        k_ms = ev * 1e3 / ksteps
 
     if args.only != "all":
-        print(json.dumps({"only": args.only, **result, "indexer_ms": idx_ms}))
+        print(json.dumps({"only": args.only, "workload": wl.name, **result, "indexer_ms": k_ms}))
         return
 
-    nn = n.numpy()
-    full_layers = sum(1 for l in range(wl.n_layers) if rmap[l] == l)
-    idx_bytes = sum(indexer_bytes(int(x), wl.H_I, wl.D_I) for x in nn)
-    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    n_full = sum(1 for l in range(wl.n_layers) if rmap[l] == l)
+    if wl.same_seq:
+        fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
+        achieved = fl / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None, "kernel": "indexer_prefill_kernel",
+                "kernel_ms": k_ms, "algorithmic_flops_per_launch": fl}
+    else:
+        by = sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn)
+        achieved = by / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("indexer_decode_kernel", wl.name),
+                "kernel": "indexer_decode_kernel",
+                "kernel_ms": k_ms, "algorithmic_bytes_per_launch": by}
 
-    # ---- CPU baseline: the oracle on this host, rank 0 only
+    # ---- CPU baseline: the oracle on this host, on a bounded sample
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_wanted:
         import oracle
         threads = len(os.sched_getaffinity(0))
-        os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-        x = host0
-        base, nv = wl.base().numpy(), nn
+        if host0 is not None:
+            x, base, nv, layers_used, qn = host0, wl.base().numpy(), n.numpy(), wl.n_layers, wl.T
+            sample = f"full passes of input set 0 ({wl.n_layers} layer(s) x {wl.T} queries)"
+        else:
+            # one query through a full and a shared layer, copied back from the device
+            import numpy as np
+            t = 0
+            rows = slice(int(qs.base[t]), int(qs.base[t]) + nn[t])
+            src = sets[0].layers
+            l_sh = next((l for l in range(wl.n_layers) if rmap[l] != l), None)
+            used = [0] + ([l_sh] if l_sh is not None else [])
+
+            class L:
+                pass
+            x = []
+            for j, l in enumerate(used):
+                o = L()
+                y = src[l]
+                o.q_idx = y["q_idx"][t:t + 1].cpu() if j == 0 else None
+                o.w = y["w"][t:t + 1].cpu() if j == 0 else None
+                o.k_idx = y["k_idx"][rows].cpu() if j == 0 else None
+                o.q, o.kv, o.sink = y["q"][t:t + 1].cpu(), y["kv"][rows].cpu(), y["sink"].cpu()
+                x.append(o)
+            rmap_s = [0] + ([0] if l_sh is not None else [])
+            base, nv, layers_used, qn = np.array([0], np.int64), np.array([nn[t]], np.int32), len(used), 1
+            rmap_cpu = rmap_s
+            sample = (f"query 0 through a full{' and a shared' if l_sh is not None else ''} layer "
+                      f"(L={nn[t]}), repeated")
+        rm = rmap if host0 is not None else rmap_cpu
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.layer_stack(x, rmap, base, nv, wl.k, wl.scale, wl.D_v)
+            oracle.layer_stack(x, rm, base, nv, wl.k, wl.scale, wl.D_v)
             reps += 1
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
-        cpu = {"value": reps * wl.T * wl.n_layers / el, "unit": "query-layers/s",
-               "cores": int(os.environ.get("OMP_NUM_THREADS", threads)), "kind": "oracle",
-               "sample": f"{reps} full passes of input set 0 ({wl.n_layers} layer(s) x {wl.T} query, "
-                         f"L={int(nn.max())}) through the C oracle (fp64, OpenMP)"}
+        cpu = {"value": reps * qn * layers_used / el, "unit": "query-layers/s", "cores": threads, "kind": "oracle",
+               "sample": f"{reps} x {sample} through the C oracle (fp64, OpenMP, {threads} threads)"}
 
     line = {
-        "metric": "decode query-layers/s at L=128K (index+topk+sparse MLA); % of HBM roofline",
+        "metric": METRIC if wl.name == "decode_128k" else f"{wl.name} query-layers/s (index+topk+sparse MLA)",
         "value": result["value"],
         "unit": "query-layers/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warm,
         "ms_per_step": result["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3+bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "L": int(nn.max()), "layers": wl.n_layers,
-                   "full_layers": full_layers, "k": wl.k, "H_I": wl.H_I, "D_I": wl.D_I, "H": wl.H,
-                   "D_qk": wl.D_qk, "D_v": wl.D_v, "rotating_sets": R, "graph": True},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "indexer_decode_kernel", "kernel_ms": idx_ms,
-                     "algorithmic_bytes_per_launch": idx_bytes},
+        "config": {"workload": wl.name, "T": wl.T, "L": max(nn) if nn else 0, "layers": wl.n_layers,
+                   "full_layers": n_full, "k": wl.k, "H_I": wl.H_I, "D_I": wl.D_I, "H": wl.H,
+                   "D_qk": wl.D_qk, "D_v": wl.D_v, "rotating_sets": R},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
-    step_bytes = sum(algorithmic_bytes(int(x), wl.k, wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, rmap[l] == l)
+    step_bytes = sum(algorithmic_bytes(x, wl.k, wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, rmap[l] == l)
                      for l in range(wl.n_layers) for x in nn)
     line["step_hbm_frac"] = step_bytes / (result["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    for k2 in ("all_full", "indexcache_speedup"):
+        if k2 in result:
+            line[k2] = result[k2]
     print(json.dumps(line))
 
 
