@@ -24,8 +24,11 @@
 //     (topk_finish_kernel). The kernel boundary orders the two phases.
 //   * row path (many queries): one workgroup per query streams its row once
 //     more to collect survivors into LDS and finishes there.
-// If the survivors exceed the LDS list (heavy ties), the finishing workgroup
-// falls back to digit passes over the full row, which is always correct.
+// When the survivors exceed the LDS list (the threshold fell into a dense
+// first-digit bin), the finishing workgroup histograms the second digit over
+// the survivors kept in global memory and keeps only those at or above the
+// second-digit threshold, which fit; only ties spanning more than the list at
+// 21 bits of the key fall back to digit passes over the full row.
 // The first-digit histogram is kept in kHistCopies copies per query (adders
 // pick a copy by workgroup index, which spreads atomic traffic); the workspace
 // holds them zeroed on entry and the finishing workgroup zeroes them again.
@@ -41,6 +44,7 @@ constexpr int kSplitChunk = kSplitThreads * 4;   // scores per split workgroup
 constexpr int kRowThreads = 1024;
 constexpr int kListCap = 8192;          // survivors held in LDS
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
+constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
 
 // Block-wide inclusive scan of one uint32 per thread.
 template <int NT>
@@ -153,6 +157,91 @@ struct ListSrc {
     }
 };
 
+// A contiguous (key << 32 | position) list in global memory, position order.
+struct GListSrc {
+    const uint64_t *list;
+    int64_t n;
+    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ok[e] = i + e < n;
+            const uint64_t v = ok[e] ? list[i + e] : 0ull;
+            key[e] = (uint32_t)(v >> 32);
+            pos[e] = (int64_t)(uint32_t)v;
+        }
+    }
+};
+
+// The survivor slices of the split path read as one list: element i lives in
+// the last slice whose starting offset (offs, in LDS) is <= i.
+struct SliceSrc {
+    const uint64_t *regions;   // this query's P slices of `chunk` entries
+    const uint32_t *offs;      // [P + 1] exclusive offsets
+    int P;
+    int chunk;
+    int64_t n;
+    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = (uint32_t)(i + e);
+            ok[e] = i + e < n;
+            uint64_t v = 0;
+            if (ok[e]) {
+                int lo = 0, hi = P;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (offs[mid] <= x)
+                        lo = mid;
+                    else
+                        hi = mid;
+                }
+                v = regions[(int64_t)lo * chunk + (x - offs[lo])];
+            }
+            key[e] = (uint32_t)(v >> 32);
+            pos[e] = (int64_t)(uint32_t)v;
+        }
+    }
+};
+
+// Ordered compaction of the entries with key >= bound into an LDS list (the
+// first lcap) and, if given, a global list (the first gcap). Returns the count.
+template <int NT, class Src>
+__device__ uint32_t collect(const Src &src, uint32_t bound, Shared &sh, uint64_t *lds, uint32_t lcap,
+                            uint64_t *glist, uint32_t gcap)
+{
+    uint32_t total = 0;
+    for (int64_t c0 = 0; c0 < src.n; c0 += (int64_t)NT * 4) {
+        uint32_t key[4];
+        int64_t pos[4];
+        bool ok[4];
+        src.get4(c0 + (int64_t)threadIdx.x * 4, key, pos, ok);
+        uint32_t sv[4], ls = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = ok[e] && key[e] >= bound;
+            ls += sv[e];
+        }
+        uint32_t tot;
+        uint32_t o = total + block_scan<NT>(ls, sh.waves, &tot) - ls;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (sv[e]) {
+                const uint64_t v = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
+                if (o < lcap)
+                    lds[o] = v;
+                if (glist && o < gcap)
+                    glist[o] = v;
+                ++o;
+            }
+        }
+        total += tot;
+    }
+    __syncthreads();
+    return total;
+}
+
 // Digit passes `first`..2 over `src`, then the ordered compaction into out[0..k).
 template <int NT, class Src>
 __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t prefix, uint32_t pmask,
@@ -222,6 +311,39 @@ __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t pr
         if (run_gt + min(run_eq, need) >= (uint32_t)k)
             break;
     }
+}
+
+// Finish from a survivor list `src` (keys with first digit >= d0, position
+// order, `total` entries) that does not fit the LDS list: histogram the second
+// digit over the first-digit bin, keep only keys at or above the second-digit
+// threshold (they fit unless ties span the list), finish from the third digit.
+template <int NT, class Src, class Fallback>
+__device__ void finish_from_overflow(const Src &src, const Fallback &row, Shared &sh, uint64_t *list, uint32_t d0,
+                                     uint32_t need0, int32_t k, int32_t *__restrict__ out)
+{
+    const uint32_t p0 = d0 << 21;
+    for (int i = threadIdx.x; i < kBins0; i += NT)
+        sh.hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = (int64_t)threadIdx.x * 4; i < src.n; i += (int64_t)NT * 4) {
+        uint32_t key[4];
+        int64_t pos[4];
+        bool ok[4];
+        src.get4(i, key, pos, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (ok[e] && (key[e] & 0xFFE00000u) == p0)
+                atomicAdd(&sh.hist[(key[e] >> 10) & 2047], 1u);
+    }
+    __syncthreads();
+    uint32_t d1, above1;
+    find_digit<NT>(sh, 2048, need0, d1, above1);
+    const uint32_t bound = p0 | (d1 << 10);
+    const uint32_t cnt = collect<NT>(src, bound, sh, list, (uint32_t)kListCap, nullptr, 0);
+    if (cnt <= (uint32_t)kListCap)
+        finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
+    else
+        finish_select<NT>(row, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
 }
 
 template <int NT>
@@ -374,6 +496,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
         offs[P] = total;
     __syncthreads();
     const uint32_t need = (uint32_t)k - above0;
+    const SliceSrc slices{regions + (int64_t)t * P * kSplitChunk, offs, P, kSplitChunk, total};
     if (total <= (uint32_t)kListCap) {
         for (uint32_t i = tid; i < total; i += kRowThreads) {
             int lo = 0, hi = P;                   // last slice whose offset <= i
@@ -389,8 +512,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
         __syncthreads();
         finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
     } else {
-        finish_select<kRowThreads>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 1, d0 << 21, 0xFFE00000u, need, k,
-                                   out);
+        finish_from_overflow<kRowThreads>(slices, RowSrc{scores + (int64_t)t * ld, nt}, sh, list, d0, need, k, out);
     }
 }
 
@@ -400,7 +522,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__restrict__ scores, int64_t ld,
                                                                const int32_t *__restrict__ n, int32_t k,
                                                                int32_t *__restrict__ idx,
-                                                               uint32_t *__restrict__ hist0)
+                                                               uint32_t *__restrict__ hist0,
+                                                               uint64_t *__restrict__ surv)
 {
     __shared__ Shared sh;
     __shared__ uint64_t list[kListCap];
@@ -440,34 +563,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
     uint32_t d0, above0;
     find_digit<kRowThreads>(sh, kBins0, (uint32_t)k, d0, above0);
     const uint32_t need = (uint32_t)k - above0;
-    // collect survivors in position order
-    uint32_t total = 0;
-    for (int64_t c0 = 0; c0 < nt; c0 += (int64_t)kRowThreads * 4) {
-        uint32_t key[4];
-        int64_t pos[4];
-        bool ok[4];
-        src.get4(c0 + (int64_t)tid * 4, key, pos, ok);
-        uint32_t sv[4], ls = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = ok[e] && (key[e] >> 21) >= d0;
-            ls += sv[e];
-        }
-        uint32_t tot;
-        uint32_t o = total + block_scan<kRowThreads>(ls, sh.waves, &tot) - ls;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (sv[e]) {
-                if (o < (uint32_t)kListCap)
-                    list[o] = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
-                ++o;
-            }
-        }
-        total += tot;
-    }
-    __syncthreads();
+    // survivors in position order: into LDS, and into this query's global list
+    uint64_t *gl = surv + (int64_t)t * kRowSurvCap;
+    const uint32_t total = collect<kRowThreads>(src, d0 << 21, sh, list, (uint32_t)kListCap, gl,
+                                                (uint32_t)kRowSurvCap);
     if (total <= (uint32_t)kListCap)
         finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+    else if (total <= (uint32_t)kRowSurvCap)
+        finish_from_overflow<kRowThreads>(GListSrc{gl, total}, src, sh, list, d0, need, k, out);
     else
         finish_select<kRowThreads>(src, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
 }
@@ -496,7 +599,7 @@ TopkLayout topk_layout(int32_t T, int64_t max_n)
         L.total = L.regions_off + up256((size_t)T * L.P * kSplitChunk * 8);
     } else {
         L.regions_off = L.counts_off;
-        L.total = L.counts_off;
+        L.total = L.regions_off + up256((size_t)T * kRowSurvCap * 8);
     }
     return L;
 }
@@ -535,7 +638,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
                            idx, hist0, counts, regions, (int32_t)L.P);
     } else {
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
-                           hist_ready ? hist0 : nullptr);
+                           hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));
     }
     return hipGetLastError();
 }

@@ -95,10 +95,25 @@ def topk_case(name):
         n = np.array([1000, 3], np.int32)
         s = rng.integers(-5, 5, size=(2, 1000)).astype(np.float32)
         return s, n, 1
+    # every score in one first-digit bin: the survivor list overflows and the
+    # second digit must thin it (split path: few queries; row path: many)
+    if name == "dense_bin_split":
+        n = np.array([131072, 100000], np.int32)
+        return rng.integers(24576, 28672, size=(2, 131072)).astype(np.float32), n, 2048
+    if name == "dense_bin_row":
+        n = np.full(300, 12000, np.int32)
+        n[::7] = 11999
+        return rng.integers(24576, 28672, size=(300, 12000)).astype(np.float32), n, 2048
+    if name == "all_equal_row":
+        n = np.full(260, 9000, np.int32)
+        s = np.full((260, 9000), 7.0, np.float32)
+        s[:, ::1000] = 8.0
+        return s, n, 2048
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1"])
+@pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1",
+                                  "dense_bin_split", "dense_bin_row", "all_equal_row"])
 def test_topk_exact(gpu, orc, name):
     s, n, k = topk_case(name)
     T, L = s.shape
