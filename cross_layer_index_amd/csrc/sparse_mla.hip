@@ -9,16 +9,18 @@
 //
 // Work split: a workgroup (4 waves) owns 64 heads of one query and a range of
 // the index list; each wave owns 16 heads. Selected rows are gathered 32 at a
-// time into LDS twice: row-major (the K operand of QK^T, d contiguous) and
-// transposed over the value dims (the V operand of PV, rows contiguous).
+// time straight from HBM into a row-major LDS tile by global_load_lds_dwordx4
+// (no registers, no VALU; two tiles, one filling while the other is used).
 // Both products run on v_mfma_f32_16x16x32_bf16:
 //   S^T[j,h] = sum_d K[j,d] Q[h,d]      (A = gathered rows, B = q in registers)
 //   O[h,v]  += sum_j P[h,j] V[j,v]      (A = P straight from the S^T
-//                                         accumulators, B = transposed V)
+//                                         accumulators, B = V read from the
+//                                         same tile by ds_read_b64_tr_b16)
 // The accumulator of S^T puts (row 4*(l/16)+r, head l%16) in lane l, element
 // r; using that as P's K-slot order (slot 4*b + r <-> row 16*b + 4*(l/16) + r)
-// and reading V^T in the same order lets P feed the second product without
-// any data movement. Softmax runs online in fp32 in log2 units.
+// and letting the transposing LDS read deliver V in the same order lets P feed
+// the second product without any data movement. Softmax runs online in fp32
+// in log2 units.
 // When one query's list is split over several workgroups, each writes its
 // unnormalised partial (m, l, o) and a combine kernel merges them and adds the
 // sink once.
@@ -30,14 +32,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMlaThreads = 256;
+constexpr int kMlaThreads = 512;
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadsPerWG = 64;
 constexpr int kTile = 32;                 // gathered rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMInit = -1.0e30f;        // finite "minus infinity" for partials
 constexpr int kMaxRowsPerSplit = 2048;    // index entries one workgroup handles
-constexpr float kSlack = 8.0f;            // lazy-rescale slack, log2 units
+// Rescale slack (log2 units). Zero keeps the running maximum exact, so the
+// dominant key's P is exactly 1 and its bf16 rounding is error-free; a larger
+// slack would skip more rescales but lets every P carry bf16 rounding.
+constexpr float kSlack = 0.0f;
 
 __device__ __forceinline__ f4 mfma_bf16_16x16x32(const bf16x8 &a, const bf16x8 &b, const f4 &c)
 {
@@ -68,21 +73,58 @@ struct MlaGeom {
     static constexpr int KROW = DQKP + 8;        // LDS row stride (bf16)
     static constexpr int NCH = DQK / 8;          // 16-byte chunks per row
     static constexpr int NTV = DV / 16;          // value column tiles
-    static constexpr int VROW = kTile + 4;       // transposed-V row stride (bf16): 72 B keeps
-                                                 // the transposing writes conflict-free
     static_assert(DQK % 8 == 0 && DV % 16 == 0 && DV <= DQK, "shape");
 };
 
-// Rows of the KV cache a thread copies per tile: items of (row quad, 16-byte
-// chunk); the tile's loads are all issued before any is used.
-template <int DQK>
-struct Gather {
-    static constexpr int NCH = DQK / 8;
-    static constexpr int ITEMS = (kTile / 4) * NCH;
-    static constexpr int PER = (ITEMS + kMlaThreads - 1) / kMlaThreads;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one instruction.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf16x2));
+}
+
+// LDS tile: kTile gathered rows, row-major, each row padded to ROWCH 16-byte
+// chunks (one spare chunk). The pad shifts consecutive rows by 4 banks, so
+// lanes reading the same column of 16 consecutive rows hit distinct banks, and
+// every operand address is a per-lane base plus a compile-time offset. The tile
+// is filled by global_load_lds_dwordx4 instructions that each place 64 lanes x
+// 16 bytes contiguously; which (row, chunk) a lane fills in a given
+// instruction is the same for every tile and is computed once.
+template <int DQK, int DV>
+struct TileGeom {
+    using G = MlaGeom<DQK, DV>;
+    static constexpr int ROWCH = G::KROW * 2 / 16;             // chunks per LDS row
+    static constexpr int INSTR = (kTile * ROWCH + 63) / 64;    // fill instructions per tile
+    static constexpr int ELEMS = INSTR * 64 * 8;               // bf16 slots per buffer
+    static_assert((G::KROW * 2) % 16 == 0, "row stride");
 };
 
-// grid: (splits, ceil(H/64), T); block: 256.
+constexpr int kBuffers = 3;                 // tiles in flight per workgroup
+constexpr int kWaves = kMlaThreads / 64;
+constexpr int kFillPerWave = 5;             // >= ceil(fill instructions / waves)
+constexpr int kQkBatch = 5;                 // QK^T K-steps whose fragments are read together
+constexpr int kPvBatch = 4;                 // PV value tiles whose fragments are read together
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// grid: splits * ceil(H/64) * T workgroups (1-D; the work unit comes from the
+// linear id, see below); block: 512 = 4 head groups x 2 halves.
+// Wave w owns heads 16*(w%4) .. +16 of the workgroup's 64 and half h = w/4:
+// QK^T over its half of the 576 dims (partial scores are summed with the
+// partner wave's through LDS), then PV over its half of the 512 value dims.
+// Halving the q fragments and the O accumulators per wave lets two waves share
+// each SIMD, which hides LDS latency.
 template <int DQK, int DV>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const int64_t *__restrict__ base,
@@ -91,99 +133,91 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     float *__restrict__ part_o, float *__restrict__ part_ml)
 {
     using G = MlaGeom<DQK, DV>;
-    using GA = Gather<DQK>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * G::KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[DV * G::VROW];
-    __shared__ int32_t rowid[kMaxRowsPerSplit];
+    using TG = TileGeom<DQK, DV>;
+    constexpr int KSH = (G::KS + 1) / 2;          // K-steps per half
+    constexpr int NTH = G::NTV / 2;               // value tiles per half
+    static_assert(TG::INSTR <= kWaves * kFillPerWave, "fill instructions per wave");
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[kBuffers][TG::ELEMS];
+    __shared__ __attribute__((aligned(16))) f4 sx[kWaves][2][64];   // partial S^T per wave
+    __shared__ __attribute__((aligned(16))) int32_t rowid[kMaxRowsPerSplit + kTile];
 
-    const int split = blockIdx.x;
-    const int t = blockIdx.z;
+    // Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8).
+    // Consecutive ids on one XCD take the head groups of the same (query,
+    // split), so they gather the same rows through the same L2.
+    const int nhg = (H + kHeadsPerWG - 1) / kHeadsPerWG;
+    int split, hg, t;
+    {
+        const int L = blockIdx.x;
+        const int xcd = L & 7, slot = L >> 3;
+        const int unit_in_xcd = slot / nhg;
+        hg = slot - unit_in_xcd * nhg;
+        int unit = unit_in_xcd * 8 + xcd;
+        // the tail (ids beyond the last full group of 8 x nhg) maps linearly
+        const int full = (int)(gridDim.x / (8 * nhg)) * (8 * nhg);
+        if (L >= full) {
+            unit = full / nhg + (L - full) / nhg;
+            hg = (L - full) % nhg;
+        }
+        split = unit % splits;
+        t = unit / splits;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int hgrp = wave & 3;
+    const int half = wave >> 2;
     const int c = lane & 15;
     const int g = lane >> 4;
-    const int h0 = blockIdx.y * kHeadsPerWG + wave * kHeadsPerWave;
+    const int h0 = hg * kHeadsPerWG + hgrp * kHeadsPerWave;
     const int hc = h0 + c;                        // head of this lane's S^T column
     const int64_t b_t = base[t];
     const int j_begin = split * rows_per_split;
     const int j_end = min(k, j_begin + rows_per_split);
     const int nrows = j_end - j_begin;
-    // a row every thread may always read: this query's own q row (used in place
-    // of empty index slots, whose data is then replaced by zeros)
+    const int ks0 = half * KSH;
+    const int nt0 = half * NTH;
+    // finite data any lane may always read: this query's own q row (used for
+    // empty index slots and for padding chunks; the math never uses it)
     const uint16_t *safe_row = q + (int64_t)t * H * DQK;
 
-    // the split's index list, kept in LDS
-    for (int i = tid; i < nrows; i += kMlaThreads)
-        rowid[i] = idx[(int64_t)t * k + j_begin + i];
+    // the split's index list in LDS, padded with empty slots to whole tiles
+    const int padded = (nrows + kTile - 1) / kTile * kTile;
+    for (int i = tid; i < padded; i += kMlaThreads)
+        rowid[i] = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
 
-    // q fragments: lane (head hc, group g) holds d = 32*ks + 8*g .. +8
-    bf16x8 qf[G::KS];
+    // q fragments of this half: lane (head hc, group g) holds d = 32*ks + 8*g .. +8
+    bf16x8 qf[KSH];
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-        const int d0 = 32 * ks + 8 * g;
+    for (int i = 0; i < KSH; ++i) {
+        const int d0 = 32 * (ks0 + i) + 8 * g;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (hc < H && d0 < DQK)
+        if (hc < H && ks0 + i < G::KS && d0 < DQK)
             v = *reinterpret_cast<const uint4 *>(q + ((int64_t)t * H + hc) * DQK + d0);
-        qf[ks] = as_bf16x8(v);
+        qf[i] = as_bf16x8(v);
     }
-    // padded K columns (d >= DQK) stay zero for the whole kernel
-    if (G::DQKP > DQK) {
-        for (int i = tid; i < kTile * (G::DQKP - DQK) / 8; i += kMlaThreads) {
-            const int r = i / ((G::DQKP - DQK) / 8);
-            const int ch = i % ((G::DQKP - DQK) / 8);
-            *reinterpret_cast<uint4 *>(&Ks[r * G::KROW + DQK + 8 * ch]) = make_uint4(0, 0, 0, 0);
-        }
+
+    // (row, chunk) this lane fills in each of this wave's fill instructions
+    int fill_row[kFillPerWave], fill_ch[kFillPerWave];
+#pragma unroll
+    for (int i = 0; i < kFillPerWave; ++i) {
+        const int chunk = (wave + kWaves * i) * 64 + lane;
+        fill_row[i] = chunk / TG::ROWCH;
+        fill_ch[i] = chunk - fill_row[i] * TG::ROWCH;
     }
     __syncthreads();
 
-    // row id of tile-local row j of the tile starting at list offset j0 (-1 = empty)
-    auto rid_of = [&](int j0, int j) -> int { return j0 + j < nrows ? rowid[j0 + j] : -1; };
-
-    uint4 pre[GA::PER][4];
-    auto prefetch = [&](int j0) {
+    auto issue = [&](int buf, int j0) {
+        uint16_t *tile = tiles[buf];
 #pragma unroll
-        for (int it = 0; it < GA::PER; ++it) {
-            const int item = tid + it * kMlaThreads;
-            const int rq = item & 7;
-            const int ch = min(item >> 3, GA::NCH - 1);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rid = rid_of(j0, 4 * rq + r);
-                const uint16_t *p = rid >= 0 ? kv + (b_t + rid) * DQK : safe_row;
-                pre[it][r] = *reinterpret_cast<const uint4 *>(p + 8 * ch);
-            }
-        }
-    };
-    // write the prefetched tile: row-major K, transposed V (zeros for empty slots)
-    auto commit = [&](int j0) {
-#pragma unroll
-        for (int it = 0; it < GA::PER; ++it) {
-            const int item = tid + it * kMlaThreads;
-            if (item >= GA::ITEMS)
-                continue;
-            const int rq = item & 7;
-            const int ch = item >> 3;
-            uint4 v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v[r] = rid_of(j0, 4 * rq + r) >= 0 ? pre[it][r] : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(&Ks[(4 * rq + r) * G::KROW + 8 * ch]) = v[r];
-            }
-            if (8 * ch < DV) {
-                // element e of the 4 rows -> V^T[8*ch + e][4*rq .. 4*rq+3]; a byte
-                // permute packs two rows' 16-bit elements per dword
-                const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-                const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-                const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-                const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    *reinterpret_cast<uint2 *>(&Vt[(8 * ch + e) * G::VROW + 4 * rq]) =
-                        make_uint2(__builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel),
-                                   __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel));
-                }
+        for (int i = 0; i < kFillPerWave; ++i) {
+            const int m = wave + kWaves * i;
+            if (m < TG::INSTR) {
+                const int r = fill_row[i];
+                const int ch = fill_ch[i];
+                const int rid = r < kTile ? rowid[j0 + r] : -1;
+                const uint16_t *src = (rid >= 0 && ch < G::NCH) ? kv + (b_t + rid) * DQK + 8 * ch
+                                                                 : safe_row + 8 * (ch < G::NCH ? ch : 0);
+                __builtin_amdgcn_global_load_lds(src, (lds_void *)(tile + m * 64 * 8), 16, 0, 0);
             }
         }
     };
@@ -196,51 +230,74 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         m_run = kMInit;
         l_run = 0.0f;
     }
-    f4 o[G::NTV];
+    f4 o[NTH];
 #pragma unroll
-    for (int nt = 0; nt < G::NTV; ++nt)
-        o[nt] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NTH; ++i)
+        o[i] = f4{0.f, 0.f, 0.f, 0.f};
 
-    if (nrows > 0)
-        prefetch(0);
-    for (int j0 = 0; j0 < nrows; j0 += kTile) {
-        __syncthreads();                          // previous tile fully consumed
-        commit(j0);
-        __syncthreads();
+    // per-lane operand bases (element offsets within a tile)
+    const int kb0 = c * G::KROW + 32 * ks0 + 8 * g;          // row c, this half's first K-step
+    const int kb1 = kb0 + 16 * G::KROW;                       // row 16 + c
+    const int vb0 = (4 * g + (c >> 2)) * G::KROW + 16 * nt0 + 4 * (c & 3);
+    const int vb1 = vb0 + 16 * G::KROW;
 
-        // S^T = K Q^T for this wave's 16 heads, rows 16*b + (0..15)
+    auto compute = [&](const uint16_t *K, int j0) {
+        // partial S^T over this half's K-steps; fragments of step i+1 are read
+        // while step i multiplies
+        // both halves have KSH steps when KS is even (the 576-wide rows); an
+        // odd KS leaves the second half one step short
+        const int nks = (G::KS % 2 == 0) ? KSH : min(KSH, G::KS - ks0);
         f4 st[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+        // fragments are read in batches of kQkBatch steps ahead of their MFMAs
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
+        for (int i0 = 0; i0 < KSH; i0 += kQkBatch) {
+            uint4 fa[kQkBatch][2];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(&Ks[(16 * b + c) * G::KROW + 32 * ks + 8 * g]);
-                st[b] = mfma_bf16_16x16x32(as_bf16x8(a), qf[ks], st[b]);
+            for (int i = 0; i < kQkBatch; ++i) {
+                if (i0 + i < nks) {
+                    fa[i][0] = *reinterpret_cast<const uint4 *>(K + kb0 + 32 * (i0 + i));
+                    fa[i][1] = *reinterpret_cast<const uint4 *>(K + kb1 + 32 * (i0 + i));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kQkBatch; ++i) {
+                if (i0 + i < nks) {
+                    st[0] = mfma_bf16_16x16x32(as_bf16x8(fa[i][0]), qf[i0 + i], st[0]);
+                    st[1] = mfma_bf16_16x16x32(as_bf16x8(fa[i][1]), qf[i0 + i], st[1]);
+                }
             }
         }
-        if (j0 + kTile < nrows)
-            prefetch(j0 + kTile);                 // in flight during softmax and PV
+        // add the partner wave's half of the dims
+        sx[wave][0][lane] = st[0];
+        sx[wave][1][lane] = st[1];
+        const int4 ra = *reinterpret_cast<const int4 *>(&rowid[j0 + 4 * g]);
+        const int4 rb = *reinterpret_cast<const int4 *>(&rowid[j0 + 16 + 4 * g]);
+        __syncthreads();
+        const f4 o0 = sx[wave ^ 4][0][lane];
+        const f4 o1 = sx[wave ^ 4][1][lane];
+        const int va[4] = {ra.x, ra.y, ra.z, ra.w};
+        const int vbv[4] = {rb.x, rb.y, rb.z, rb.w};
         float s[8];
         float mt = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool ok = rid_of(j0, 16 * b + 4 * g + r) >= 0;
-                s[4 * b + r] = ok ? st[b][r] * scale_log2 : -INFINITY;
-                mt = fmaxf(mt, s[4 * b + r]);
-            }
+        for (int r = 0; r < 4; ++r) {
+            const float t0 = half ? o0[r] + st[0][r] : st[0][r] + o0[r];   // same order in both waves
+            const float t1 = half ? o1[r] + st[1][r] : st[1][r] + o1[r];
+            s[r] = va[r] >= 0 ? t0 * scale_log2 : -INFINITY;
+            s[4 + r] = vbv[r] >= 0 ? t1 * scale_log2 : -INFINITY;
+            mt = fmaxf(mt, fmaxf(s[r], s[4 + r]));
+        }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // Lazy rescaling: the reference point m_run only moves when a column's
-        // maximum exceeds it by more than kSlack (log2 units), so most tiles
-        // skip the O rescale; exponents stay <= 2^kSlack, exact in fp32/bf16 range.
+        // The reference point m_run moves only when a column's maximum exceeds
+        // it by more than kSlack; tiles that do not raise any maximum skip the
+        // O rescale.
         const bool grow = mt > m_run + kSlack;
         float al[4] = {1.0f, 1.0f, 1.0f, 1.0f};
         const bool rescale = __any(grow);
         if (rescale) {
             const float m_new = grow ? mt : m_run;
-            const float alpha = exp2f(m_run - m_new);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
 #pragma unroll
@@ -251,30 +308,63 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         float ps = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            p[i] = exp2f(s[i] - m_run);
+            p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
             ps += p[i];
         }
         ps += __shfl_xor(ps, 16);
         ps += __shfl_xor(ps, 32);
         l_run += ps;
-        const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+        const uint4 pw = make_uint4(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                                    cvt_pk_bf16(p[6], p[7]));
         const bf16x8 pa = as_bf16x8(pw);
         if (__builtin_amdgcn_readfirstlane(rescale)) {   // rare: a branch, not selects
 #pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt)
+            for (int i = 0; i < NTH; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    o[nt][r] *= al[r];
+                    o[i][r] *= al[r];
         }
+        // V operand by transposing reads of the row-major tile: per 16-lane
+        // group, lane p addresses row 16*b + 4*g + p/4, columns v0 + 4*(p%4) ..
+        // +4; lane i then receives column v0 + i of those 4 rows, which is P's
+        // slot order (slot 4*b + e <-> row 16*b + 4*g + e).
+        auto vfrag = [&](int i) -> bf16x8 {
+            const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(K + vb0 + 16 * i));
+            const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(K + vb1 + 16 * i));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
 #pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt) {
-            const uint16_t *vr = &Vt[(16 * nt + c) * G::VROW + 4 * g];
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
-            const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16);
-            const bf16x8 vb = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-            o[nt] = mfma_bf16_16x16x32(pa, vb, o[nt]);
+        for (int i0 = 0; i0 < NTH; i0 += kPvBatch) {
+            bf16x8 vb[kPvBatch];
+#pragma unroll
+            for (int i = 0; i < kPvBatch; ++i)
+                if (i0 + i < NTH)
+                    vb[i] = vfrag(i0 + i);
+#pragma unroll
+            for (int i = 0; i < kPvBatch; ++i)
+                if (i0 + i < NTH)
+                    o[i0 + i] = mfma_bf16_16x16x32(pa, vb[i], o[i0 + i]);
         }
+    };
+
+    // ring of kBuffers tiles: tile i lives in buffer i % kBuffers; tiles i+1 ..
+    // i+kBuffers-2 are in flight while tile i is computed
+    const int ntiles = padded / kTile;
+    for (int i = 0; i < kBuffers - 1 && i < ntiles; ++i)
+        issue(i, i * kTile);
+    // fill loads a wave issues per tile (the smallest count over the waves)
+    constexpr int kPerWave = TG::INSTR / kWaves;
+    for (int i = 0; i < ntiles; ++i) {
+        // wait for tile i's fills; the fills of younger tiles may stay in flight
+        if (i + kBuffers - 2 < ntiles)
+            wait_vmcnt<kPerWave * (kBuffers - 2)>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();                          // every wave's fills of tile i are in LDS,
+                                                  // and buffer (i-1) % kBuffers is no longer read
+        if (i + kBuffers - 1 < ntiles)
+            issue((i + kBuffers - 1) % kBuffers, (i + kBuffers - 1) * kTile);
+        compute(tiles[i % kBuffers], i * kTile);
     }
 
     if (splits == 1) {
@@ -289,12 +379,13 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
                 continue;
             const int64_t orow = ((int64_t)t * H + h) * DV;
 #pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) {
-                const float val = o[nt][r] * inv[r];
+            for (int i = 0; i < NTH; ++i) {
+                const float val = o[i][r] * inv[r];
+                const int v = 16 * (nt0 + i) + c;
                 if (out_f32)
-                    reinterpret_cast<float *>(out)[orow + 16 * nt + c] = val;
+                    reinterpret_cast<float *>(out)[orow + v] = val;
                 else
-                    reinterpret_cast<uint16_t *>(out)[orow + 16 * nt + c] = (uint16_t)f32_to_bf16_rne(val);
+                    reinterpret_cast<uint16_t *>(out)[orow + v] = (uint16_t)f32_to_bf16_rne(val);
             }
         }
     } else {
@@ -305,10 +396,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             if (h >= H)
                 continue;
 #pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt)
-                part_o[(prow + h) * DV + 16 * nt + c] = o[nt][r];
+            for (int i = 0; i < NTH; ++i)
+                part_o[(prow + h) * DV + 16 * (nt0 + i) + c] = o[i][r];
         }
-        if (g == 0 && hc < H) {
+        if (half == 0 && g == 0 && hc < H) {
             part_ml[(prow + hc) * 2 + 0] = m_run;
             part_ml[(prow + hc) * 2 + 1] = l_run;
         }
@@ -393,7 +484,7 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
         part_o = reinterpret_cast<float *>(ws);
         part_ml = part_o + (size_t)T * plan.splits * H * DV;
     }
-    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), dim3(plan.splits, hg, T), dim3(kMlaThreads), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
                        q, kv, base, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
                        out_f32, part_o, part_ml);
     hipError_t e = hipGetLastError();
