@@ -42,7 +42,9 @@ constexpr int kBins0 = kHistBins0;      // first digit: bits 31..21
 constexpr int kSplitThreads = 256;
 constexpr int kSplitChunk = kSplitThreads * 4;   // scores per split workgroup
 constexpr int kRowThreads = 1024;
-constexpr int kListCap = 8192;          // survivors held in LDS
+constexpr int kFinishThreads = 1024;
+constexpr int kListCap = 12288;         // survivors held in LDS (split path)
+constexpr int kRowListCap = 8192;       // survivors held in LDS (row path: two workgroups per CU)
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
 constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
 
@@ -183,20 +185,27 @@ struct SliceSrc {
     int64_t n;
     __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
     {
+        // one binary search for the first element, then walk forward
+        int lo = 0;
+        if (i < n) {
+            int hi = P;
+            const uint32_t x = (uint32_t)i;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (offs[mid] <= x)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t x = (uint32_t)(i + e);
             ok[e] = i + e < n;
             uint64_t v = 0;
             if (ok[e]) {
-                int lo = 0, hi = P;
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (offs[mid] <= x)
-                        lo = mid;
-                    else
-                        hi = mid;
-                }
+                while (lo + 1 < P && offs[lo + 1] <= x)
+                    ++lo;
                 v = regions[(int64_t)lo * chunk + (x - offs[lo])];
             }
             key[e] = (uint32_t)(v >> 32);
@@ -318,8 +327,9 @@ __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t pr
 // digit over the first-digit bin, keep only keys at or above the second-digit
 // threshold (they fit unless ties span the list), finish from the third digit.
 template <int NT, class Src, class Fallback>
-__device__ void finish_from_overflow(const Src &src, const Fallback &row, Shared &sh, uint64_t *list, uint32_t d0,
-                                     uint32_t need0, int32_t k, int32_t *__restrict__ out)
+__device__ void finish_from_overflow(const Src &src, const Fallback &row, Shared &sh, uint64_t *list,
+                                     uint32_t list_cap, uint32_t d0, uint32_t need0, int32_t k,
+                                     int32_t *__restrict__ out)
 {
     const uint32_t p0 = d0 << 21;
     for (int i = threadIdx.x; i < kBins0; i += NT)
@@ -339,8 +349,8 @@ __device__ void finish_from_overflow(const Src &src, const Fallback &row, Shared
     uint32_t d1, above1;
     find_digit<NT>(sh, 2048, need0, d1, above1);
     const uint32_t bound = p0 | (d1 << 10);
-    const uint32_t cnt = collect<NT>(src, bound, sh, list, (uint32_t)kListCap, nullptr, 0);
-    if (cnt <= (uint32_t)kListCap)
+    const uint32_t cnt = collect<NT>(src, bound, sh, list, list_cap, nullptr, 0);
+    if (cnt <= list_cap)
         finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
     else
         finish_select<NT>(row, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
@@ -418,7 +428,8 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict_
 // order, into the workgroup's slice of `regions`, and their count to counts.
 __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
-    const uint32_t *__restrict__ hist0, uint32_t *__restrict__ counts, uint64_t *__restrict__ regions)
+    const uint32_t *__restrict__ hist0, uint32_t *__restrict__ counts, uint64_t *__restrict__ regions,
+    uint32_t *__restrict__ digit0)
 {
     __shared__ Shared sh;
     const int t = blockIdx.y;
@@ -452,18 +463,24 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
     for (int e = 0; e < 4; ++e)
         if (sv[e])
             reg[o++] = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
-    if (tid == 0)
+    if (tid == 0) {
         counts[(int64_t)t * P + w] = tot;
+        if (w == 0) {                             // every workgroup found the same digit
+            digit0[2 * t] = d0;
+            digit0[2 * t + 1] = above0;
+        }
+    }
 }
 
-// Phase 2. grid: T; block: 1024. Gathers the survivors of all P slices in
-// slice order (= position order) into LDS and finishes the selection; zeroes
-// the query's histogram copies.
-__global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
+// Phase 2. grid: T; block: kFinishThreads. Gathers the survivors of all P
+// slices in slice order (= position order) into LDS and finishes the
+// selection; zeroes the query's histogram copies.
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
     int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, const uint32_t *__restrict__ counts,
-    const uint64_t *__restrict__ regions, int32_t P)
+    const uint64_t *__restrict__ regions, int32_t P, const uint32_t *__restrict__ digit0)
 {
+    constexpr int NT = kFinishThreads;
     __shared__ Shared sh;
     __shared__ uint64_t list[kListCap];
     __shared__ uint32_t offs[kMaxSplit + 1];
@@ -472,22 +489,19 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const int64_t nt = n[t];
     int32_t *out = idx + (int64_t)t * k;
     uint32_t *h0 = hist0 + (int64_t)t * kHistCopies * kBins0;
+    zero_hist0<NT>(h0);                           // no reader of this query's copies remains
     if (nt <= k) {
-        write_all<kRowThreads>(out, nt, k);
-        zero_hist0<kRowThreads>(h0);
+        write_all<NT>(out, nt, k);
         return;
     }
-    uint32_t d0, above0;
-    load_hist0<kRowThreads>(sh, h0);
-    find_digit<kRowThreads>(sh, kBins0, (uint32_t)k, d0, above0);
-    zero_hist0<kRowThreads>(h0);
+    const uint32_t d0 = digit0[2 * t], above0 = digit0[2 * t + 1];
     // slice offsets
     uint32_t total = 0;
-    for (int w0 = 0; w0 < P; w0 += kRowThreads) {
+    for (int w0 = 0; w0 < P; w0 += NT) {
         const int ww = w0 + tid;
         const uint32_t c = ww < P ? counts[(int64_t)t * P + ww] : 0u;
         uint32_t tot;
-        const uint32_t excl = block_scan<kRowThreads>(c, sh.waves, &tot) - c;
+        const uint32_t excl = block_scan<NT>(c, sh.waves, &tot) - c;
         if (ww < P)
             offs[ww] = total + excl;
         total += tot;
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
     const uint32_t need = (uint32_t)k - above0;
     const SliceSrc slices{regions + (int64_t)t * P * kSplitChunk, offs, P, kSplitChunk, total};
     if (total <= (uint32_t)kListCap) {
-        for (uint32_t i = tid; i < total; i += kRowThreads) {
+        for (uint32_t i = tid; i < total; i += NT) {
             int lo = 0, hi = P;                   // last slice whose offset <= i
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
@@ -510,9 +524,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_finish_kernel(
             list[i] = regions[((int64_t)t * P + lo) * kSplitChunk + (i - offs[lo])];
         }
         __syncthreads();
-        finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+        finish_select<NT>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
     } else {
-        finish_from_overflow<kRowThreads>(slices, RowSrc{scores + (int64_t)t * ld, nt}, sh, list, d0, need, k, out);
+        finish_from_overflow<NT>(slices, RowSrc{scores + (int64_t)t * ld, nt}, sh, list, (uint32_t)kListCap, d0,
+                                 need, k, out);
     }
 }
 
@@ -526,7 +541,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
                                                                uint64_t *__restrict__ surv)
 {
     __shared__ Shared sh;
-    __shared__ uint64_t list[kListCap];
+    __shared__ uint64_t list[kRowListCap];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t nt = n[t];
@@ -565,12 +580,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
     const uint32_t need = (uint32_t)k - above0;
     // survivors in position order: into LDS, and into this query's global list
     uint64_t *gl = surv + (int64_t)t * kRowSurvCap;
-    const uint32_t total = collect<kRowThreads>(src, d0 << 21, sh, list, (uint32_t)kListCap, gl,
+    const uint32_t total = collect<kRowThreads>(src, d0 << 21, sh, list, (uint32_t)kRowListCap, gl,
                                                 (uint32_t)kRowSurvCap);
-    if (total <= (uint32_t)kListCap)
+    if (total <= (uint32_t)kRowListCap)
         finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
     else if (total <= (uint32_t)kRowSurvCap)
-        finish_from_overflow<kRowThreads>(GListSrc{gl, total}, src, sh, list, d0, need, k, out);
+        finish_from_overflow<kRowThreads>(GListSrc{gl, total}, src, sh, list, (uint32_t)kRowListCap, d0, need, k,
+                                          out);
     else
         finish_select<kRowThreads>(src, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
 }
@@ -578,7 +594,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
 struct TopkLayout {
     bool split;
     int64_t P;
-    size_t hist_off, counts_off, regions_off, total;
+    size_t hist_off, counts_off, digit_off, regions_off, total;
 };
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -595,7 +611,8 @@ TopkLayout topk_layout(int32_t T, int64_t max_n)
     L.hist_off = 0;
     L.counts_off = up256((size_t)T * kHistCopies * kBins0 * 4);
     if (L.split) {
-        L.regions_off = L.counts_off + up256((size_t)T * L.P * 4);
+        L.digit_off = L.counts_off + up256((size_t)T * L.P * 4);
+        L.regions_off = L.digit_off + up256((size_t)T * 8);
         L.total = L.regions_off + up256((size_t)T * L.P * kSplitChunk * 8);
     } else {
         L.regions_off = L.counts_off;
@@ -629,13 +646,14 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
             if (e != hipSuccess)
                 return e;
         }
+        uint32_t *digit0 = reinterpret_cast<uint32_t *>(base + L.digit_off);
         hipLaunchKernelGGL(topk_survivors_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0,
-                           stream, scores, ld, n, k, hist0, counts, regions);
+                           stream, scores, ld, n, k, hist0, counts, regions, digit0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k,
-                           idx, hist0, counts, regions, (int32_t)L.P);
+        hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kFinishThreads), 0, stream, scores, ld, n,
+                           k, idx, hist0, counts, regions, (int32_t)L.P, digit0);
     } else {
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
                            hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));
