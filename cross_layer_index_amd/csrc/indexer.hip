@@ -34,6 +34,15 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i &a, const v8i &b, co
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// ReLU of a matrix-core result as a signed-integer max on its bits: a
+// negative float is a negative integer and -0 becomes +0, in one VALU op
+// (fmaxf adds a NaN-quieting step per element). The inputs are finite
+// e4m3fn codes, so every accumulator is finite.
+__device__ __forceinline__ float relu_bits(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 template <int DI>
 struct IdxGeom {
     static constexpr int HALF = DI / 2;                 // bytes per lane per row
@@ -64,36 +73,57 @@ __device__ __forceinline__ void load_run(const uint8_t *p, v8i (&frag)[IdxGeom<D
 }
 
 constexpr int kIdxWaves = 4;
+constexpr int kIdxThreads = kIdxWaves * 64;
 constexpr int kIdxUnroll = 2;                                  // 32-token groups per wave step
 constexpr int kIdxStep = kIdxWaves * 32 * kIdxUnroll;          // tokens per WG step
+constexpr int kIdxMaxChunk = 1024;                             // tokens per WG, upper bound
+constexpr int64_t kIdxResident = 2 * 256;                      // resident WGs: 2 per CU x 256 CUs
 
-// grid: (token chunks, T); block: 256 threads. Each wave scores groups of 32
-// consecutive tokens; a WG covers `chunk` tokens of one query.
+// One wave step's key fragments: kIdxUnroll groups of 32 tokens, each lane
+// holding its run of one token row (rows past the query's end are clamped to
+// its last row; their scores are never stored).
+template <int DI>
+struct KeyStep {
+    v8i b[kIdxUnroll][IdxGeom<DI>::KS];
+};
+
+template <int DI>
+__device__ __forceinline__ void load_step(KeyStep<DI> &ks, const uint8_t *krows, int64_t s0, int j, int64_t nt)
+{
+#pragma unroll
+    for (int u = 0; u < kIdxUnroll; ++u) {
+        int64_t s = s0 + 32 * u + j;
+        s = s < nt ? s : nt - 1;
+        load_run<DI>(krows + s * DI, ks.b[u]);
+    }
+}
+
+// grid: (token chunks, T); block: 256 threads. A workgroup scores `chunk`
+// consecutive tokens of one query; each wave takes every fourth step of 64
+// tokens and keeps the next step's key rows in flight while it scores the
+// current one. Head weights come from LDS as float4 (four consecutive heads
+// per accumulator quad), q fragments stay in registers. With `hist0` set the
+// workgroup also counts the first radix digit of its scores and adds its
+// counts to copy (blockIdx.x mod kHistCopies) of the query's histogram.
 template <int DI, int MT>
-__global__ __launch_bounds__(256) void indexer_decode_kernel(
+__global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
     const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t H_I,
     float *__restrict__ scores, int64_t ld, int64_t chunk, uint32_t *__restrict__ hist0)
 {
     using G = IdxGeom<DI>;
     __shared__ uint32_t hist[kHistBins0];
+    __shared__ __attribute__((aligned(16))) float wsh[MT * 32];
     const int t = blockIdx.y;
-    const int64_t nt = n[t];
-    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
-    if (s_begin >= nt)
-        return;
-    const int64_t s_end = min(nt, s_begin + chunk);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
     const int g = lane >> 5;
     const int j = lane & 31;
-    if (hist0) {
-        for (int i = threadIdx.x; i < kHistBins0; i += 256)
-            hist[i] = 0;
-        __syncthreads();
-    }
 
-    // q fragments for all heads of this query, kept in registers
+    // the query's extent and first row (scalar loads) go out first; q
+    // fragments and weights, which do not depend on them, follow at once
+    const int64_t nt = n[t];
+    const int64_t bt = base[t];
     v8i a[MT][G::KS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -106,27 +136,32 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
                 a[mt][ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
-    // head weight of every accumulator element this lane holds
-    float wr[MT][16];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int h = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-            wr[mt][r] = h < H_I ? w[(int64_t)t * H_I + h] : 0.0f;
-        }
+    float wv = 0.0f;
+    if (threadIdx.x < MT * 32 && (int)threadIdx.x < H_I)
+        wv = w[(int64_t)t * H_I + threadIdx.x];
 
-    const uint8_t *krows = k_idx + (base[t] * DI) + g * G::HALF;
+    asm volatile("" ::"s"(nt), "s"(bt));   // both loads complete here, not one after the other
+    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
+    if (s_begin >= nt)
+        return;
+    const int64_t s_end = min(nt, s_begin + chunk);
+    const uint8_t *krows = k_idx + (bt * DI) + g * G::HALF;
     float *srow = scores + (int64_t)t * ld;
 
-    for (int64_t s0 = s_begin + (int64_t)wave * 32 * kIdxUnroll; s0 < s_end; s0 += kIdxStep) {
-        v8i b[kIdxUnroll][G::KS];
-#pragma unroll
-        for (int u = 0; u < kIdxUnroll; ++u) {
-            int64_t s = s0 + 32 * u + j;
-            s = s < nt ? s : nt - 1;       // stay inside this query's rows
-            load_run<DI>(krows + s * DI, b[u]);
-        }
+    // the wave's first key rows go out before the weights are staged (the
+    // LDS store waits for the weight load; the key loads need not)
+    int64_t s0 = s_begin + (int64_t)wave * 32 * kIdxUnroll;
+    KeyStep<DI> x, y;
+    load_step<DI>(x, krows, s0 < s_end ? s0 : s_begin, j, nt);
+    if (threadIdx.x < MT * 32)
+        wsh[threadIdx.x] = wv;
+    if (hist0)
+        for (int i = threadIdx.x; i < kHistBins0; i += kIdxThreads)
+            hist[i] = 0;
+    __syncthreads();
+    const float4 *w4 = reinterpret_cast<const float4 *>(wsh);
+
+    auto score_step = [&](const KeyStep<DI> &ks, int64_t s0) {
 #pragma unroll
         for (int u = 0; u < kIdxUnroll; ++u) {
             float sum = 0.0f;
@@ -134,11 +169,17 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
             for (int mt = 0; mt < MT; ++mt) {
                 v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < G::KS; ++ks)
-                    acc = mfma_fp8_32x32x64(a[mt][ks], b[u][ks], acc);
+                for (int k = 0; k < G::KS; ++k)
+                    acc = mfma_fp8_32x32x64(a[mt][k], ks.b[u][k], acc);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sum = fmaf(wr[mt][r], fmaxf(acc[r], 0.0f), sum);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    // accumulator quad q4 holds heads 32*mt + 8*q4 + 4*g + (0..3)
+                    const float4 wq = w4[8 * mt + 2 * q4 + g];
+                    sum = fmaf(wq.x, relu_bits(acc[4 * q4 + 0]), sum);
+                    sum = fmaf(wq.y, relu_bits(acc[4 * q4 + 1]), sum);
+                    sum = fmaf(wq.z, relu_bits(acc[4 * q4 + 2]), sum);
+                    sum = fmaf(wq.w, relu_bits(acc[4 * q4 + 3]), sum);
+                }
             }
             sum += __shfl_xor(sum, 32);
             const int64_t s = s0 + 32 * u + j;
@@ -148,11 +189,34 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
                     atomicAdd(&hist[ord_key(sum) >> kHistShift0], 1u);
             }
         }
+    };
+
+    // two register buffers alternated by an unrolled pair of steps: the next
+    // step's loads are always issued before the current step is scored, and
+    // every load in the loop is unconditional so the compiler's wait counts
+    // stay exact (a conditional load makes it wait for everything)
+    const int nsteps = s0 < s_end ? (int)((s_end - s0 + kIdxStep - 1) / kIdxStep) : 0;
+    int i = 0;
+    for (; i + 2 < nsteps; i += 2, s0 += 2 * kIdxStep) {
+        load_step<DI>(y, krows, s0 + kIdxStep, j, nt);
+        __builtin_amdgcn_sched_barrier(0);
+        score_step(x, s0);
+        load_step<DI>(x, krows, s0 + 2 * kIdxStep, j, nt);
+        __builtin_amdgcn_sched_barrier(0);
+        score_step(y, s0 + kIdxStep);
+    }
+    if (nsteps - i == 2) {
+        load_step<DI>(y, krows, s0 + kIdxStep, j, nt);
+        __builtin_amdgcn_sched_barrier(0);
+        score_step(x, s0);
+        score_step(y, s0 + kIdxStep);
+    } else if (nsteps - i == 1) {
+        score_step(x, s0);
     }
     if (hist0) {
         __syncthreads();
         uint32_t *h = hist0 + ((int64_t)t * kHistCopies + (blockIdx.x % kHistCopies)) * kHistBins0;
-        for (int i = threadIdx.x; i < kHistBins0; i += 256)
+        for (int i = threadIdx.x; i < kHistBins0; i += kIdxThreads)
             if (hist[i])
                 atomicAdd(&h[i], hist[i]);
     }
@@ -163,20 +227,21 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
                             const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
                             int32_t H_I, float *scores, int64_t ld, uint32_t *hist0, hipStream_t stream)
 {
-    // aim for >= 2048 workgroups over the whole call, chunks of >= one WG step
-    int64_t total = max_n * (int64_t)T;
+    // one WG step per workgroup while the whole grid fits on the chip at
+    // once (two workgroups per CU at this kernel's register use); beyond
+    // that, longer chunks whose steps are pipelined inside each wave
     int64_t chunk = kIdxStep;
-    while (chunk < max_n && total / chunk > 2048 && chunk < (1 << 16))
+    while (chunk < kIdxMaxChunk && chunk < max_n && T * ((max_n + chunk - 1) / chunk) > kIdxResident)
         chunk *= 2;
     const int64_t nchunks = (max_n + chunk - 1) / chunk;
     if (nchunks == 0 || T == 0)
         return hipSuccess;
     dim3 grid((unsigned)nchunks, (unsigned)T);
     if (H_I <= 32)
-        hipLaunchKernelGGL((indexer_decode_kernel<DI, 1>), grid, dim3(256), 0, stream, q_idx, w, k_idx,
+        hipLaunchKernelGGL((indexer_decode_kernel<DI, 1>), grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx,
                            base, n, H_I, scores, ld, chunk, hist0);
     else
-        hipLaunchKernelGGL((indexer_decode_kernel<DI, 2>), grid, dim3(256), 0, stream, q_idx, w, k_idx,
+        hipLaunchKernelGGL((indexer_decode_kernel<DI, 2>), grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx,
                            base, n, H_I, scores, ld, chunk, hist0);
     return hipGetLastError();
 }
@@ -298,7 +363,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
                         acc = mfma_fp8_32x32x64(a[i][mt][ks], b[ks], acc);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        sum = fmaf(wr[i][mt][r], fmaxf(acc[r], 0.0f), sum);
+                        sum = fmaf(wr[i][mt][r], relu_bits(acc[r]), sum);
                 }
                 sum += __shfl_xor(sum, 32);
                 if (g == 0 && s < nq[i])

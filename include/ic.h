@@ -94,7 +94,9 @@ typedef struct {
  *   q_idx  [T, H_I, D_I] fp8 e4m3fn     w      [T, H_I] fp32
  *   k_idx  [rows, D_I]   fp8 e4m3fn     scores [T, ld] fp32, ld >= max_n, ld % 4 == 0
  * Products accumulate in fp32 on the matrix cores; with integer-valued inputs
- * whose partial sums stay below 2^24 the result is exact. */
+ * whose partial sums stay below 2^24 the result is exact. q_idx and k_idx
+ * hold finite codes: the two NaN codes (0x7F, 0xFF) are outside the domain
+ * and the scores they reach are unspecified (top-k takes no NaN scores). */
 ic_status ic_indexer_score(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                            const ic_queries *qs, int32_t H_I, int32_t D_I,
                            float *scores, int64_t ld, void *stream);

@@ -110,10 +110,14 @@ def decode_bf16(b) -> np.ndarray:
 def indexer_scores(q_idx, w, k_idx, base, n, ld: Optional[int] = None) -> np.ndarray:
     """I[t, s] = sum_h w[t,h] * relu(q[t,h,:] . k[base_t + s, :]) in fp64.
 
-    Entries s >= n[t] are NaN (no score exists there)."""
+    Entries s >= n[t] are NaN (no score exists there). The fp8 inputs must be
+    finite: the NaN codes 0x7F and 0xFF are outside the indexer's domain."""
     q = _np(q_idx, np.uint8)
     wv = _np(w, np.float32)
     kk = _np(k_idx, np.uint8)
+    for name, a in (("q_idx", q), ("k_idx", kk)):
+        if np.any((a & 0x7F) == 0x7F):
+            raise ValueError(f"indexer_scores: {name} holds an fp8 NaN code (0x7F or 0xFF)")
     b = _np(base, np.int64)
     nn = _np(n, np.int32)
     T, H_I, D_I = q.shape

@@ -78,3 +78,19 @@ def test_rows_follow_base_and_length(orc):
         exp = D_I * H_I * np.maximum(vals[base[t]:base[t] + n[t]], 0)
         assert np.array_equal(got[t, :n[t]], exp)
         assert np.all(np.isnan(got[t, n[t]:]))
+
+
+def test_nan_codes_rejected(orc):
+    """The fp8 NaN codes lie outside the indexer's input domain."""
+    q = np.zeros((1, 1, 32), np.uint8)
+    w = np.ones((1, 1), np.float32)
+    k = np.zeros((4, 32), np.uint8)
+    for bad in (0x7F, 0xFF):
+        kk = k.copy()
+        kk[2, 5] = bad
+        with pytest.raises(ValueError):
+            orc.indexer_scores(q, w, kk, np.array([0], np.int64), np.array([4], np.int32))
+        qq = q.copy()
+        qq[0, 0, 3] = bad
+        with pytest.raises(ValueError):
+            orc.indexer_scores(qq, w, k, np.array([0], np.int64), np.array([4], np.int32))
