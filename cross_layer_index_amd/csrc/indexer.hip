@@ -26,6 +26,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i &a, const v8i &b, const v16f &c)
 {
@@ -41,6 +42,15 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i &a, const v8i &b, co
 __device__ __forceinline__ float relu_bits(float x)
 {
     return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Sum over the two half-waves: v_permlane32_swap exchanges lanes 32..63 of
+// one copy with lanes 0..31 of the other inside the VGPRs, so the first
+// result holds x[l % 32] and the second x[l % 32 + 32] on every lane l.
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int DI>
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
                     sum = fmaf(wq.w, relu_bits(acc[4 * q4 + 3]), sum);
                 }
             }
-            sum += __shfl_xor(sum, 32);
+            sum = half_sum(sum);
             const int64_t s = s0 + 32 * u + j;
             if (g == 0 && s < s_end) {
                 srow[s] = sum;
@@ -250,19 +260,31 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
 // All queries read one sequence (causal prefill: query t sees tokens
 // 0..n_t-1 of the shared cache), so a key tile staged in LDS serves a group of
 // 16 queries: 8 waves x 2 queries, each wave holding its queries' q fragments
-// and head weights in registers. Per 32-token group a wave reads the key
-// fragments from LDS once and runs 4 MFMAs per query. Key rows sit in LDS with
-// a 144-byte stride so the fragment reads (64 contiguous bytes per lane, lanes
-// on consecutive rows) hit distinct banks. The next tile is loaded into
-// registers while the current one is scored.
+// and head weights in registers.
+//
+// Tiles of 256 tokens go straight from memory into LDS (global_load_lds, no
+// registers), three buffers deep. Within a tile, 32-token group gi occupies
+// 4 KB as four 1 KB slabs; slot i (16 bytes) of slab v holds token
+// 32*gi + i%32, bytes 16*(4*(i/32) + v) .. +16 of its row. Lane i of a wave
+// reads slot i of each slab, so the four conflict-free 16-byte reads hand lane
+// (j = i%32, g = i/32) bytes 64g .. 64g+63 of token j: its B fragments for
+// both K-steps, in the K-slot order the q fragments use. Wave w fills group w.
+//
+// The work of a tile is 16 units (group, query). Unit u+1's four MFMAs are
+// interleaved with unit u's ReLU / weight / head-sum epilogue on the VALU, so
+// the matrix cores and the vector ALUs of a wave run side by side.
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfQW = 2;                                  // queries per wave
 constexpr int kPfQ = kPfWaves * kPfQW;                    // queries per workgroup
 constexpr int kPfTile = 256;                              // tokens per LDS tile
-constexpr int kPfRow = 144;                               // LDS bytes per key row
+constexpr int kPfGroups = kPfTile / 32;                   // 32-token groups per tile
 constexpr int kPfDI = 128;
-constexpr int kPfLoads = kPfTile * kPfDI / 16 / kPfThreads;   // 16-byte loads per thread per tile
+constexpr int kPfSlab = 1024;                             // bytes per fill instruction
+constexpr int kPfGroupBytes = 32 * kPfDI;                 // 4 slabs
+constexpr int kPfBufs = 3;
+constexpr int kPfUnits = kPfGroups * kPfQW;
+static_assert(kPfGroups == kPfWaves, "wave w fills group w of each tile");
 
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
@@ -270,10 +292,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     int64_t ld, int64_t chunk)
 {
     using G = IdxGeom<kPfDI>;
-    __shared__ __attribute__((aligned(16))) uint8_t keys[2][kPfTile * kPfRow];
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[kPfBufs][kPfTile * kPfDI];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;
     const int j = lane & 31;
     const int t_base = blockIdx.y * kPfQ;
@@ -315,63 +337,88 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
         }
     }
 
-    // tile loads: chunk c of the tile = (row c / 8, 16-byte column c % 8)
-    uint4 pre[kPfLoads];
-    auto fetch = [&](int64_t tile) {
+    // fills of this wave's group: row 32*wave + lane%32 of the tile (clamped
+    // to the group's extent), bytes 64*(lane/32) + 16*v for slab v
+    const int64_t frow = 32 * wave + j;
+    const int fcol = 64 * g;
+    auto issue = [&](int buf, int64_t tile) {
+        int64_t row = tile + frow;
+        row = row < s_end ? row : s_end - 1;
+        const uint8_t *src = krows + row * kPfDI + fcol;
+        uint8_t *dst = &tiles[buf][wave * kPfGroupBytes];
 #pragma unroll
-        for (int u = 0; u < kPfLoads; ++u) {
-            const int c = tid + u * kPfThreads;
-            int64_t row = tile + (c >> 3);
-            row = row < s_end ? row : s_end - 1;
-            pre[u] = *reinterpret_cast<const uint4 *>(krows + row * kPfDI + (c & 7) * 16);
-        }
+        for (int v = 0; v < 4; ++v)
+            __builtin_amdgcn_global_load_lds(src + 16 * v, (lds_void *)(dst + v * kPfSlab), 16, 0, 0);
     };
-    auto stage = [&](int buf) {
+
+    auto bfrag = [&](const uint8_t *tb, int gi, v8i (&b)[G::KS]) {
+        const uint8_t *p = tb + gi * kPfGroupBytes + 16 * lane;
 #pragma unroll
-        for (int u = 0; u < kPfLoads; ++u) {
-            const int c = tid + u * kPfThreads;
-            *reinterpret_cast<uint4 *>(&keys[buf][(c >> 3) * kPfRow + (c & 7) * 16]) = pre[u];
+        for (int ks = 0; ks < G::KS; ++ks) {
+            const uint4 lo = *reinterpret_cast<const uint4 *>(p + (2 * ks) * kPfSlab);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(p + (2 * ks + 1) * kPfSlab);
+            b[ks] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
     };
 
-    fetch(s_begin);
-    int buf = 0;
-    for (int64_t tile = s_begin; tile < s_end; tile += kPfTile, buf ^= 1) {
-        stage(buf);
-        __syncthreads();
-        if (tile + kPfTile < s_end)
-            fetch(tile + kPfTile);
-        const int groups = (int)min((int64_t)(kPfTile / 32), (s_end - tile + 31) / 32);
-        for (int grp = 0; grp < groups; ++grp) {
-            const uint8_t *kr = &keys[buf][(32 * grp + j) * kPfRow + g * G::HALF];
-            v8i b[G::KS];
+    auto compute = [&](const uint8_t *tb, int64_t tile) {
+        v8i b[2][G::KS];
+        v16f acc[2][2];
+        auto mfmas = [&](int u) {
+            const int i = u & 1;
+            const v8i(&bb)[G::KS] = b[(u >> 1) & 1];
+            v16f(&c)[2] = acc[u & 1];
+            const v16f z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            c[0] = mfma_fp8_32x32x64(a[i][0][0], bb[0], z);
+            c[1] = mfma_fp8_32x32x64(a[i][1][0], bb[0], z);
+            c[0] = mfma_fp8_32x32x64(a[i][0][1], bb[1], c[0]);
+            c[1] = mfma_fp8_32x32x64(a[i][1][1], bb[1], c[1]);
+        };
+        bfrag(tb, 0, b[0]);
+        mfmas(0);
 #pragma unroll
-            for (int ks = 0; ks < G::KS; ++ks) {
-                const uint4 lo = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(kr + 32 * ks + 16);
-                b[ks] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            }
-            const int64_t s = tile + 32 * grp + j;
+        for (int u = 0; u < kPfUnits; ++u) {
+            const int gi = u >> 1, i = u & 1;
+            if (i == 0 && gi + 1 < kPfGroups)
+                bfrag(tb, gi + 1, b[(gi + 1) & 1]);
+            if (u + 1 < kPfUnits)
+                mfmas(u + 1);
+            const v16f(&c)[2] = acc[u & 1];
+            float sum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kPfQW; ++i) {
-                float sum = 0.0f;
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < 16; ++r)
+                    sum = fmaf(wr[i][mt][r], relu_bits(c[mt][r]), sum);
+            if (u + 1 < kPfUnits) {
+                // one MFMA, then a quarter of the epilogue, four times over
 #pragma unroll
-                    for (int ks = 0; ks < G::KS; ++ks)
-                        acc = mfma_fp8_32x32x64(a[i][mt][ks], b[ks], acc);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        sum = fmaf(wr[i][mt][r], relu_bits(acc[r]), sum);
+                for (int k = 0; k < 4; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
                 }
-                sum += __shfl_xor(sum, 32);
-                if (g == 0 && s < nq[i])
-                    scores[(int64_t)tq[i] * ld + s] = sum;
             }
+            sum = half_sum(sum);
+            const int64_t s = tile + 32 * gi + j;
+            if (g == 0 && s < nq[i])
+                scores[(int64_t)tq[i] * ld + s] = sum;
         }
-        // no barrier here: buffer `buf` is next written two tiles on, after the
-        // barrier that follows the other buffer's staging
+    };
+
+    // ring of three tiles: tile it+1 is in flight while tile it is scored and
+    // tile it+2 is issued at the top of iteration it. The score stores share
+    // the vector-memory counter with the fills (and may complete out of
+    // order with them), so the wait before a tile is a full one.
+    const int ntiles = (int)((s_end - s_begin + kPfTile - 1) / kPfTile);
+    issue(0, s_begin);
+    if (ntiles > 1)
+        issue(1, s_begin + kPfTile);
+    for (int it = 0; it < ntiles; ++it) {
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));    // vmcnt(0)
+        __syncthreads();            // tile it is in LDS for every wave; buffer (it+2)%3 is free
+        if (it + 2 < ntiles)
+            issue((it + 2) % kPfBufs, s_begin + (int64_t)(it + 2) * kPfTile);
+        compute(tiles[it % kPfBufs], s_begin + (int64_t)it * kPfTile);
     }
 }
 

@@ -141,15 +141,36 @@ def _bf16(t, name):
     return _dev(t, torch.bfloat16, name)
 
 
+def _shape(t, expect, name):
+    """Host-side shape check: the library sees pointers only, so a tensor
+    smaller than the descriptor says must be caught here, before any launch.
+    ``expect`` entries are ints (exact) or ``(">=", v)``."""
+    if t is None:
+        return
+    ok = t.dim() == len(expect)
+    for got, e in zip(t.shape, expect):
+        ok = ok and (got >= e[1] if isinstance(e, tuple) else got == e)
+    if not ok:
+        raise ValueError(f"{name}: shape {tuple(t.shape)} does not match {expect}")
+
+
+def _cache_rows(qs: "Queries"):
+    return (">=", int(qs.rows))
+
+
 # ---------------------------------------------------------------- entries --
 def indexer_score(q_idx, w, k_idx, qs: Queries, scores: Optional[torch.Tensor] = None, stream=None):
     """Indexer scores [T, ld] fp32 (ld = max_n rounded up to 4)."""
     q_idx, k_idx = _u8(q_idx, "q_idx"), _u8(k_idx, "k_idx")
     _dev(w, torch.float32, "w")
     T, H_I, D_I = q_idx.shape
+    _shape(q_idx, (qs.T, H_I, D_I), "q_idx")
+    _shape(w, (qs.T, H_I), "w")
+    _shape(k_idx, (_cache_rows(qs), D_I), "k_idx")
     if scores is None:
         scores = torch.empty((T, score_ld(qs.max_n)), dtype=torch.float32, device=q_idx.device)
     _dev(scores, torch.float32, "scores")
+    _shape(scores, (qs.T, (">=", qs.max_n)), "scores")
     qc = qs.c()
     _check(_lib.ic_indexer_score(_ptr(q_idx), _ptr(w), _ptr(k_idx), ctypes.byref(qc), H_I, D_I, _ptr(scores),
                                  scores.shape[1], _stream(stream)))
@@ -163,6 +184,7 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def topk(scores, qs: Queries, k: int, idx: Optional[torch.Tensor] = None, ws=None, stream=None):
     _dev(scores, torch.float32, "scores")
+    _shape(scores, (qs.T, (">=", qs.max_n)), "scores")
     qc = qs.c()
     need = _lib.ic_topk_workspace_size(ctypes.byref(qc), k)
     if ws is None:
@@ -170,6 +192,7 @@ def topk(scores, qs: Queries, k: int, idx: Optional[torch.Tensor] = None, ws=Non
     if idx is None:
         idx = torch.empty((qs.T, k), dtype=torch.int32, device=scores.device)
     _dev(idx, torch.int32, "idx")
+    _shape(idx, (qs.T, k), "idx")
     _check(_lib.ic_topk(_ptr(scores), scores.shape[1], ctypes.byref(qc), k, _ptr(idx), _ptr(ws), ws.numel(),
                         _stream(stream)))
     return idx
@@ -182,6 +205,10 @@ def sparse_mla(q, kv, qs: Queries, idx, sink, scale: float, D_v: int, out=None, 
     _dev(idx, torch.int32, "idx")
     _dev(sink, torch.float32, "sink")
     T, H, D_qk = q.shape
+    _shape(q, (qs.T, H, D_qk), "q")
+    _shape(kv, (_cache_rows(qs), D_qk), "kv")
+    _shape(idx, (qs.T, (">=", 1)), "idx")
+    _shape(sink, (H,), "sink")
     d = dims(0, 0, idx.shape[1], H, D_qk, D_v, out_f32)
     qc = qs.c()
     need = _lib.ic_sparse_mla_workspace_size(ctypes.byref(qc), ctypes.byref(d))
@@ -190,6 +217,7 @@ def sparse_mla(q, kv, qs: Queries, idx, sink, scale: float, D_v: int, out=None, 
     if out is None:
         out = torch.empty((T, H, D_v), dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
     _dev(out, torch.float32 if out_f32 else torch.bfloat16, "out")
+    _shape(out, (qs.T, H, D_v), "out")
     _check(_lib.ic_sparse_mla(_ptr(q), _ptr(kv), ctypes.byref(qc), _ptr(idx), _ptr(sink), float(scale),
                               ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
@@ -216,7 +244,12 @@ class LayerStack:
         self.scale = float(scale)
         self.rmap = (ctypes.c_int32 * self.n)(*reuse_map)
         arr = (ic_layer * self.n)()
+        T, rows = qs.T, _cache_rows(qs)
         for l, y in enumerate(layers):
+            for key, expect in (("q_idx", (T, d.H_I, d.D_I)), ("w", (T, d.H_I)), ("k_idx", (rows, d.D_I)),
+                                ("q", (T, d.H, d.D_qk)), ("kv", (rows, d.D_qk)), ("sink", (d.H,)),
+                                ("out", (T, d.H, d.D_v))):
+                _shape(y.get(key), expect, f"layer {l} {key}")
             arr[l] = ic_layer(_ptr(_u8(y.get("q_idx"), "q_idx")), _ptr(_dev(y.get("w"), torch.float32, "w")),
                               _ptr(_u8(y.get("k_idx"), "k_idx")), _ptr(_bf16(y["q"], "q")),
                               _ptr(_bf16(y["kv"], "kv")), _ptr(_dev(y["sink"], torch.float32, "sink")),

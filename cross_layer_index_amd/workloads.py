@@ -134,11 +134,13 @@ def _randn_bf16(shape, g, device, chunk_rows=1 << 16):
     return out
 
 
-def layer_inputs(wl: Workload, layer: int, device="cpu", with_indexer=True) -> LayerInputs:
+def layer_inputs(wl: Workload, layer: int, device="cpu", with_indexer=True, variant: int = 0) -> LayerInputs:
     """Draw one layer's tensors on ``device`` (the stream of random numbers
-    depends on the device: CPU and GPU draws differ for the same seed)."""
+    depends on the device: CPU and GPU draws differ for the same seed).
+    ``variant`` > 0 selects an independent draw of the same shapes: the query
+    geometry (lengths, rows) always comes from the workload's own seed."""
     rows = wl.rows()
-    s = wl.seed
+    s = wl.seed + variant * 7_919
     lo, hi = wl.qk_range
     wlo, whi = wl.w_range
     if with_indexer:

@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from cross_layer_index_amd import workloads as W
 
@@ -138,3 +139,32 @@ def test_layer_stack_rejects_bad_maps(ic, bad):
 def test_layer_stack_needs_workspace_and_cache(ic):
     st, _ = stack_call(ic, [0, 0], T=1)
     assert st == ic.IC_ERR_NULL     # index_cache missing
+
+
+def test_binding_rejects_short_caches():
+    """The library sees pointers only; the binding checks every tensor's shape
+    against the query descriptor before any launch (a cache drawn for other
+    lengths than the descriptor's must never reach a kernel)."""
+    from cross_layer_index_amd import ic
+    kv = torch.empty((100, 576), dtype=torch.bfloat16)
+    ic._shape(kv, ((">=", 100), 576), "kv")
+    ic._shape(kv, ((">=", 99), 576), "kv")
+    with pytest.raises(ValueError):
+        ic._shape(kv, ((">=", 101), 576), "kv")
+    with pytest.raises(ValueError):
+        ic._shape(kv, ((">=", 100), 512), "kv")
+    with pytest.raises(ValueError):
+        ic._shape(kv[0], ((">=", 1), 576), "kv")
+
+
+def test_variant_draws_keep_geometry():
+    """Input sets drawn with another variant share the workload's lengths and
+    row count and differ in values."""
+    wl = W.scaled(W.WORKLOADS["ragged_64"], T=5, len_range=(10, 300))
+    a = W.layer_inputs(wl, 0)
+    b = W.layer_inputs(wl, 0, variant=3)
+    for f in ("q_idx", "w", "k_idx", "q", "kv", "sink"):
+        x, y = getattr(a, f), getattr(b, f)
+        assert x.shape == y.shape and x.dtype == y.dtype
+    assert not torch.equal(a.kv, b.kv) and not torch.equal(a.k_idx, b.k_idx)
+    assert a.kv.shape[0] == wl.rows()
