@@ -136,6 +136,10 @@ ic_status check_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs,
         return fail(IC_ERR_NULL, "sparse MLA: q, kv, idx, sink and out are required");
     if (!aligned16(q) || !aligned16(kv) || !aligned16(idx) || !aligned16(sink) || !aligned16(out))
         return fail(IC_ERR_ALIGN, "sparse MLA: device pointers must be 16-byte aligned");
+    // a query's latent rows are addressed by 32-bit byte offsets from its first row
+    if ((uint64_t)qs->max_n * (uint64_t)d->D_qk * 2u >= (1ull << 32))
+        return fail(IC_ERR_UNSUPPORTED, "sparse MLA: max_n=%lld rows of %d bf16 exceed 4 GiB per sequence",
+                    (long long)qs->max_n, d->D_qk);
     const ic::MlaPlan plan = ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v);
     if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
         return fail(IC_ERR_WORKSPACE, "sparse MLA: workspace of %zu bytes required, %zu given", plan.ws_bytes,

@@ -282,7 +282,6 @@ constexpr int kPfGroups = kPfTile / 32;                   // 32-token groups per
 constexpr int kPfDI = 128;
 constexpr int kPfSlab = 1024;                             // bytes per fill instruction
 constexpr int kPfGroupBytes = 32 * kPfDI;                 // 4 slabs
-constexpr int kPfBufs = 3;
 constexpr int kPfUnits = kPfGroups * kPfQW;
 static_assert(kPfGroups == kPfWaves, "wave w fills group w of each tile");
 
@@ -292,7 +291,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     int64_t ld, int64_t chunk)
 {
     using G = IdxGeom<kPfDI>;
-    __shared__ __attribute__((aligned(16))) uint8_t tiles[kPfBufs][kPfTile * kPfDI];
+    // three separate LDS objects (not one array): a read of one buffer is then
+    // known not to alias the fills in flight into the others, and the
+    // compiler need not wait for those fills before reading
+    __shared__ __attribute__((aligned(16))) uint8_t tile0[kPfTile * kPfDI];
+    __shared__ __attribute__((aligned(16))) uint8_t tile1[kPfTile * kPfDI];
+    __shared__ __attribute__((aligned(16))) uint8_t tile2[kPfTile * kPfDI];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -341,11 +345,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     // to the group's extent), bytes 64*(lane/32) + 16*v for slab v
     const int64_t frow = 32 * wave + j;
     const int fcol = 64 * g;
-    auto issue = [&](int buf, int64_t tile) {
+    auto issue = [&](uint8_t *buf, int64_t tile) {
         int64_t row = tile + frow;
         row = row < s_end ? row : s_end - 1;
         const uint8_t *src = krows + row * kPfDI + fcol;
-        uint8_t *dst = &tiles[buf][wave * kPfGroupBytes];
+        uint8_t *dst = buf + wave * kPfGroupBytes;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             __builtin_amdgcn_global_load_lds(src + 16 * v, (lds_void *)(dst + v * kPfSlab), 16, 0, 0);
@@ -410,15 +414,23 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     // the vector-memory counter with the fills (and may complete out of
     // order with them), so the wait before a tile is a full one.
     const int ntiles = (int)((s_end - s_begin + kPfTile - 1) / kPfTile);
-    issue(0, s_begin);
+    issue(tile0, s_begin);
     if (ntiles > 1)
-        issue(1, s_begin + kPfTile);
-    for (int it = 0; it < ntiles; ++it) {
+        issue(tile1, s_begin + kPfTile);
+    // the ring unrolled by three so that every access names its buffer
+    auto step = [&](int it, uint8_t *cur, uint8_t *ahead) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));    // vmcnt(0)
-        __syncthreads();            // tile it is in LDS for every wave; buffer (it+2)%3 is free
+        __syncthreads();            // tile it is in LDS for every wave; `ahead` is free
         if (it + 2 < ntiles)
-            issue((it + 2) % kPfBufs, s_begin + (int64_t)(it + 2) * kPfTile);
-        compute(tiles[it % kPfBufs], s_begin + (int64_t)it * kPfTile);
+            issue(ahead, s_begin + (int64_t)(it + 2) * kPfTile);
+        compute(cur, s_begin + (int64_t)it * kPfTile);
+    };
+    for (int it = 0; it < ntiles; it += 3) {
+        step(it, tile0, tile2);
+        if (it + 1 < ntiles)
+            step(it + 1, tile1, tile0);
+        if (it + 2 < ntiles)
+            step(it + 2, tile2, tile1);
     }
 }
 

@@ -82,6 +82,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
+// Reductions over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48)
+// inside the VGPRs: v_permlane16_swap pairs rows (0,1) and (2,3),
+// v_permlane32_swap pairs rows (0,2) and (1,3); each swap of a value with
+// itself leaves one partner's copy in each result.
+__device__ __forceinline__ float rows_max(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Two fp32 -> two bf16 (round to nearest even) in one instruction.
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
 {
@@ -110,6 +130,18 @@ constexpr int kFillPerWave = 5;             // >= ceil(fill instructions / waves
 constexpr int kQkBatch = 5;                 // QK^T K-steps whose fragments are read together
 constexpr int kPvBatch = 4;                 // PV value tiles whose fragments are read together
 
+// Workgroup barrier that orders LDS traffic only: this wave's LDS operations
+// complete, then s_barrier. (__syncthreads carries a release fence that also
+// waits for every load in flight, including the ring's LDS fills of later
+// tiles, which the barriers of the tile loop do not need: before the barrier
+// at the top of a step each wave has waited for its own fills of the tile
+// about to be read.) The memory clobber keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at max)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -137,7 +169,13 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     constexpr int KSH = (G::KS + 1) / 2;          // K-steps per half
     constexpr int NTH = G::NTV / 2;               // value tiles per half
     static_assert(TG::INSTR <= kWaves * kFillPerWave, "fill instructions per wave");
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[kBuffers][TG::ELEMS];
+    // the ring's buffers are separate LDS objects (not one array): a read of
+    // one buffer is then known not to alias the fills in flight into the
+    // others, so the compiler does not wait for those fills before reading
+    static_assert(kBuffers == 3, "the ring below is unrolled for three buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t tile0[TG::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t tile1[TG::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t tile2[TG::ELEMS];
     __shared__ __attribute__((aligned(16))) f4 sx[kWaves][2][64];   // partial S^T per wave
     __shared__ __attribute__((aligned(16))) int32_t rowid[kMaxRowsPerSplit + kTile];
 
@@ -170,20 +208,22 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const int g = lane >> 4;
     const int h0 = hg * kHeadsPerWG + hgrp * kHeadsPerWave;
     const int hc = h0 + c;                        // head of this lane's S^T column
-    const int64_t b_t = base[t];
+    // this query's latent rows: row j is at byte 2*DQK*j from kvq (a
+    // workgroup-uniform base, so fills address by 32-bit offsets)
+    const char *kvq = reinterpret_cast<const char *>(kv + base[t] * DQK);
     const int j_begin = split * rows_per_split;
     const int j_end = min(k, j_begin + rows_per_split);
     const int nrows = j_end - j_begin;
     const int ks0 = half * KSH;
     const int nt0 = half * NTH;
-    // finite data any lane may always read: this query's own q row (used for
-    // empty index slots and for padding chunks; the math never uses it)
-    const uint16_t *safe_row = q + (int64_t)t * H * DQK;
-
     // the split's index list in LDS, padded with empty slots to whole tiles
     const int padded = (nrows + kTile - 1) / kTile * kTile;
-    for (int i = tid; i < padded; i += kMlaThreads)
-        rowid[i] = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
+    int any_valid = 0;
+    for (int i = tid; i < padded; i += kMlaThreads) {
+        const int r = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
+        rowid[i] = r;
+        any_valid |= r >= 0;
+    }
 
     // q fragments of this half: lane (head hc, group g) holds d = 32*ks + 8*g .. +8
     bf16x8 qf[KSH];
@@ -204,20 +244,26 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         fill_row[i] = chunk / TG::ROWCH;
         fill_ch[i] = chunk - fill_row[i] * TG::ROWCH;
     }
-    __syncthreads();
+    // A split with no valid entry skips the tile loop (its result is the
+    // empty one: zero output, or m = kMInit and l = 0). Otherwise the query
+    // has at least one row, row 0 exists, and empty slots (and the spare
+    // chunk of each LDS row) read row 0: finite data the math never uses.
+    const bool has_rows = __syncthreads_or(any_valid);
+    // byte offset of each fill's 16-byte chunk within its row
+    int fill_boff[kFillPerWave];
+#pragma unroll
+    for (int i = 0; i < kFillPerWave; ++i)
+        fill_boff[i] = fill_ch[i] < G::NCH ? 16 * fill_ch[i] : 0;
 
-    auto issue = [&](int buf, int j0) {
-        uint16_t *tile = tiles[buf];
+    auto issue = [&](uint16_t *tile, int j0) {
 #pragma unroll
         for (int i = 0; i < kFillPerWave; ++i) {
             const int m = wave + kWaves * i;
             if (m < TG::INSTR) {
                 const int r = fill_row[i];
-                const int ch = fill_ch[i];
                 const int rid = r < kTile ? rowid[j0 + r] : -1;
-                const uint16_t *src = (rid >= 0 && ch < G::NCH) ? kv + (b_t + rid) * DQK + 8 * ch
-                                                                 : safe_row + 8 * (ch < G::NCH ? ch : 0);
-                __builtin_amdgcn_global_load_lds(src, (lds_void *)(tile + m * 64 * 8), 16, 0, 0);
+                const uint32_t off = (uint32_t)max(rid, 0) * (uint32_t)(2 * DQK) + (uint32_t)fill_boff[i];
+                __builtin_amdgcn_global_load_lds(kvq + off, (lds_void *)(tile + m * 64 * 8), 16, 0, 0);
             }
         }
     };
@@ -235,11 +281,20 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     for (int i = 0; i < NTH; ++i)
         o[i] = f4{0.f, 0.f, 0.f, 0.f};
 
+    // Matrix row m of a 16-row block is tile row perm(m) of that block:
+    // perm(4a + j) = 8*(a/2) + 2*j + a%2. The S^T operand reads (8 lanes on 8
+    // rows, 16 bytes each) and the transposing V reads (16 lanes on 4 rows x
+    // 4 column quads) then both spread over all LDS banks; with plain row
+    // order the V reads of neighbouring rows collide.
+    auto perm = [](int m) { return 8 * (m >> 3) + 2 * (m & 3) + ((m >> 2) & 1); };
     // per-lane operand bases (element offsets within a tile)
-    const int kb0 = c * G::KROW + 32 * ks0 + 8 * g;          // row c, this half's first K-step
-    const int kb1 = kb0 + 16 * G::KROW;                       // row 16 + c
-    const int vb0 = (4 * g + (c >> 2)) * G::KROW + 16 * nt0 + 4 * (c & 3);
+    const int kb0 = perm(c) * G::KROW + 32 * ks0 + 8 * g;    // matrix row c, this half's first K-step
+    const int kb1 = kb0 + 16 * G::KROW;                       // matrix row 16 + c
+    const int vb0 = perm(4 * g + (c >> 2)) * G::KROW + 16 * nt0 + 4 * (c & 3);
     const int vb1 = vb0 + 16 * G::KROW;
+    // rows of this lane's S^T elements r = 0..3: perm(4g + r) = rb8 + 2r + odd
+    const int rb8 = 8 * (g >> 1);
+    const bool odd = g & 1;
 
     auto compute = [&](const uint16_t *K, int j0) {
         // partial S^T over this half's K-steps; fragments of step i+1 are read
@@ -270,25 +325,29 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // add the partner wave's half of the dims
         sx[wave][0][lane] = st[0];
         sx[wave][1][lane] = st[1];
-        const int4 ra = *reinterpret_cast<const int4 *>(&rowid[j0 + 4 * g]);
-        const int4 rb = *reinterpret_cast<const int4 *>(&rowid[j0 + 16 + 4 * g]);
-        __syncthreads();
+        const int *rp = &rowid[j0 + rb8 + odd];
+        int va[4], vbv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            va[r] = rp[2 * r];
+            vbv[r] = rp[16 + 2 * r];
+        }
+        lds_barrier();
         const f4 o0 = sx[wave ^ 4][0][lane];
         const f4 o1 = sx[wave ^ 4][1][lane];
-        const int va[4] = {ra.x, ra.y, ra.z, ra.w};
-        const int vbv[4] = {rb.x, rb.y, rb.z, rb.w};
         float s[8];
         float mt = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float t0 = half ? o0[r] + st[0][r] : st[0][r] + o0[r];   // same order in both waves
-            const float t1 = half ? o1[r] + st[1][r] : st[1][r] + o1[r];
+            // a two-term fp32 sum is commutative, so both waves of the pair
+            // get identical scores
+            const float t0 = st[0][r] + o0[r];
+            const float t1 = st[1][r] + o1[r];
             s[r] = va[r] >= 0 ? t0 * scale_log2 : -INFINITY;
             s[4 + r] = vbv[r] >= 0 ? t1 * scale_log2 : -INFINITY;
             mt = fmaxf(mt, fmaxf(s[r], s[4 + r]));
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = rows_max(mt);
         // The reference point m_run moves only when a column's maximum exceeds
         // it by more than kSlack; tiles that do not raise any maximum skip the
         // O rescale.
@@ -311,8 +370,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
             ps += p[i];
         }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
+        ps = rows_sum(ps);
         l_run += ps;
         const uint4 pw = make_uint4(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                                     cvt_pk_bf16(p[6], p[7]));
@@ -325,9 +383,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
                     o[i][r] *= al[r];
         }
         // V operand by transposing reads of the row-major tile: per 16-lane
-        // group, lane p addresses row 16*b + 4*g + p/4, columns v0 + 4*(p%4) ..
-        // +4; lane i then receives column v0 + i of those 4 rows, which is P's
-        // slot order (slot 4*b + e <-> row 16*b + 4*g + e).
+        // group, lane p addresses matrix row 16*b + 4*g + p/4 (tile row
+        // 16*b + perm(4*g + p/4)), columns v0 + 4*(p%4) .. +4; lane i then
+        // receives column v0 + i of those 4 rows, which is P's slot order
+        // (slot 4*b + e <-> matrix row 16*b + 4*g + e).
         auto vfrag = [&](int i) -> bf16x8 {
             const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(K + vb0 + 16 * i));
             const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(K + vb1 + 16 * i));
@@ -347,24 +406,35 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         }
     };
 
-    // ring of kBuffers tiles: tile i lives in buffer i % kBuffers; tiles i+1 ..
-    // i+kBuffers-2 are in flight while tile i is computed
-    const int ntiles = padded / kTile;
-    for (int i = 0; i < kBuffers - 1 && i < ntiles; ++i)
-        issue(i, i * kTile);
+    // ring of three tiles: tile i lives in buffer i % 3; tile i+1 is in
+    // flight while tile i is computed. The ring is unrolled by three so that
+    // every access names its buffer.
+    const int ntiles = has_rows ? padded / kTile : 0;
+    if (ntiles > 0)
+        issue(tile0, 0);
+    if (ntiles > 1)
+        issue(tile1, kTile);
     // fill loads a wave issues per tile (the smallest count over the waves)
     constexpr int kPerWave = TG::INSTR / kWaves;
-    for (int i = 0; i < ntiles; ++i) {
-        // wait for tile i's fills; the fills of younger tiles may stay in flight
-        if (i + kBuffers - 2 < ntiles)
-            wait_vmcnt<kPerWave * (kBuffers - 2)>();
+    auto step = [&](int i, const uint16_t *cur, uint16_t *ahead) {
+        // wait for tile i's fills; the fills of tile i+1 may stay in flight
+        if (i + 1 < ntiles)
+            wait_vmcnt<kPerWave>();
         else
             wait_vmcnt<0>();
-        __syncthreads();                          // every wave's fills of tile i are in LDS,
-                                                  // and buffer (i-1) % kBuffers is no longer read
-        if (i + kBuffers - 1 < ntiles)
-            issue((i + kBuffers - 1) % kBuffers, (i + kBuffers - 1) * kTile);
-        compute(tiles[i % kBuffers], i * kTile);
+        // every wave's fills of tile i are in LDS (each wave waited for its
+        // own above), and `ahead` (tile i-1) is no longer read
+        lds_barrier();
+        if (i + 2 < ntiles)
+            issue(ahead, (i + 2) * kTile);
+        compute(cur, i * kTile);
+    };
+    for (int i = 0; i < ntiles; i += 3) {
+        step(i, tile0, tile2);
+        if (i + 1 < ntiles)
+            step(i + 1, tile1, tile0);
+        if (i + 2 < ntiles)
+            step(i + 2, tile2, tile1);
     }
 
     if (splits == 1) {
@@ -406,70 +476,90 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     }
 }
 
-// grid: (H, T); block: 256. Merges the per-split partials and adds the sink.
+// grid: (H, T); block: DV/4 threads, one float4 of value columns each.
+// Merges the per-split partials and adds the sink.
 constexpr int kMaxSplits = 256;
+constexpr int kCombineBatch = 16;           // partial loads in flight per thread
 
 template <int DV>
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restrict__ part_o,
-                                                          const float *__restrict__ part_ml,
-                                                          const float *__restrict__ sink, int32_t H,
-                                                          int32_t splits, void *__restrict__ out,
-                                                          int32_t out_f32)
+__global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__restrict__ part_o,
+                                                             const float *__restrict__ part_ml,
+                                                             const float *__restrict__ sink, int32_t H,
+                                                             int32_t splits, void *__restrict__ out,
+                                                             int32_t out_f32)
 {
+    constexpr int NT = DV / 4;
+    constexpr int NW = (NT + 63) / 64;
     __shared__ float wgt[kMaxSplits];
-    __shared__ float red[4];
+    __shared__ float red[2][NW];
     const int h = blockIdx.x;
     const int t = blockIdx.y;
     const int tid = threadIdx.x;
     const float ms = sink[h] * kLog2e;
+    const int64_t pr0 = (int64_t)t * splits * H + h;          // row of split 0
     // global maximum over the sink and the partial maxima
     float m = tid == 0 ? ms : -INFINITY;
-    for (int s = tid; s < splits; s += 256)
-        m = fmaxf(m, part_ml[(((int64_t)t * splits + s) * H + h) * 2]);
+    for (int s = tid; s < splits; s += NT)
+        m = fmaxf(m, part_ml[(pr0 + (int64_t)s * H) * 2]);
+    // butterfly over the active lanes of a wave (a block of DV/4 < 64 threads
+    // fills only part of one)
+    constexpr int kFirstOff = (NT < 64 ? NT : 64) / 2;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
+    for (int off = kFirstOff; off > 0; off >>= 1)
         m = fmaxf(m, __shfl_xor(m, off));
     if ((tid & 63) == 0)
-        red[tid >> 6] = m;
+        red[0][tid >> 6] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
+    m = red[0][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i)
+        m = fmaxf(m, red[0][i]);
     // per-split weights and the denominator
     float dsum = tid == 0 ? exp2f(ms - m) : 0.0f;
-    for (int s = tid; s < splits; s += 256) {
-        const int64_t pr = ((int64_t)t * splits + s) * H + h;
+    for (int s = tid; s < splits; s += NT) {
+        const int64_t pr = pr0 + (int64_t)s * H;
         const float wv = exp2f(part_ml[pr * 2] - m);
         wgt[s] = wv;
         dsum += part_ml[pr * 2 + 1] * wv;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
+    for (int off = kFirstOff; off > 0; off >>= 1)
         dsum += __shfl_xor(dsum, off);
     if ((tid & 63) == 0)
-        red[tid >> 6] = dsum;
+        red[1][tid >> 6] = dsum;
     __syncthreads();
-    const float inv = 1.0f / (red[0] + red[1] + red[2] + red[3]);
-    const int64_t stride = (int64_t)H * DV;
-    for (int v = tid; v < DV; v += 256) {
-        const float *p = part_o + ((int64_t)t * splits * H + h) * DV + v;
-        float acc = 0.0f;
-        int s = 0;
-        for (; s + 8 <= splits; s += 8) {
-            float x[8];
+    float den = red[1][0];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                x[u] = p[(int64_t)(s + u) * stride];
+    for (int i = 1; i < NW; ++i)
+        den += red[1][i];
+    const float inv = 1.0f / den;
+    // this thread's four columns of every split, kCombineBatch loads in flight
+    const float4 *p = reinterpret_cast<const float4 *>(part_o + pr0 * DV) + tid;
+    const int64_t stride = (int64_t)H * DV / 4;               // float4s between splits
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
+        float4 x[kCombineBatch];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                acc = fmaf(x[u], wgt[s + u], acc);
-        }
-        for (; s < splits; ++s)
-            acc = fmaf(p[(int64_t)s * stride], wgt[s], acc);
-        const int64_t oi = ((int64_t)t * H + h) * DV + v;
-        if (out_f32)
-            reinterpret_cast<float *>(out)[oi] = acc * inv;
-        else
-            reinterpret_cast<uint16_t *>(out)[oi] = (uint16_t)f32_to_bf16_rne(acc * inv);
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < splits)
+                x[u] = p[(int64_t)(s0 + u) * stride];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < splits) {
+                const float wv = wgt[s0 + u];
+                acc.x = fmaf(x[u].x, wv, acc.x);
+                acc.y = fmaf(x[u].y, wv, acc.y);
+                acc.z = fmaf(x[u].z, wv, acc.z);
+                acc.w = fmaf(x[u].w, wv, acc.w);
+            }
+    }
+    const int64_t oi = ((int64_t)t * H + h) * DV + 4 * tid;
+    if (out_f32) {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + oi) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    } else {
+        const uint2 v = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + oi) = v;
     }
 }
 
@@ -490,7 +580,7 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
-    hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3(H, T), dim3(256), 0, stream, part_o, part_ml, sink, H,
+    hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3(H, T), dim3(DV / 4), 0, stream, part_o, part_ml, sink, H,
                        plan.splits, out, out_f32);
     return hipGetLastError();
 }
