@@ -271,7 +271,7 @@ IC_EXPORT ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const i
     if (qs->T == 0)
         return ok();
     const ic::MlaPlan plan = ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v);
-    return hip_status(ic::launch_sparse_mla(q, kv, qs->base, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, sink, scale,
+    return hip_status(ic::launch_sparse_mla(q, kv, qs->base, qs->n_valid, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, sink, scale,
                                             out, d->out_dtype == IC_OUT_F32, plan, ws,
                                             reinterpret_cast<hipStream_t>(stream)),
                       "sparse MLA launch");
@@ -378,7 +378,7 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
                 return hip_status(e, "layer stack: top-k launch");
         }
         const int32_t *idx = index_cache + slot[reuse_map[l]] * slot_elems;
-        hipError_t e = ic::launch_sparse_mla(y.q, y.kv, qs->base, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, y.sink,
+        hipError_t e = ic::launch_sparse_mla(y.q, y.kv, qs->base, qs->n_valid, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, y.sink,
                                              scale, y.out, d->out_dtype == IC_OUT_F32, plan, mla_ws, st);
         if (e != hipSuccess)
             return hip_status(e, "layer stack: sparse MLA launch");

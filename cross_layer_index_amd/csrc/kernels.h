@@ -43,7 +43,7 @@ struct MlaPlan {
 bool sparse_mla_supported(int32_t D_qk, int32_t D_v);
 MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v);
 hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_t *base,
-                             const int32_t *idx, int32_t T, int32_t H, int32_t k, int32_t D_qk,
+                             const int32_t *n_valid, const int32_t *idx, int32_t T, int32_t H, int32_t k, int32_t D_qk,
                              int32_t D_v, const float *sink, float scale, void *out, int32_t out_f32,
                              const MlaPlan &plan, void *ws, hipStream_t stream);
 

@@ -160,7 +160,8 @@ __device__ __forceinline__ void wait_vmcnt()
 template <int DQK, int DV>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const int64_t *__restrict__ base,
-    const int32_t *__restrict__ idx, int32_t k, int32_t H, const float *__restrict__ sink, float scale_log2,
+    const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
+    const float *__restrict__ sink, float scale_log2,
     int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
     float *__restrict__ part_o, float *__restrict__ part_ml)
 {
@@ -216,11 +217,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const int nrows = j_end - j_begin;
     const int ks0 = half * KSH;
     const int nt0 = half * NTH;
-    // the split's index list in LDS, padded with empty slots to whole tiles
+    // the split's index list in LDS, padded with empty slots to whole tiles;
+    // an entry outside [0, n_valid[t]) counts as empty (it never addresses memory)
     const int padded = (nrows + kTile - 1) / kTile * kTile;
+    const int32_t nt = n_valid[t];
     int any_valid = 0;
     for (int i = tid; i < padded; i += kMlaThreads) {
-        const int r = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
+        int r = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
+        r = (r >= 0 && r < nt) ? r : -1;
         rowid[i] = r;
         any_valid |= r >= 0;
     }
@@ -564,7 +568,8 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
 }
 
 template <int DQK, int DV>
-hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *base, const int32_t *idx,
+hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *base, const int32_t *n_valid,
+                        const int32_t *idx,
                         int32_t T, int32_t H, int32_t k, const float *sink, float scale, void *out,
                         int32_t out_f32, const MlaPlan &plan, void *ws, hipStream_t stream)
 {
@@ -575,7 +580,7 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
         part_ml = part_o + (size_t)T * plan.splits * H * DV;
     }
     hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
-                       q, kv, base, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
+                       q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
                        out_f32, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
@@ -617,17 +622,17 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     return p;
 }
 
-hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_t *base, const int32_t *idx,
-                             int32_t T, int32_t H, int32_t k, int32_t D_qk, int32_t D_v, const float *sink,
+hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_t *base, const int32_t *n_valid,
+                             const int32_t *idx, int32_t T, int32_t H, int32_t k, int32_t D_qk, int32_t D_v, const float *sink,
                              float scale, void *out, int32_t out_f32, const MlaPlan &plan, void *ws,
                              hipStream_t stream)
 {
     if (T == 0 || H == 0)
         return hipSuccess;
     if (D_qk == 576 && D_v == 512)
-        return launch_shape<576, 512>(q, kv, base, idx, T, H, k, sink, scale, out, out_f32, plan, ws, stream);
+        return launch_shape<576, 512>(q, kv, base, n_valid, idx, T, H, k, sink, scale, out, out_f32, plan, ws, stream);
     if (D_qk == 80 && D_v == 64)
-        return launch_shape<80, 64>(q, kv, base, idx, T, H, k, sink, scale, out, out_f32, plan, ws, stream);
+        return launch_shape<80, 64>(q, kv, base, n_valid, idx, T, H, k, sink, scale, out, out_f32, plan, ws, stream);
     return hipErrorInvalidValue;
 }
 

@@ -43,9 +43,10 @@ constexpr int kSplitThreads = 256;
 constexpr int kSplitChunk = kSplitThreads * 4;   // scores per split workgroup
 constexpr int kRowThreads = 1024;
 constexpr int kFinishThreads = 1024;
-constexpr int kListCap = 12288;         // survivors held in LDS (split path)
+constexpr int kListCap = 18432;         // survivors held in LDS (split path)
 constexpr int kRowListCap = 8192;       // survivors held in LDS (row path: two workgroups per CU)
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
+static_assert(kListCap % kFinishThreads == 0, "whole runs of list entries per finishing thread");
 constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
 
 // Block-wide inclusive scan of one uint32 per thread.
@@ -423,13 +424,49 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict_
 }
 
 // ---- split path -------------------------------------------------------------
+// First digit from the query's histogram copies, read from the top bin down
+// NT bins at a time (the threshold sits in the highest bins, so one round
+// usually suffices). Falls back to digit 0 (everything survives) if the
+// counts never reach `need`.
+template <int NT>
+__device__ void find_digit0_topdown(Shared &sh, const uint32_t *h, uint32_t need, uint32_t &digit, uint32_t &above)
+{
+    uint32_t run = 0;
+    digit = 0;
+    above = 0;
+    for (int top = kBins0; top > 0; top -= NT) {
+        const int b = top - 1 - (int)threadIdx.x;          // thread 0 takes the highest bin
+        uint32_t c = 0;
+        if (b >= 0) {
+#pragma unroll
+            for (int cp = 0; cp < kHistCopies; ++cp)
+                c += h[cp * kBins0 + b];
+        }
+        uint32_t tot;
+        const uint32_t incl = block_scan<NT>(c, sh.waves, &tot);
+        if (run + tot >= need) {                           // uniform: the bin is in this round
+            if (b >= 0 && run + incl - c < need && run + incl >= need) {
+                sh.digit = (uint32_t)b;
+                sh.above = run + incl - c;
+            }
+            __syncthreads();
+            digit = sh.digit;
+            above = sh.above;
+            __syncthreads();
+            return;
+        }
+        run += tot;
+    }
+}
+
 // Phase 1. grid: (P, T); block: 256; kSplitChunk scores per workgroup. Copies
 // the chunk's survivors (first digit >= the threshold digit), in position
-// order, into the workgroup's slice of `regions`, and their count to counts.
+// order, into the workgroup's slice of `regions`, and their count to counts;
+// adds the second-digit histogram of its threshold-bin keys to hist1.
 __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
-    const uint32_t *__restrict__ hist0, uint32_t *__restrict__ counts, uint64_t *__restrict__ regions,
-    uint32_t *__restrict__ digit0)
+    const uint32_t *__restrict__ hist0, uint32_t *__restrict__ hist1, uint32_t *__restrict__ counts,
+    uint64_t *__restrict__ regions, uint32_t *__restrict__ digit0)
 {
     __shared__ Shared sh;
     const int t = blockIdx.y;
@@ -446,23 +483,30 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
     int64_t pos[4];
     bool ok[4];
     RowSrc{row, nt}.get4(s, key, pos, ok);
+    for (int i = tid; i < kBins0; i += kSplitThreads)
+        sh.hist[i] = 0;
 
     uint32_t d0, above0;
-    load_hist0<kSplitThreads>(sh, hist0 + (int64_t)t * kHistCopies * kBins0);
-    find_digit<kSplitThreads>(sh, kBins0, (uint32_t)k, d0, above0);
+    find_digit0_topdown<kSplitThreads>(sh, hist0 + (int64_t)t * kHistCopies * kBins0, (uint32_t)k, d0, above0);
     uint32_t sv[4], ls = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         sv[e] = ok[e] && (key[e] >> 21) >= d0;
         ls += sv[e];
+        if (ok[e] && (key[e] >> 21) == d0)
+            atomicAdd(&sh.hist[(key[e] >> 10) & (kBins0 - 1)], 1u);
     }
     uint32_t tot;
-    uint32_t o = block_scan<kSplitThreads>(ls, sh.waves, &tot) - ls;
+    uint32_t o = block_scan<kSplitThreads>(ls, sh.waves, &tot) - ls;   // its barriers also close the histogram
     uint64_t *reg = regions + ((int64_t)t * P + w) * kSplitChunk;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (sv[e])
             reg[o++] = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
+    uint32_t *h1 = hist1 + (int64_t)t * kBins0;
+    for (int i = tid; i < kBins0; i += kSplitThreads)
+        if (sh.hist[i])
+            atomicAdd(&h1[i], sh.hist[i]);
     if (tid == 0) {
         counts[(int64_t)t * P + w] = tot;
         if (w == 0) {                             // every workgroup found the same digit
@@ -472,13 +516,16 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
     }
 }
 
-// Phase 2. grid: T; block: kFinishThreads. Gathers the survivors of all P
-// slices in slice order (= position order) into LDS and finishes the
-// selection; zeroes the query's histogram copies.
+// Phase 2. grid: T; block: kFinishThreads. The second digit comes from hist1;
+// the survivors of all P slices are gathered in slice order (= position
+// order) into LDS, compacted in place to the keys at or above the two-digit
+// bound (about k of them), and the last digit finishes the selection. Zeroes
+// the query's histograms.
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
-    int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, const uint32_t *__restrict__ counts,
-    const uint64_t *__restrict__ regions, int32_t P, const uint32_t *__restrict__ digit0)
+    int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, uint32_t *__restrict__ hist1,
+    const uint32_t *__restrict__ counts, const uint64_t *__restrict__ regions, int32_t P,
+    const uint32_t *__restrict__ digit0)
 {
     constexpr int NT = kFinishThreads;
     __shared__ Shared sh;
@@ -489,12 +536,23 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const int64_t nt = n[t];
     int32_t *out = idx + (int64_t)t * k;
     uint32_t *h0 = hist0 + (int64_t)t * kHistCopies * kBins0;
+    uint32_t *h1 = hist1 + (int64_t)t * kBins0;
     zero_hist0<NT>(h0);                           // no reader of this query's copies remains
     if (nt <= k) {
-        write_all<NT>(out, nt, k);
+        write_all<NT>(out, nt, k);                // hist1 was not touched for this query
         return;
     }
     const uint32_t d0 = digit0[2 * t], above0 = digit0[2 * t + 1];
+    const uint32_t need0 = (uint32_t)k - above0;
+    // second digit over the first-digit bin
+    for (int i = tid; i < kBins0; i += NT) {
+        sh.hist[i] = h1[i];
+        h1[i] = 0;
+    }
+    __syncthreads();
+    uint32_t d1, above1;
+    find_digit<NT>(sh, kBins0, need0, d1, above1);
+    const uint32_t bound = (d0 << 21) | (d1 << 10);
     // slice offsets
     uint32_t total = 0;
     for (int w0 = 0; w0 < P; w0 += NT) {
@@ -509,25 +567,56 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     if (tid == 0)
         offs[P] = total;
     __syncthreads();
-    const uint32_t need = (uint32_t)k - above0;
     const SliceSrc slices{regions + (int64_t)t * P * kSplitChunk, offs, P, kSplitChunk, total};
     if (total <= (uint32_t)kListCap) {
-        for (uint32_t i = tid; i < total; i += NT) {
-            int lo = 0, hi = P;                   // last slice whose offset <= i
+        // each thread moves a run of consecutive entries: one search for the
+        // slice of its first entry, then a forward walk with the next slice's
+        // offset in a register; every load is in flight before any store
+        constexpr int kPer = kListCap / NT;
+        const uint32_t per = (total + NT - 1) / NT;
+        const uint32_t i0 = (uint32_t)tid * per;
+        int lo = 0;
+        if (i0 < total) {
+            int hi = P;
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
-                if (offs[mid] <= i)
+                if (offs[mid] <= i0)
                     lo = mid;
                 else
                     hi = mid;
             }
-            list[i] = regions[((int64_t)t * P + lo) * kSplitChunk + (i - offs[lo])];
+        }
+        uint32_t next = offs[lo + 1];
+        const uint64_t *reg_t = regions + (int64_t)t * P * kSplitChunk;
+        uint64_t v[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const uint32_t x = i0 + e;
+            if (e < (int)per && x < total) {
+                while (next <= x) {               // offs[P] = total > x ends the walk
+                    ++lo;
+                    next = offs[lo + 1];
+                }
+                v[e] = reg_t[(int64_t)lo * kSplitChunk + (x - offs[lo])];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const uint32_t x = i0 + e;
+            if (e < (int)per && x < total)
+                list[x] = v[e];
         }
         __syncthreads();
-        finish_select<NT>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+        // in place: a chunk's entries are all read before any of its slots is written
+        const uint32_t cnt = collect<NT>(ListSrc{list, total}, bound, sh, list, (uint32_t)kListCap, nullptr, 0);
+        finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
     } else {
-        finish_from_overflow<NT>(slices, RowSrc{scores + (int64_t)t * ld, nt}, sh, list, (uint32_t)kListCap, d0,
-                                 need, k, out);
+        const uint32_t cnt = collect<NT>(slices, bound, sh, list, (uint32_t)kListCap, nullptr, 0);
+        if (cnt <= (uint32_t)kListCap)
+            finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
+        else
+            finish_select<NT>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k,
+                              out);
     }
 }
 
@@ -594,7 +683,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
 struct TopkLayout {
     bool split;
     int64_t P;
-    size_t hist_off, counts_off, digit_off, regions_off, total;
+    size_t hist_off, hist1_off, counts_off, digit_off, regions_off, total;
 };
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -608,8 +697,11 @@ TopkLayout topk_layout(int32_t T, int64_t max_n)
     // split when the queries alone cannot fill the chip and the survivor
     // slices stay small
     L.split = T < 256 && (int64_t)T * L.P * kSplitChunk <= ((int64_t)1 << 26) && L.P <= kMaxSplit;
+    // counters that start and end at zero: first-digit histogram copies and
+    // the second-digit histogram of the split path
     L.hist_off = 0;
-    L.counts_off = up256((size_t)T * kHistCopies * kBins0 * 4);
+    L.hist1_off = up256((size_t)T * kHistCopies * kBins0 * 4);
+    L.counts_off = L.hist1_off + up256((size_t)T * kBins0 * 4);
     if (L.split) {
         L.digit_off = L.counts_off + up256((size_t)T * L.P * 4);
         L.regions_off = L.digit_off + up256((size_t)T * 8);
@@ -647,13 +739,14 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
                 return e;
         }
         uint32_t *digit0 = reinterpret_cast<uint32_t *>(base + L.digit_off);
+        uint32_t *hist1 = reinterpret_cast<uint32_t *>(base + L.hist1_off);
         hipLaunchKernelGGL(topk_survivors_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0,
-                           stream, scores, ld, n, k, hist0, counts, regions, digit0);
+                           stream, scores, ld, n, k, hist0, hist1, counts, regions, digit0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
         hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kFinishThreads), 0, stream, scores, ld, n,
-                           k, idx, hist0, counts, regions, (int32_t)L.P, digit0);
+                           k, idx, hist0, hist1, counts, regions, (int32_t)L.P, digit0);
     } else {
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
                            hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));

@@ -120,7 +120,8 @@ ic_status ic_topk(const float *scores, int64_t ld, const ic_queries *qs, int32_t
  *   q   [T, H, D_qk] bf16     kv  [rows, D_qk] bf16     idx [T, k] int32
  *   sink [H] fp32 (a logit in the units of the scaled scores)
  *   out [T, H, D_v] bf16 (round to nearest even) or fp32, per dims->out_dtype.
- * An all-empty selection gives zeros. QK^T and PV run on bf16 matrix cores
+ * An all-empty selection gives zeros. Entries outside [0, n_valid[t]) are
+ * treated as -1 on the device (they never address memory). QK^T and PV run on bf16 matrix cores
  * with fp32 accumulation and an fp32 online softmax; P is rounded to bf16. */
 size_t ic_sparse_mla_workspace_size(const ic_queries *qs, const ic_dims *d);
 ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs,

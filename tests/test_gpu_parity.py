@@ -212,3 +212,26 @@ def test_layer_stack_small(gpu, orc, case):
         assert np.array_equal(got_idx, r_index[l])
         err = np.abs(outs[l].cpu().numpy() - r_outs[l]).max()
         assert err <= ATOL, f"layer {l}: {err}"
+
+
+def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc):
+    """Index entries outside [0, n_valid[t]) (a list that breaks the contract)
+    are treated as empty on the device: the output equals the oracle's on the
+    same list with those entries replaced by -1, and no latent row outside the
+    query's range is read."""
+    wl = W.scaled(W.WORKLOADS["decode_128k"], T=3, k=64, lengths=[200, 90, 130])
+    rng = np.random.default_rng(11)
+    n = wl.n_valid().numpy()
+    idx = np.stack([rng.choice(int(x), 64, replace=False) for x in n]).astype(np.int32)
+    idx[0, 5] = n[0]                     # one past the query's rows
+    idx[0, 9] = n[0] + n[1]              # a row of the next query
+    idx[1, :8] = 2_000_000_000           # far outside the cache
+    idx[2, -3:] = -7                     # negative but not -1
+    clean = np.where((idx >= 0) & (idx < n[:, None]), idx, -1).astype(np.int32)
+    li = W.layer_inputs(wl, 0, with_indexer=False)
+    d = dev(li)
+    qs = qs_of(gpu, wl)
+    got = gpu.sparse_mla(d.q, d.kv, qs, torch.from_numpy(idx).cuda(), d.sink, wl.scale, wl.D_v,
+                         out_f32=True).float().cpu().numpy()
+    ref = orc.sparse_mla(li.q, li.kv, wl.base(), clean, li.sink, wl.scale, wl.D_v)
+    assert_close(got, ref, True)
