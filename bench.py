@@ -80,6 +80,30 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def reuse_overlap(ic, W, wl, st, rmap, qs, d, dev):
+    """Mean fraction of a shared layer's own top-k that its inherited index
+    also holds (each shared layer's own indexer run on its own inputs), over
+    the shared layers and queries of one input set. On synthetic inputs the
+    layers are independent, so the expected value is about k / L; it measures
+    the machinery, not the quality of reuse."""
+    import torch
+    st()                                      # fills the index cache
+    slots = {l: i for i, l in enumerate(l for l in range(wl.n_layers) if rmap[l] == l)}
+    n = int(qs.max_n)
+    fr = []
+    for l in range(wl.n_layers):
+        if rmap[l] == l:
+            continue
+        y = st.layers[l]
+        own = ic.topk(ic.indexer_score(y["q_idx"], y["w"], y["k_idx"], qs), qs, wl.k)
+        inh = st.index_cache[slots[rmap[l]]]
+        mask = torch.zeros((wl.T, n + 1), dtype=torch.bool, device=dev)
+        mask.scatter_(1, torch.where(inh >= 0, inh, n).long(), True)
+        hit = torch.gather(mask, 1, torch.where(own >= 0, own, n).long()) & (own >= 0)
+        fr.append((hit.sum(1).float() / (own >= 0).sum(1).clamp(min=1).float()).mean().item())
+    return {"mean": sum(fr) / len(fr), "shared_layers": len(fr), "expected_independent": wl.k / n}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +248,17 @@ def main():
                                   "indexer_passes": wl.n_layers}
             result["indexcache_speedup"] = el2 / el
             del allfull
+            # reuse-pattern variants: the same stack and inputs under other full-layer sets
+            pats = {}
+            for name, fl in W.REUSE_PATTERNS.items():
+                m = ic.reuse_map_last_full([l in set(fl) for l in range(wl.n_layers)])
+                st = [ic.LayerStack(s.layers, m, qs, d, wl.scale, device=dev) for s in sets]
+                elp, _ = timed(runner(st), steps, warm)
+                pats[name] = {"indexer_passes": len(fl), "ms_per_step": elp * 1e3 / steps,
+                              "value": wl.T * wl.n_layers * steps / elp, "speedup_vs_all_full": el2 / elp}
+                del st
+            result["reuse_patterns"] = pats
+            result["reuse_overlap"] = reuse_overlap(ic, W, wl, sets[0], rmap, qs, d, dev)
 
     # ---- dominant kernel: the indexer, timed alone with events on its stream,
     # rotating over the key caches of every full layer of every set
@@ -332,7 +367,7 @@ def main():
         step_bytes = sum(algorithmic_bytes(x, wl.k, wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, rmap[l] == l)
                          for l in range(wl.n_layers) for x in nn)
         line["step_hbm_frac"] = step_bytes / (result["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
-    for k2 in ("all_full", "indexcache_speedup"):
+    for k2 in ("all_full", "indexcache_speedup", "reuse_patterns", "reuse_overlap"):
         if k2 in result:
             line[k2] = result[k2]
     print(json.dumps(line))

@@ -162,6 +162,17 @@ def layer_inputs(wl: Workload, layer: int, device="cpu", with_indexer=True, vari
 # 0, 1, 2 and every fourth layer from 6 to 74 (21 of 78).
 HY4_FULL_LAYERS = [0, 1, 2] + list(range(6, 75, 4))
 
+# Full-layer sets of the 78-layer stack compared by the reuse-pattern
+# measurement: the issue's map (21 full), an index refreshed every six layers
+# (13 builds per token, the explainer's "13x" reading), one index for the whole
+# stack, and no reuse at all.
+REUSE_PATTERNS = {
+    "hy4_21": HY4_FULL_LAYERS,
+    "every6_13": list(range(0, 78, 6)),
+    "first_only_1": [0],
+    "all_78": list(range(78)),
+}
+
 WORKLOADS = {
     "tiny_2layer": Workload(
         name="tiny_2layer", seed=1, n_layers=2, full_layers=[0], T=1, H_I=4, D_I=32, k=64,

@@ -168,3 +168,29 @@ def test_variant_draws_keep_geometry():
         assert x.shape == y.shape and x.dtype == y.dtype
     assert not torch.equal(a.kv, b.kv) and not torch.equal(a.k_idx, b.k_idx)
     assert a.kv.shape[0] == wl.rows()
+
+
+def test_reuse_patterns_match_the_pages_counts(orc):
+    """The full-layer sets the reuse-pattern measurement compares give the
+    index-build counts the pages print (tests/golden/index_score_counts.txt),
+    and under each of them every shared layer reads the last full layer
+    before it (library and oracle agree)."""
+    from cross_layer_index_amd import ic
+    golden = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "index_score_counts.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            golden[k] = v
+    L = int(golden["layers"])
+    want = {"hy4_21": int(golden["hy4_full_layers"]), "every6_13": int(golden["refresh_every_index_builds"]),
+            "first_only_1": 1, "all_78": L}
+    assert set(W.REUSE_PATTERNS) == set(want)
+    for name, fl in W.REUSE_PATTERNS.items():
+        flags = [l in set(fl) for l in range(L)]
+        assert sum(flags) == want[name], name
+        m = ic.reuse_map_last_full(flags)
+        assert m == orc.reuse_map_last_full(flags)
+        for l in range(L):
+            assert m[l] == max(f for f in fl if f <= l)
+    assert "".join("F" if l in set(W.REUSE_PATTERNS["hy4_21"]) else "S" for l in range(6)) == \
+        golden["hy4_pattern_prefix"]

@@ -194,12 +194,18 @@ def run_stack(ic, wl, layers_dev, rmap, out_f32=False):
     return outs, cache, passes
 
 
-@pytest.mark.parametrize("case", ["tiny", "small_5layer"])
+@pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer"])
 def test_layer_stack_small(gpu, orc, case):
     if case == "tiny":
         wl = W.WORKLOADS["tiny_2layer"]
-    else:
+    elif case == "small_5layer":
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=5, full_layers=[0, 3], T=3, lengths=[3000, 2048, 100])
+    elif case == "every6_13layer":
+        # an index refreshed every sixth layer, on small shapes
+        wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=13, full_layers=[0, 6, 12], T=2, k=64,
+                      lengths=[700, 65], H=8)
+    else:
+        wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=4, full_layers=[0], T=2, k=64, lengths=[300, 50], H=8)
     host = [W.layer_inputs(wl, l) for l in range(wl.n_layers)]
     rmap = gpu.reuse_map_last_full(wl.is_full())
     outs, cache, passes = run_stack(gpu, wl, [dev(x) for x in host], rmap, out_f32=True)
