@@ -50,9 +50,20 @@ def default_sets(wl, nn) -> int:
     (one shared sequence, matrix-core bound) uses one set."""
     if wl.same_seq:
         return 1
-    per_step = sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn) * sum(wl.is_full())
+    per_step = indexer_launch_bytes(wl, nn) * sum(wl.is_full())
     per_step += sum(min(wl.k, x) * wl.D_qk * 2 for x in nn) * wl.n_layers
     return int(min(64, max(1, -(-(1 << 30) // per_step))))
+
+
+def indexer_launch_bytes(wl, nn) -> int:
+    """Algorithmic bytes of one indexer launch: every query's q and w, and the
+    key rows of every sequence once (queries of a draft/verify group share
+    their sequence's key stream)."""
+    g = max(1, wl.group)
+    if g == 1:
+        return sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn)
+    keys = sum(max(nn[i:i + g]) for i in range(0, len(nn), g)) * wl.D_I
+    return keys + len(nn) * wl.H_I * (wl.D_I + 4)
 
 
 def indexer_bytes(n: int, H_I: int, D_I: int) -> int:
@@ -110,7 +121,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode_128k",
-                    choices=["decode_128k", "ragged_64", "stack_78", "prefill_1m", "tiny_2layer"])
+                    choices=["decode_128k", "ragged_64", "stack_78", "prefill_1m", "mtp_verify", "tiny_2layer"])
     ap.add_argument("--sets", type=int, default=None, help="rotating input sets (default 8 for decode_128k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -147,7 +158,7 @@ def main():
     n = wl.n_valid()
     nn = [int(x) for x in n.tolist()]
     R = args.sets if args.sets is not None else default_sets(wl, nn)
-    qs = ic.make_queries(wl.base(), n, wl.rows(), wl.same_seq, device=dev)
+    qs = ic.make_queries(wl.base(), n, wl.rows(), wl.same_seq, device=dev, group=wl.group)
     d = ic.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v)
     rmap = ic.reuse_map_last_full(wl.is_full())
     small = wl.rows() * wl.D_qk * 2 * wl.n_layers < (1 << 30)
@@ -291,12 +302,17 @@ def main():
                 "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None, "kernel": "indexer_prefill_kernel",
                 "kernel_ms": k_ms, "algorithmic_flops_per_launch": fl}
     else:
-        by = sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn)
+        by = indexer_launch_bytes(wl, nn)
         achieved = by / (k_ms * 1e-3) / 1e9
+        kname = "indexer_prefill_kernel" if wl.group > 1 else "indexer_decode_kernel"
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("indexer_decode_kernel", wl.name),
-                "kernel": "indexer_decode_kernel",
-                "kernel_ms": k_ms, "algorithmic_bytes_per_launch": by}
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kname, wl.name),
+                "kernel": kname, "kernel_ms": k_ms, "algorithmic_bytes_per_launch": by}
+        if wl.group > 1:
+            # a group of m queries does m x 128 flop per key byte: report the
+            # matrix-core side too
+            fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
+            roof["mfma_frac"] = fl / (k_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS
 
     # ---- CPU baseline: the oracle on this host, on a bounded sample
     cpu = None
@@ -366,6 +382,8 @@ def main():
         # prefill queries share one key and latent cache, and that path is MFMA-bound
         step_bytes = sum(algorithmic_bytes(x, wl.k, wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, rmap[l] == l)
                          for l in range(wl.n_layers) for x in nn)
+        # a draft/verify group streams its sequence's keys once
+        step_bytes -= n_full * (sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn) - indexer_launch_bytes(wl, nn))
         line["step_hbm_frac"] = step_bytes / (result["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
     for k2 in ("all_full", "indexcache_speedup", "reuse_patterns", "reuse_overlap"):
         if k2 in result:

@@ -60,6 +60,11 @@ ic_status check_queries(const ic_queries *qs)
         return fail(IC_ERR_SHAPE, "max_n=%lld exceeds rows=%lld", (long long)qs->max_n, (long long)qs->rows);
     if (qs->T > 0 && (!aligned16(qs->base) || !aligned16(qs->n_valid)))
         return fail(IC_ERR_ALIGN, "queries base/n_valid not 16-byte aligned");
+    if (qs->group < 0 || qs->reserved != 0)
+        return fail(IC_ERR_SHAPE, "queries group=%d must be >= 0 and reserved=%d must be 0", qs->group,
+                    qs->reserved);
+    if (qs->group > 1 && qs->T % qs->group != 0)
+        return fail(IC_ERR_SHAPE, "T=%d is not a multiple of group=%d", qs->T, qs->group);
     return IC_OK;
 }
 
@@ -188,19 +193,31 @@ StackLayout stack_layout(const ic_queries *qs, const ic_dims *d)
     return L;
 }
 
-// Prefill (all queries on one sequence) uses the key-sharing GEMM form when it
-// is built for the shape; everything else streams keys per query.
+// Queries that share a sequence (prefill, or draft/verify groups of 2..16)
+// use the key-sharing GEMM form when it is built for the shape; everything
+// else streams keys per query. Returns the queries per workgroup, 0 for none.
+int32_t shared_key_group(const ic_queries *qs, int32_t H_I, int32_t D_I)
+{
+    if (!ic::indexer_prefill_supported(H_I, D_I))
+        return 0;
+    if (qs->same_seq && qs->T > 1)
+        return 16;
+    if (qs->group >= 2 && qs->group <= 16)
+        return qs->group;
+    return 0;
+}
+
 bool use_prefill_indexer(const ic_queries *qs, int32_t H_I, int32_t D_I)
 {
-    return qs->same_seq && qs->T > 1 && ic::indexer_prefill_supported(H_I, D_I);
+    return shared_key_group(qs, H_I, D_I) > 0;
 }
 
 hipError_t launch_indexer(const uint8_t *q_idx, const float *w, const uint8_t *k_idx, const ic_queries *qs,
                           int32_t H_I, int32_t D_I, float *scores, int64_t ld, uint32_t *hist0, hipStream_t st)
 {
-    if (use_prefill_indexer(qs, H_I, D_I))
-        return ic::launch_indexer_prefill(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I, D_I, scores,
-                                          ld, st);
+    if (const int32_t G = shared_key_group(qs, H_I, D_I))
+        return ic::launch_indexer_prefill(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I, D_I, G,
+                                          scores, ld, st);
     return ic::launch_indexer_decode(q_idx, w, k_idx, qs->base, qs->n_valid, qs->T, qs->max_n, H_I, D_I, scores, ld,
                                      hist0, st);
 }

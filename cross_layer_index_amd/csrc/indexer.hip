@@ -256,11 +256,15 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
     return hipGetLastError();
 }
 
-// ---- prefill form ------------------------------------------------------------
-// All queries read one sequence (causal prefill: query t sees tokens
-// 0..n_t-1 of the shared cache), so a key tile staged in LDS serves a group of
-// 16 queries: 8 waves x 2 queries, each wave holding its queries' q fragments
-// and head weights in registers.
+// ---- shared-sequence form ----------------------------------------------------
+// Queries that read one sequence share its key stream: causal prefill (every
+// query on one sequence; query t sees tokens 0..n_t-1) and draft/verify
+// decode (groups of G consecutive queries per sequence). A workgroup takes G
+// queries (G <= 2P) of one sequence and a chunk of its tokens; a key tile
+// staged in LDS serves all of them. Wave w takes query pair w % P (q
+// fragments and head weights in registers) and token split w / P of the
+// tile's S = 8 / P splits (P = 8 for prefill: every wave covers the whole
+// tile; smaller groups split the tokens instead).
 //
 // Tiles of 256 tokens go straight from memory into LDS (global_load_lds, no
 // registers), three buffers deep. Within a tile, 32-token group gi occupies
@@ -276,20 +280,23 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfQW = 2;                                  // queries per wave
-constexpr int kPfQ = kPfWaves * kPfQW;                    // queries per workgroup
+constexpr int kPfQ = kPfWaves * kPfQW;                    // most queries per workgroup
 constexpr int kPfTile = 256;                              // tokens per LDS tile
 constexpr int kPfGroups = kPfTile / 32;                   // 32-token groups per tile
 constexpr int kPfDI = 128;
 constexpr int kPfSlab = 1024;                             // bytes per fill instruction
 constexpr int kPfGroupBytes = 32 * kPfDI;                 // 4 slabs
-constexpr int kPfUnits = kPfGroups * kPfQW;
 static_assert(kPfGroups == kPfWaves, "wave w fills group w of each tile");
 
+template <int P>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
-    const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t T, float *__restrict__ scores,
-    int64_t ld, int64_t chunk)
+    const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t T, int32_t grp,
+    float *__restrict__ scores, int64_t ld, int64_t chunk)
 {
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8, "query pairs per workgroup");
+    constexpr int S = kPfWaves / P;                       // token splits of a tile
+    constexpr int kUnits = 2 * P;                         // (group, query) units per wave per tile
     using G = IdxGeom<kPfDI>;
     // three separate LDS objects (not one array): a read of one buffer is then
     // known not to alias the fills in flight into the others, and the
@@ -302,11 +309,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;
     const int j = lane & 31;
-    const int t_base = blockIdx.y * kPfQ;
+    const int t_base = blockIdx.y * grp;
+    const int qp = wave % P;                              // this wave's query pair
+    const int ts = wave / P;                              // and token split
 
-    // causal extent of the group: the largest n among its queries
+    // extent of the group: the largest n among its queries
     int64_t nmax = 0;
-    for (int i = 0; i < kPfQ; ++i)
+    for (int i = 0; i < grp; ++i)
         if (t_base + i < T)
             nmax = max(nmax, (int64_t)n[t_base + i]);
     const int64_t s_begin = (int64_t)blockIdx.x * chunk;
@@ -321,8 +330,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     float wr[kPfQW][2][16];
 #pragma unroll
     for (int i = 0; i < kPfQW; ++i) {
-        tq[i] = t_base + wave * kPfQW + i;
-        const bool ok = tq[i] < T;
+        tq[i] = t_base + qp * kPfQW + i;
+        const bool ok = qp * kPfQW + i < grp && tq[i] < T;
         nq[i] = ok ? n[tq[i]] : 0;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -365,6 +374,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
         }
     };
 
+    // this wave's k-th 32-token group of a tile
+    auto gidx = [&](int kk) { return S == 1 ? kk : ts + S * kk; };
     auto compute = [&](const uint8_t *tb, int64_t tile) {
         v8i b[2][G::KS];
         v16f acc[2][2];
@@ -378,14 +389,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
             c[0] = mfma_fp8_32x32x64(a[i][0][1], bb[1], c[0]);
             c[1] = mfma_fp8_32x32x64(a[i][1][1], bb[1], c[1]);
         };
-        bfrag(tb, 0, b[0]);
+        bfrag(tb, gidx(0), b[0]);
         mfmas(0);
 #pragma unroll
-        for (int u = 0; u < kPfUnits; ++u) {
-            const int gi = u >> 1, i = u & 1;
-            if (i == 0 && gi + 1 < kPfGroups)
-                bfrag(tb, gi + 1, b[(gi + 1) & 1]);
-            if (u + 1 < kPfUnits)
+        for (int u = 0; u < kUnits; ++u) {
+            const int kk = u >> 1, i = u & 1;
+            if (i == 0 && kk + 1 < P)
+                bfrag(tb, gidx(kk + 1), b[(kk + 1) & 1]);
+            if (u + 1 < kUnits)
                 mfmas(u + 1);
             const v16f(&c)[2] = acc[u & 1];
             float sum = 0.0f;
@@ -394,16 +405,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     sum = fmaf(wr[i][mt][r], relu_bits(c[mt][r]), sum);
-            if (u + 1 < kPfUnits) {
+            if (u + 1 < kUnits) {
                 // one MFMA, then a quarter of the epilogue, four times over
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
+                for (int q4 = 0; q4 < 4; ++q4) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
                 }
             }
             sum = half_sum(sum);
-            const int64_t s = tile + 32 * gi + j;
+            const int64_t s = tile + 32 * gidx(kk) + j;
             if (g == 0 && s < nq[i])
                 scores[(int64_t)tq[i] * ld + s] = sum;
         }
@@ -453,22 +464,37 @@ bool indexer_prefill_supported(int32_t H_I, int32_t D_I) { return H_I == 64 && D
 
 hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                                   const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
-                                  int32_t H_I, int32_t D_I, float *scores, int64_t ld, hipStream_t stream)
+                                  int32_t H_I, int32_t D_I, int32_t G, float *scores, int64_t ld,
+                                  hipStream_t stream)
 {
-    if (!indexer_prefill_supported(H_I, D_I))
+    if (!indexer_prefill_supported(H_I, D_I) || G < 1 || G > kPfQ)
         return hipErrorInvalidValue;
     if (T == 0 || max_n == 0)
         return hipSuccess;
-    const int64_t groups = (T + kPfQ - 1) / kPfQ;
-    // token chunks: enough workgroups to fill the chip several times over
-    int64_t chunk = kPfTile;
+    const int64_t groups = (T + G - 1) / G;
+    const int P = G <= 2 ? 1 : (G <= 4 ? 2 : (G <= 8 ? 4 : 8));
+    // token chunks: enough workgroups to fill the chip several times over, and
+    // at least 32 units per wave per workgroup (16 / P tiles) so that the tile
+    // ring hides the fill latency when a group has few queries
+    int64_t chunk = (int64_t)kPfTile * (16 / P);
     while (chunk < max_n && groups * ((max_n + chunk - 1) / chunk) > 16384)
         chunk *= 2;
     const int64_t nchunks = (max_n + chunk - 1) / chunk;
     if (groups > 65535)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)nchunks, (unsigned)groups), dim3(kPfThreads), 0,
-                       stream, q_idx, w, k_idx, base, n, T, scores, ld, chunk);
+    const dim3 grid((unsigned)nchunks, (unsigned)groups);
+    if (P == 1)
+        hipLaunchKernelGGL(indexer_prefill_kernel<1>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
+                           T, G, scores, ld, chunk);
+    else if (P == 2)
+        hipLaunchKernelGGL(indexer_prefill_kernel<2>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
+                           T, G, scores, ld, chunk);
+    else if (P == 4)
+        hipLaunchKernelGGL(indexer_prefill_kernel<4>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
+                           T, G, scores, ld, chunk);
+    else
+        hipLaunchKernelGGL(indexer_prefill_kernel<8>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
+                           T, G, scores, ld, chunk);
     return hipGetLastError();
 }
 

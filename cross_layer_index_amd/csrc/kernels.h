@@ -19,9 +19,11 @@ hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uin
                                  uint32_t *hist0, hipStream_t stream);
 // Prefill form: all queries read one sequence; key tiles are shared by a
 // group of queries through LDS.
+// Shared-sequence indexer: groups of G (<= 16) consecutive queries, each
+// group reading one sequence (every base[t] equal within a group).
 hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                                   const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
-                                  int32_t H_I, int32_t D_I, float *scores, int64_t ld,
+                                  int32_t H_I, int32_t D_I, int32_t G, float *scores, int64_t ld,
                                   hipStream_t stream);
 bool indexer_prefill_supported(int32_t H_I, int32_t D_I);
 

@@ -30,7 +30,7 @@ _i32, _i64, _sz, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.
 
 class ic_queries(ctypes.Structure):
     _fields_ = [("base", _P), ("n_valid", _P), ("T", _i32), ("same_seq", _i32), ("max_n", _i64),
-                ("rows", _i64)]
+                ("rows", _i64), ("group", _i32), ("reserved", _i32)]
 
 
 class ic_dims(ctypes.Structure):
@@ -105,6 +105,7 @@ class Queries:
     max_n: int
     rows: int
     same_seq: bool = False
+    group: int = 1          # consecutive queries sharing one sequence (draft/verify)
 
     @property
     def T(self) -> int:
@@ -114,13 +115,14 @@ class Queries:
         _dev(self.base, torch.int64, "base")
         _dev(self.n_valid, torch.int32, "n_valid")
         return ic_queries(_ptr(self.base), _ptr(self.n_valid), self.T, int(self.same_seq), int(self.max_n),
-                          int(self.rows))
+                          int(self.rows), int(self.group), 0)
 
 
-def make_queries(base: torch.Tensor, n_valid: torch.Tensor, rows: int, same_seq=False, device="cuda") -> Queries:
+def make_queries(base: torch.Tensor, n_valid: torch.Tensor, rows: int, same_seq=False, device="cuda",
+                 group: int = 1) -> Queries:
     nv = n_valid.to(torch.int32)
     return Queries(base.to(device=device, dtype=torch.int64).contiguous(), nv.to(device).contiguous(),
-                   int(nv.max().item()) if nv.numel() else 0, int(rows), same_seq)
+                   int(nv.max().item()) if nv.numel() else 0, int(rows), same_seq, int(group))
 
 
 def dims(H_I, D_I, k, H, D_qk, D_v, out_f32=False) -> ic_dims:

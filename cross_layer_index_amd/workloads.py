@@ -66,6 +66,8 @@ class Workload:
     len_range: Optional[tuple] = None   # ragged decode: n_t ~ U{a..b}
     prefill_first_pos: Optional[int] = None  # causal prefill: p_t = first + t
     prefill_rows: Optional[int] = None  # rows of the one shared cache (prefill)
+    group: int = 1                      # consecutive queries sharing one sequence (draft/verify)
+    seq_lengths: Optional[List[int]] = None  # with group > 1: rows of each sequence
     description: str = ""
 
     @property
@@ -85,6 +87,13 @@ class Workload:
         """int32 [T]: cached tokens each query sees."""
         if self.prefill_first_pos is not None:
             return torch.arange(self.T, dtype=torch.int64).add_(self.prefill_first_pos + 1).to(torch.int32)
+        if self.group > 1:
+            # draft/verify: the last `group` rows of a sequence are its queries'
+            # own tokens; query i of the group sees the rows up to its own
+            assert self.seq_lengths is not None and len(self.seq_lengths) * self.group == self.T
+            t = torch.arange(self.T, dtype=torch.int64)
+            L = torch.tensor(self.seq_lengths, dtype=torch.int64).repeat_interleave(self.group)
+            return (L - (self.group - 1) + t % self.group).clamp_(min=0).to(torch.int32)
         if self.lengths is not None:
             assert len(self.lengths) == self.T
             return torch.tensor(self.lengths, dtype=torch.int32)
@@ -96,12 +105,17 @@ class Workload:
         """int64 [T]: first cache row of each query's sequence."""
         if self.same_seq:
             return torch.zeros(self.T, dtype=torch.int64)
+        if self.group > 1:
+            L = torch.tensor(self.seq_lengths, dtype=torch.int64)
+            return (torch.cumsum(L, 0) - L).repeat_interleave(self.group)
         n = self.n_valid().to(torch.int64)
         return torch.cumsum(n, 0) - n
 
     def rows(self) -> int:
         if self.same_seq:
             return int(self.prefill_rows)
+        if self.group > 1:
+            return int(sum(self.seq_lengths))
         return int(self.n_valid().to(torch.int64).sum().item())
 
     def max_n(self) -> int:
@@ -194,6 +208,10 @@ WORKLOADS = {
         name="prefill_1m", seed=5, n_layers=2, full_layers=[0], T=4096, H_I=64, D_I=128, k=2048,
         H=128, D_qk=576, D_v=512, prefill_first_pos=1_044_480, prefill_rows=1_048_576,
         description="chunked prefill, 4096 queries at positions 1044480.., 1M-token cache, causal"),
+    "mtp_verify": Workload(
+        name="mtp_verify", seed=6, n_layers=1, full_layers=[0], T=32, H_I=64, D_I=128, k=2048,
+        H=128, D_qk=576, D_v=512, group=4, seq_lengths=[131072] * 8,
+        description="draft/verify decode: 8 sequences x 4 queries each over one shared cache, L=131072"),
     "edge_lengths": Workload(
         name="edge_lengths", seed=11, n_layers=1, full_layers=[0], T=9, H_I=64, D_I=128, k=2048,
         H=128, D_qk=576, D_v=512, lengths=[0, 1, 63, 64, 65, 2047, 2048, 2049, 4095],

@@ -66,7 +66,12 @@ enum { IC_OUT_BF16 = 0, IC_OUT_F32 = 1 };
  * positions are sequence-local: position s means row base[t] + s.
  * Decode: each query's cache is its own, n_valid[t] = its length.
  * Causal prefill: all queries read one sequence (same_seq = 1, every base[t]
- * equal) and n_valid[t] = position_t + 1 (a query sees itself). */
+ * equal) and n_valid[t] = position_t + 1 (a query sees itself).
+ * Draft/verify decode ([E] Jargon "MTP": a draft layer proposes several next
+ * tokens that one verify pass checks): group = m >= 2 says that queries
+ * g*m .. g*m + m - 1 read one sequence (every base[t] equal within a group),
+ * typically with n_valid growing by one from query to query. Queries of a
+ * group then share the indexer's key stream. */
 typedef struct {
     const int64_t *base;     /* device [T]                                     */
     const int32_t *n_valid;  /* device [T]                                     */
@@ -74,6 +79,9 @@ typedef struct {
     int32_t same_seq;        /* nonzero: every query reads the same rows       */
     int64_t max_n;           /* host: upper bound of n_valid[t]                */
     int64_t rows;            /* host: rows in the key and latent caches        */
+    int32_t group;           /* 0 or 1: no grouping; m >= 2: T % m == 0 and
+                                each run of m queries shares a sequence        */
+    int32_t reserved;        /* must be 0                                      */
 } ic_queries;
 
 /* Shapes. Indexer: H_I heads of dim D_I (D_I in {32, 64, 128}, 1 <= H_I <= 64).

@@ -66,6 +66,19 @@ def test_indexer_validation(ic):
     assert call_indexer(ic, Q(ic, T=0)) == ic.IC_OK                  # nothing to do, nothing launched
 
 
+def test_query_group_validation(ic):
+    """Draft/verify groups: T must be a multiple of the group size, the group
+    is non-negative and the reserved field zero; rejected before any launch."""
+    def G(group, T=4, reserved=0):
+        q = Q(ic, T=T)
+        q.group, q.reserved = group, reserved
+        return q
+    assert call_indexer(ic, G(-1)) == ic.IC_ERR_SHAPE
+    assert call_indexer(ic, G(3, T=4)) == ic.IC_ERR_SHAPE          # 4 queries are not groups of 3
+    assert call_indexer(ic, G(2, reserved=1)) == ic.IC_ERR_SHAPE
+    assert call_indexer(ic, G(3, T=0)) == ic.IC_OK                  # no queries: nothing to check
+
+
 def test_topk_validation(ic):
     qs = Q(ic)
     f = ic._lib.ic_topk

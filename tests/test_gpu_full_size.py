@@ -68,7 +68,7 @@ def oracle_query(orc, wl, qd, idx_src=None):
 def run_case(gpu, orc, wl, sample_t, sample_layers=None, device_gen=True):
     rmap = gpu.reuse_map_last_full(wl.is_full())
     lays, host = build_stack(gpu, wl, rmap, device_gen)
-    qs = gpu.make_queries(wl.base(), wl.n_valid(), wl.rows(), wl.same_seq)
+    qs = gpu.make_queries(wl.base(), wl.n_valid(), wl.rows(), wl.same_seq, group=wl.group)
     d = gpu.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v)
     st = gpu.LayerStack(lays, rmap, qs, d, wl.scale)
     passes = st()
@@ -113,6 +113,14 @@ def test_ragged_64_full(gpu, orc):
 def test_edge_lengths_full(gpu, orc):
     wl = W.WORKLOADS["edge_lengths"]
     run_case(gpu, orc, wl, list(range(wl.T)), device_gen=False)
+
+
+def test_mtp_verify_full(gpu, orc):
+    """Draft/verify decode at full size: 8 sequences x 4 queries sharing each
+    cache (the grouped key-sharing indexer); first and last query of three
+    groups checked against the oracle."""
+    wl = W.WORKLOADS["mtp_verify"]
+    run_case(gpu, orc, wl, [0, 3, 12, 15, 28, 31])
 
 
 def test_stack_78_full(gpu, orc):

@@ -37,7 +37,7 @@ def dev(li):
 
 
 def qs_of(ic, wl):
-    return ic.make_queries(wl.base(), wl.n_valid(), wl.rows(), wl.same_seq)
+    return ic.make_queries(wl.base(), wl.n_valid(), wl.rows(), wl.same_seq, group=wl.group)
 
 
 SMALL = {
@@ -51,6 +51,14 @@ SMALL = {
     "prefill_tail": W.scaled(W.WORKLOADS["prefill_1m"], T=37, prefill_first_pos=2900, prefill_rows=3000),
     "prefill_diag": W.scaled(W.WORKLOADS["prefill_1m"], T=300, prefill_first_pos=0, prefill_rows=300),
     "prefill_long": W.scaled(W.WORKLOADS["prefill_1m"], T=20, prefill_first_pos=70000, prefill_rows=70100),
+    # draft/verify groups sharing a sequence (one workgroup per group; waves
+    # split the tokens when the group has fewer than 16 queries)
+    "mtp_g2": W.scaled(W.WORKLOADS["mtp_verify"], T=6, group=2, seq_lengths=[3000, 1, 700]),
+    "mtp_g3": W.scaled(W.WORKLOADS["mtp_verify"], T=9, group=3, seq_lengths=[2, 2049, 513]),
+    "mtp_g4": W.scaled(W.WORKLOADS["mtp_verify"], T=8, group=4, seq_lengths=[5000, 257]),
+    "mtp_g5": W.scaled(W.WORKLOADS["mtp_verify"], T=10, group=5, seq_lengths=[1500, 4]),
+    "mtp_g8": W.scaled(W.WORKLOADS["mtp_verify"], T=16, group=8, seq_lengths=[2500, 40]),
+    "mtp_g16": W.scaled(W.WORKLOADS["mtp_verify"], T=32, group=16, seq_lengths=[1000, 3333]),
 }
 
 
