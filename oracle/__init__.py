@@ -60,7 +60,9 @@ def lib():
         L.orc_indexer_scores.argtypes = [i32, i32, i32, P, P, P, P, P, P, i64]
         L.orc_topk.argtypes = [i32, P, i64, P, i32, P]
         L.orc_sparse_mla.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, P, f64, P]
-        for f in (L.orc_decode_fp8, L.orc_decode_bf16, L.orc_indexer_scores, L.orc_topk, L.orc_sparse_mla):
+        L.orc_gated_output.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        for f in (L.orc_decode_fp8, L.orc_decode_bf16, L.orc_indexer_scores, L.orc_topk, L.orc_sparse_mla,
+                  L.orc_gated_output):
             f.restype = None
         _lib = L
     return _lib
@@ -160,6 +162,21 @@ def sparse_mla(q, kv, base, idx, sink, scale: float, D_v: int) -> np.ndarray:
         assert r.size == 0 or b[t] + int(r.max()) < kk.shape[0]
     out = np.empty((T, H, D_v), np.float64)
     lib().orc_sparse_mla(T, H, D_qk, D_v, _p(qq), _p(kk), _p(b), _p(ii), k, _p(sk), float(scale), _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ O5 -----
+def gated_output(o, wv_b, gate) -> np.ndarray:
+    """sigmoid(gate) * (wv_b @ o) per head, fp64 (bf16 inputs). o [T,H,D_v],
+    wv_b [H,D_o,D_v], gate [T,H,D_o]; returns [T,H,D_o]."""
+    oo = _np(o, np.uint16)
+    ww = _np(wv_b, np.uint16)
+    gg = _np(gate, np.uint16)
+    T, H, D_v = oo.shape
+    D_o = ww.shape[1]
+    assert ww.shape == (H, D_o, D_v) and gg.shape == (T, H, D_o)
+    out = np.empty((T, H, D_o), np.float64)
+    lib().orc_gated_output(T, H, D_v, D_o, _p(oo), _p(ww), _p(gg), _p(out))
     return out
 
 

@@ -17,6 +17,10 @@
  *       and on the 576-wide MLA row: 512 latent + 64 RoPE), two-pass softmax.
  * The layer-stack rule (O4: shared layers reuse the index of the last
  * preceding full layer, issue #90 "Indexer:" bullet) lives in __init__.py.
+ *   O5  the gated head output that follows the attention (issue #90, bullet on
+ *       the elementwise sigmoid gate): each head's latent output is first
+ *       decompressed by its value up-projection wv_b, then multiplied
+ *       elementwise by sigmoid of the gate pre-activation, before o_proj.
  *
  * Readings where the pages are silent are listed with each function.
  */
@@ -212,6 +216,32 @@ void orc_sparse_mla(int32_t T, int32_t H, int32_t D_qk, int32_t D_v,
                 o[v] /= den;
             free(qd);
             free(s);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- O5 ---- */
+
+/* Gated head output (issue #90, sigmoid-gate bullet: the gate multiplies the
+ * decompressed per-head attention output, so wv_b is applied first):
+ *   out[t,h,e] = sigmoid(gate[t,h,e]) * sum_c wv_b[h,e,c] * o[t,h,c]
+ * o [T,H,D_v], wv_b [H,D_o,D_v], gate [T,H,D_o] as bf16 bytes; out fp64.
+ * sigmoid(x) = 1 / (1 + e^-x). */
+void orc_gated_output(int32_t T, int32_t H, int32_t D_v, int32_t D_o, const uint16_t *o, const uint16_t *wv_b,
+                      const uint16_t *gate, double *out)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            const uint16_t *ot = o + ((int64_t)t * H + h) * D_v;
+            for (int32_t e = 0; e < D_o; ++e) {
+                const uint16_t *wr = wv_b + ((int64_t)h * D_o + e) * D_v;
+                double acc = 0.0;
+                for (int32_t c = 0; c < D_v; ++c)
+                    acc += orc_bf16_to_double(wr[c]) * orc_bf16_to_double(ot[c]);
+                const double g = orc_bf16_to_double(gate[((int64_t)t * H + h) * D_o + e]);
+                out[((int64_t)t * H + h) * D_o + e] = acc / (1.0 + exp(-g));
+            }
         }
     }
 }

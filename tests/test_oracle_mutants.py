@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_gate as TG
 import test_oracle_indexer as TI
 import test_oracle_mla as TM
 import test_oracle_topk as TT
@@ -31,6 +32,12 @@ MUTANTS = {
     "fp8_no_subnormal": ("v = ldexp((double)m / 8.0, -6);", "v = 0.0;"),
     "padding_not_skipped": ("if (row[j] < 0)\n                    continue;\n                const uint16_t *kr = kv + (base[t] + row[j]) * (int64_t)D_qk;\n                double p",
                             "if (row[j] < -1)\n                    continue;\n                const uint16_t *kr = kv + (base[t] + (row[j] < 0 ? 0 : row[j])) * (int64_t)D_qk;\n                double p"),
+    "gate_sign_flipped": ("acc / (1.0 + exp(-g))", "acc / (1.0 + exp(g))"),
+    "gate_dropped": ("= acc / (1.0 + exp(-g));", "= acc;"),
+    "wv_b_transposed": ("acc += orc_bf16_to_double(wr[c]) * orc_bf16_to_double(ot[c]);",
+                        "acc += orc_bf16_to_double(wv_b[((int64_t)h * D_v + c) * D_o + e]) * orc_bf16_to_double(ot[c]);"),
+    "gate_in_latent_space": ("const double g = orc_bf16_to_double(gate[((int64_t)t * H + h) * D_o + e]);",
+                             "const double g = orc_bf16_to_double(gate[((int64_t)t * H + h) * D_o + (e % 2) * 4 + 1]);"),
 }
 
 
@@ -51,6 +58,10 @@ def run_pins():
         ("mla_perm", lambda: TM.test_permutation_and_padding_invariant(oracle)),
         ("mla_value", lambda: TM.test_value_is_leading_part_and_linear(oracle)),
         ("mla_base", lambda: TM.test_rows_offset_by_base(oracle)),
+        ("gate_identity", lambda: TG.test_identity_upprojection(oracle)),
+        ("gate_rank1", lambda: TG.test_rank1_closed_form(oracle)),
+        ("gate_logistic", lambda: TG.test_gate_is_logistic(oracle)),
+        ("gate_heads", lambda: TG.test_heads_permute(oracle)),
     ]
     for name, fn in cases:
         try:
