@@ -314,6 +314,25 @@ def main():
             fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
             roof["mfma_frac"] = fl / (k_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS
 
+    # ---- the step after the path: gated head output (wv_b, sigmoid gate) for
+    # this workload's queries, timed alone over rotating inputs
+    gate = None
+    if args.only == "all" and wl.D_v == 512 and wl.name in ("decode_128k", "mtp_verify", "prefill_1m"):
+        D_o, NG = 128, 8
+        gsets = [W.gate_inputs(W.scaled(wl, seed=wl.seed + 100 + i), 0, D_o, device=dev) for i in range(NG)]
+        gouts = torch.empty((wl.T, wl.H, D_o), dtype=torch.bfloat16, device=dev)
+        gfns = [lambda x=x: ic.gated_output(x.o, x.wv_b, x.gate, out=gouts) for x in gsets]
+        grun = runner(gfns)
+        gk = 8 * NG
+        _, gev = timed(grun, gk, NG)
+        g_s = gev / gk
+        gbytes = 2 * (wl.H * D_o * wl.D_v + wl.T * wl.H * (wl.D_v + 2 * D_o))
+        gflops = 2 * wl.T * wl.H * D_o * wl.D_v
+        gate = {"T": wl.T, "H": wl.H, "D_v": wl.D_v, "D_o": D_o, "us": g_s * 1e6,
+                "GB/s": gbytes / g_s / 1e9, "hbm_frac": gbytes / g_s / 1e9 / HBM_PEAK_GBS,
+                "TFLOP/s": gflops / g_s / 1e12, "bf16_mfma_frac": gflops / g_s / 1e12 / BF16_PEAK_TFLOPS}
+        del gsets
+
     # ---- CPU baseline: the oracle on this host, on a bounded sample
     cpu = None
     if cpu_wanted:
@@ -388,6 +407,8 @@ def main():
     for k2 in ("all_full", "indexcache_speedup", "reuse_patterns", "reuse_overlap"):
         if k2 in result:
             line[k2] = result[k2]
+    if gate is not None:
+        line["gated_output"] = gate
     print(json.dumps(line))
 
 

@@ -294,6 +294,27 @@ IC_EXPORT ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const i
                       "sparse MLA launch");
 }
 
+IC_EXPORT ic_status ic_gated_output(const uint16_t *o, const uint16_t *wv_b, const uint16_t *gate, int32_t T,
+                                    int32_t H, int32_t D_v, int32_t D_o, uint16_t *out, void *stream)
+{
+    if (T < 0 || T > (1 << 20))
+        return fail(IC_ERR_SHAPE, "gated output: T=%d outside [0, 2^20]", T);
+    if (H < 1 || H > 4096)
+        return fail(IC_ERR_SHAPE, "gated output: H=%d outside [1, 4096]", H);
+    if (!ic::gated_output_supported(D_v, D_o))
+        return fail(IC_ERR_UNSUPPORTED, "gated output: (D_v, D_o)=(%d, %d) not built; D_v in {512, 64}, D_o a "
+                    "multiple of 64 in [64, 1024]", D_v, D_o);
+    if (T == 0)
+        return ok();
+    if (!o || !wv_b || !gate || !out)
+        return fail(IC_ERR_NULL, "gated output: o, wv_b, gate and out are required");
+    if (!aligned16(o) || !aligned16(wv_b) || !aligned16(gate) || !aligned16(out))
+        return fail(IC_ERR_ALIGN, "gated output: device pointers must be 16-byte aligned");
+    return hip_status(ic::launch_gated_output(o, wv_b, gate, T, H, D_v, D_o, out,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      "gated output launch");
+}
+
 IC_EXPORT ic_status ic_reuse_map_last_full(int32_t n_layers, const uint8_t *is_full, int32_t *reuse_map)
 {
     if (n_layers < 1)

@@ -49,4 +49,9 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_
                              int32_t D_v, const float *sink, float scale, void *out, int32_t out_f32,
                              const MlaPlan &plan, void *ws, hipStream_t stream);
 
+// Gated head output: out = sigmoid(gate) * (wv_b @ o) per head.
+bool gated_output_supported(int32_t D_v, int32_t D_o);
+hipError_t launch_gated_output(const uint16_t *o, const uint16_t *wv_b, const uint16_t *gate, int32_t T, int32_t H,
+                               int32_t D_v, int32_t D_o, uint16_t *out, hipStream_t stream);
+
 }  // namespace ic

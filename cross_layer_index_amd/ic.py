@@ -49,6 +49,7 @@ _SIGS = {
     "ic_topk": ([_P, _i64, _QP, _i32, _P, _P, _sz, _P], _i32),
     "ic_sparse_mla_workspace_size": ([_QP, _DP], _sz),
     "ic_sparse_mla": ([_P, _P, _QP, _P, _P, _f32, _DP, _P, _P, _sz, _P], _i32),
+    "ic_gated_output": ([_P, _P, _P, _i32, _i32, _i32, _i32, _P, _P], _i32),
     "ic_reuse_map_last_full": ([_i32, _P, _P], _i32),
     "ic_layer_stack_workspace_size": ([_QP, _DP], _sz),
     "ic_layer_stack": ([_i32, ctypes.POINTER(ic_layer), _P, _QP, _DP, _f32, _P, ctypes.POINTER(_i32), _P, _sz,
@@ -222,6 +223,24 @@ def sparse_mla(q, kv, qs: Queries, idx, sink, scale: float, D_v: int, out=None, 
     _shape(out, (qs.T, H, D_v), "out")
     _check(_lib.ic_sparse_mla(_ptr(q), _ptr(kv), ctypes.byref(qc), _ptr(idx), _ptr(sink), float(scale),
                               ctypes.byref(d), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def gated_output(o, wv_b, gate, out=None, stream=None):
+    """sigmoid(gate) * (wv_b @ o) per head: o [T,H,D_v], wv_b [H,D_o,D_v],
+    gate [T,H,D_o], all bf16; returns out [T,H,D_o] bf16."""
+    _bf16(o, "o")
+    _bf16(wv_b, "wv_b")
+    _bf16(gate, "gate")
+    T, H, D_v = o.shape
+    D_o = wv_b.shape[1]
+    _shape(wv_b, (H, D_o, D_v), "wv_b")
+    _shape(gate, (T, H, D_o), "gate")
+    if out is None:
+        out = torch.empty((T, H, D_o), dtype=torch.bfloat16, device=o.device)
+    _bf16(out, "out")
+    _shape(out, (T, H, D_o), "out")
+    _check(_lib.ic_gated_output(_ptr(o), _ptr(wv_b), _ptr(gate), T, H, D_v, D_o, _ptr(out), _stream(stream)))
     return out
 
 

@@ -33,6 +33,7 @@ import torch
 # tensor ids inside one layer
 _TID_QI, _TID_W, _TID_KI, _TID_Q, _TID_KV, _TID_SINK = 1, 2, 3, 4, 5, 6
 _TID_LEN = 0
+_TID_GO, _TID_GW, _TID_GG = 7, 8, 9          # gated head output: o, wv_b, gate
 
 
 def sub_seed(seed: int, layer: int, tensor_id: int) -> int:
@@ -146,6 +147,25 @@ def _randn_bf16(shape, g, device, chunk_rows=1 << 16):
         flat[r0:r1] = torch.randn((r1 - r0, flat.shape[1]), generator=g, device=device,
                                   dtype=torch.float32).to(torch.bfloat16)
     return out
+
+
+@dataclass
+class GateInputs:
+    o: torch.Tensor       # bfloat16 [T, H, D_v]   latent per-head attention output
+    wv_b: torch.Tensor    # bfloat16 [H, D_o, D_v] value up-projection (synthetic weights)
+    gate: torch.Tensor    # bfloat16 [T, H, D_o]   gate pre-activation
+
+
+def gate_inputs(wl: Workload, layer: int, D_o: int = 128, device="cpu") -> GateInputs:
+    """Synthetic inputs of the gated head output: o ~ N(0,1), wv_b ~ N(0,1/D_v)
+    (so the decompressed values stay O(1)), gate ~ N(0, 4)."""
+    s = wl.seed
+    o = _randn_bf16((wl.T, wl.H, wl.D_v), _gen(device, sub_seed(s, layer, _TID_GO)), device)
+    w = torch.randn((wl.H * D_o, wl.D_v), generator=_gen(device, sub_seed(s, layer, _TID_GW)), device=device,
+                    dtype=torch.float32).mul_(1.0 / math.sqrt(wl.D_v)).to(torch.bfloat16).view(wl.H, D_o, wl.D_v)
+    g = torch.randn((wl.T, wl.H, D_o), generator=_gen(device, sub_seed(s, layer, _TID_GG)), device=device,
+                    dtype=torch.float32).mul_(2.0).to(torch.bfloat16)
+    return GateInputs(o, w, g)
 
 
 def layer_inputs(wl: Workload, layer: int, device="cpu", with_indexer=True, variant: int = 0) -> LayerInputs:

@@ -136,6 +136,21 @@ ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries 
                         const int32_t *idx, const float *sink, float scale, const ic_dims *d,
                         void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Gated head output, the step after the sparse attention ([G] bullet on the
+ * elementwise sigmoid gate: it multiplies the decompressed per-head output
+ * before o_proj, so the value up-projection wv_b must be applied first rather
+ * than folded into o_proj):
+ *   out[t,h,e] = sigmoid(gate[t,h,e]) * sum_c wv_b[h,e,c] * o[t,h,c]
+ *   o    [T, H, D_v] bf16  the latent per-head output of ic_sparse_mla
+ *   wv_b [H, D_o, D_v] bf16 the per-head value up-projection
+ *   gate [T, H, D_o] bf16  the gate's pre-activation (linear_gate's output)
+ *   out  [T, H, D_o] bf16 (round to nearest even)
+ * Products run on bf16 matrix cores with fp32 accumulation; sigmoid in fp32.
+ * Built: D_v in {512, 64}; D_o a multiple of 64 in [64, 1024]. o_proj itself
+ * and linear_gate are plain GEMMs outside this library. */
+ic_status ic_gated_output(const uint16_t *o, const uint16_t *wv_b, const uint16_t *gate, int32_t T, int32_t H,
+                          int32_t D_v, int32_t D_o, uint16_t *out, void *stream);
+
 /* One attention layer's tensors for ic_layer_stack. q_idx, w and k_idx are
  * read only on full layers and may be NULL on shared ones. */
 typedef struct {

@@ -28,7 +28,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(ic):
     names = declared_entry_points()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(ic._lib, n), n
     assert sorted(ic.EXPORTED) == names
@@ -207,3 +207,14 @@ def test_reuse_patterns_match_the_pages_counts(orc):
             assert m[l] == max(f for f in fl if f <= l)
     assert "".join("F" if l in set(W.REUSE_PATTERNS["hy4_21"]) else "S" for l in range(6)) == \
         golden["hy4_pattern_prefix"]
+
+
+def test_gated_output_validation(ic):
+    f = ic._lib.ic_gated_output
+    assert f(FAKE, FAKE, FAKE, -1, 128, 512, 128, FAKE, None) == ic.IC_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1, 0, 512, 128, FAKE, None) == ic.IC_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1, 128, 576, 128, FAKE, None) == ic.IC_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 128, 512, 96, FAKE, None) == ic.IC_ERR_UNSUPPORTED
+    assert f(None, FAKE, FAKE, 1, 128, 512, 128, FAKE, None) == ic.IC_ERR_NULL
+    assert f(FAKE, FAKE + 4, FAKE, 1, 128, 512, 128, FAKE, None) == ic.IC_ERR_ALIGN
+    assert f(None, None, None, 0, 128, 512, 128, None, None) == ic.IC_OK          # nothing to do

@@ -249,3 +249,26 @@ def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc):
                          out_f32=True).float().cpu().numpy()
     ref = orc.sparse_mla(li.q, li.kv, wl.base(), clean, li.sink, wl.scale, wl.D_v)
     assert_close(got, ref, True)
+
+
+# ------------------------------------------------------------ gated output --
+@pytest.mark.parametrize("T,H,D_v,D_o", [(1, 128, 512, 128), (5, 3, 512, 64), (17, 2, 512, 192),
+                                         (33, 4, 64, 64), (40, 1, 512, 1024)])
+def test_gated_output_close(gpu, orc, T, H, D_v, D_o):
+    """sigmoid(gate) * (wv_b @ o) per head against the fp64 oracle: partial
+    query blocks (T % 16), several column blocks, both built latent widths."""
+    wl = W.scaled(W.WORKLOADS["decode_128k"], T=T, H=H, D_v=D_v)
+    gi = W.gate_inputs(wl, 0, D_o)
+    got = gpu.gated_output(gi.o.cuda(), gi.wv_b.cuda(), gi.gate.cuda()).float().cpu().numpy()
+    ref = orc.gated_output(gi.o, gi.wv_b, gi.gate)
+    assert_close(got, ref, False)
+
+
+def test_gated_output_prefill_sampled(gpu, orc):
+    """4096 queries x 128 heads (the prefill shape), oracle on sampled queries."""
+    wl = W.scaled(W.WORKLOADS["prefill_1m"], T=4096)
+    gi = W.gate_inputs(wl, 1, 128, device="cuda")
+    got = gpu.gated_output(gi.o, gi.wv_b, gi.gate).float().cpu().numpy()
+    for t in (0, 15, 16, 2047, 4095):
+        ref = orc.gated_output(gi.o[t:t + 1].cpu(), gi.wv_b.cpu(), gi.gate[t:t + 1].cpu())
+        assert_close(got[t:t + 1], ref, False)
