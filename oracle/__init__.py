@@ -61,8 +61,12 @@ def lib():
         L.orc_topk.argtypes = [i32, P, i64, P, i32, P]
         L.orc_sparse_mla.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, P, f64, P]
         L.orc_gated_output.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.orc_encode_fp8_e4m3fn.argtypes = [f64]
+        L.orc_encode_fp8_e4m3fn.restype = ctypes.c_uint8
+        L.orc_index_key.argtypes = [i32, i32, i32, P, P, P, f64, P, P, P, P]
+        L.orc_latent_row.argtypes = [i32, i32, i32, P, P, P, P]
         for f in (L.orc_decode_fp8, L.orc_decode_bf16, L.orc_indexer_scores, L.orc_topk, L.orc_sparse_mla,
-                  L.orc_gated_output):
+                  L.orc_gated_output, L.orc_index_key, L.orc_latent_row):
             f.restype = None
         _lib = L
     return _lib
@@ -177,6 +181,54 @@ def gated_output(o, wv_b, gate) -> np.ndarray:
     assert ww.shape == (H, D_o, D_v) and gg.shape == (T, H, D_o)
     out = np.empty((T, H, D_o), np.float64)
     lib().orc_gated_output(T, H, D_v, D_o, _p(oo), _p(ww), _p(gg), _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ O6 -----
+def encode_fp8(x) -> np.ndarray:
+    """Real values -> fp8 e4m3fn codes: nearest code, ties to even mantissa,
+    saturating at +-448, sign kept."""
+    a = np.asarray(x, np.float64)
+    f = lib().orc_encode_fp8_e4m3fn
+    return np.array([f(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+
+
+def _rope_check(rope, pos, D_rope):
+    rp = _np(rope, np.float32)
+    ps = _np(pos, np.int32)
+    if D_rope:
+        assert D_rope % 2 == 0 and rp.ndim == 2 and rp.shape[1] == D_rope
+        assert np.all((ps >= 0) & (ps < rp.shape[0]))
+    return rp, ps
+
+
+def index_key(k_pre, ln_w, ln_b, eps: float, rope, pos, D_rope: int):
+    """Indexer key of each new token: LayerNorm with bias, interleaved RoPE on
+    the trailing D_rope entries at pos[t], fp8 cast. Returns (y fp64 [T, D_I],
+    code uint8 [T, D_I]); the code is decided on y rounded to fp32."""
+    x = _np(k_pre, np.uint16)
+    w = _np(ln_w, np.float32)
+    b = _np(ln_b, np.float32)
+    T, D_I = x.shape
+    assert w.shape == (D_I,) and b.shape == (D_I,) and 0 <= D_rope <= D_I and eps > 0
+    rp, ps = _rope_check(rope, pos, D_rope)
+    assert ps.shape == (T,)
+    y = np.empty((T, D_I), np.float64)
+    code = np.empty((T, D_I), np.uint8)
+    lib().orc_index_key(T, D_I, D_rope, _p(x), _p(w), _p(b), float(eps), _p(rp), _p(ps), _p(y), _p(code))
+    return y, code
+
+
+def latent_row(kv_pre, rope, pos, D_rope: int) -> np.ndarray:
+    """Latent row of each new token: leading entries as given, trailing D_rope
+    entries rotated (interleaved pairs) at pos[t]. Returns fp64 [T, D_qk]."""
+    x = _np(kv_pre, np.uint16)
+    T, D_qk = x.shape
+    assert 0 <= D_rope <= D_qk
+    rp, ps = _rope_check(rope, pos, D_rope)
+    assert ps.shape == (T,)
+    out = np.empty((T, D_qk), np.float64)
+    lib().orc_latent_row(T, D_qk, D_rope, _p(x), _p(rp), _p(ps), _p(out))
     return out
 
 

@@ -21,6 +21,10 @@
  *       the elementwise sigmoid gate): each head's latent output is first
  *       decompressed by its value up-projection wv_b, then multiplied
  *       elementwise by sigmoid of the gate pre-activation, before o_proj.
+ *   O6  the cache write that precedes the path: the new token's indexer key
+ *       (LayerNorm with bias, interleaved RoPE on its trailing span, fp8
+ *       cast) and its latent row (latent as given, interleaved RoPE on the
+ *       trailing 64 entries).
  *
  * Readings where the pages are silent are listed with each function.
  */
@@ -243,5 +247,106 @@ void orc_gated_output(int32_t T, int32_t H, int32_t D_v, int32_t D_o, const uint
                 out[((int64_t)t * H + h) * D_o + e] = acc / (1.0 + exp(-g));
             }
         }
+    }
+}
+
+/* ---------------------------------------------------------------- O6 ---- */
+
+/* The cache write that precedes the path: for each new token, its indexer key
+ * and its latent row are stored in the two caches (issue #90: the "Indexer:"
+ * bullet puts the key through a LayerNorm with bias whose eps is the model's
+ * RMS-norm eps; the RoPE bullet says the rotary embedding is interleaved,
+ * i.e. not NeoX style; the first paragraph fixes the 576-wide latent row as
+ * 512 latent entries plus 64 RoPE entries).
+ * Readings: the rotary angles come as a table (cos and sin per position and
+ * frequency), so no base or scaling rule is assumed; the rotated span of the
+ * indexer key is its trailing D_rope entries, the same place as in the latent
+ * row; the key is stored as a plain fp8 cast, without a scale, as the indexer
+ * reads it. */
+
+/* fp8 e4m3fn code of a real value: the nearest finite code, ties to the code
+ * with even mantissa; magnitudes past 448 take 448 (the format has no
+ * infinity, so the cast saturates). The 127 non-negative finite codes are
+ * scanned in increasing value. The sign is kept (-0 gives 0x80); NaN gives
+ * 0x7F. */
+uint8_t orc_encode_fp8_e4m3fn(double x)
+{
+    if (isnan(x))
+        return 0x7F;
+    const int sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs(x);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(orc_fp8_e4m3fn_to_double((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Interleaved rotary embedding of one span of D_rope entries at position p:
+ * entries 2i and 2i+1 form a pair that turns by the angle whose cosine is
+ * rope[p, i] and whose sine is rope[p, D_rope/2 + i]. */
+static void orc_rope_interleaved(double *x, int32_t D_rope, const float *rope, int32_t p)
+{
+    const float *cs = rope + (int64_t)p * D_rope;
+    for (int32_t i = 0; i < D_rope / 2; ++i) {
+        const double c = cs[i], s = cs[D_rope / 2 + i];
+        const double x0 = x[2 * i], x1 = x[2 * i + 1];
+        x[2 * i] = x0 * c - x1 * s;
+        x[2 * i + 1] = x1 * c + x0 * s;
+    }
+}
+
+/* Indexer key of each new token:
+ *   y = (x - mean(x)) / sqrt(var(x) + eps) * ln_w + ln_b, var the mean squared
+ *       deviation (LayerNorm with bias);
+ *   the trailing D_rope entries of y rotate at position pos[t];
+ *   code = fp8 e4m3fn of y, the decision taken on y rounded to fp32 (the
+ *          precision the stored code is computed in).
+ * k_pre [T, D_I] bf16, ln_w and ln_b [D_I] fp32, rope [*, D_rope] fp32,
+ * pos [T]; y [T, D_I] fp64 and code [T, D_I] are outputs. */
+void orc_index_key(int32_t T, int32_t D_I, int32_t D_rope, const uint16_t *k_pre, const float *ln_w,
+                   const float *ln_b, double eps, const float *rope, const int32_t *pos, double *y, uint8_t *code)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; ++t) {
+        double *yt = y + (int64_t)t * D_I;
+        double mean = 0.0, var = 0.0;
+        for (int32_t d = 0; d < D_I; ++d) {
+            yt[d] = orc_bf16_to_double(k_pre[(int64_t)t * D_I + d]);
+            mean += yt[d];
+        }
+        mean /= D_I;
+        for (int32_t d = 0; d < D_I; ++d)
+            var += (yt[d] - mean) * (yt[d] - mean);
+        var /= D_I;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int32_t d = 0; d < D_I; ++d)
+            yt[d] = (yt[d] - mean) * inv * (double)ln_w[d] + (double)ln_b[d];
+        if (D_rope > 0)
+            orc_rope_interleaved(yt + (D_I - D_rope), D_rope, rope, pos[t]);
+        for (int32_t d = 0; d < D_I; ++d)
+            code[(int64_t)t * D_I + d] = orc_encode_fp8_e4m3fn((double)(float)yt[d]);
+    }
+}
+
+/* Latent row of each new token: the leading D_qk - D_rope entries (the
+ * compressed latent, which is also the value) are stored as given; the
+ * trailing D_rope entries rotate at position pos[t].
+ * kv_pre [T, D_qk] bf16 -> out [T, D_qk] fp64. */
+void orc_latent_row(int32_t T, int32_t D_qk, int32_t D_rope, const uint16_t *kv_pre, const float *rope,
+                    const int32_t *pos, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; ++t) {
+        double *ot = out + (int64_t)t * D_qk;
+        for (int32_t d = 0; d < D_qk; ++d)
+            ot[d] = orc_bf16_to_double(kv_pre[(int64_t)t * D_qk + d]);
+        if (D_rope > 0)
+            orc_rope_interleaved(ot + (D_qk - D_rope), D_rope, rope, pos[t]);
     }
 }

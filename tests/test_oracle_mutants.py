@@ -13,6 +13,7 @@ import test_oracle_gate as TG
 import test_oracle_indexer as TI
 import test_oracle_mla as TM
 import test_oracle_topk as TT
+import test_oracle_write as TW
 
 MUTANTS = {
     "dropped_relu": ("if (dot > 0.0)\n                    I +=", "if (1)\n                    I +="),
@@ -38,6 +39,20 @@ MUTANTS = {
                         "acc += orc_bf16_to_double(wv_b[((int64_t)h * D_v + c) * D_o + e]) * orc_bf16_to_double(ot[c]);"),
     "gate_in_latent_space": ("const double g = orc_bf16_to_double(gate[((int64_t)t * H + h) * D_o + e]);",
                              "const double g = orc_bf16_to_double(gate[((int64_t)t * H + h) * D_o + (e % 2) * 4 + 1]);"),
+    "rope_neox_pairs": ("const double x0 = x[2 * i], x1 = x[2 * i + 1];\n        x[2 * i] = x0 * c - x1 * s;\n        x[2 * i + 1] = x1 * c + x0 * s;",
+                        "const double x0 = x[i], x1 = x[i + D_rope / 2];\n        x[i] = x0 * c - x1 * s;\n        x[i + D_rope / 2] = x1 * c + x0 * s;"),
+    "rope_sign_flipped": ("x[2 * i] = x0 * c - x1 * s;", "x[2 * i] = x0 * c + x1 * s;"),
+    "rope_sin_cos_swapped": ("const double c = cs[i], s = cs[D_rope / 2 + i];", "const double s = cs[i], c = cs[D_rope / 2 + i];"),
+    "ln_unbiased_variance": ("var /= D_I;", "var /= (D_I - 1);"),
+    "ln_bias_dropped": (" * (double)ln_w[d] + (double)ln_b[d];", " * (double)ln_w[d];"),
+    "ln_eps_outside_sqrt": ("1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    "key_rope_on_leading_span": ("orc_rope_interleaved(yt + (D_I - D_rope), D_rope, rope, pos[t]);",
+                                 "orc_rope_interleaved(yt, D_rope, rope, pos[t]);"),
+    "latent_rope_on_leading_span": ("orc_rope_interleaved(ot + (D_qk - D_rope), D_rope, rope, pos[t]);",
+                                    "orc_rope_interleaved(ot, D_rope, rope, pos[t]);"),
+    "fp8_ties_away_from_zero": ("if (d < bd || (d == bd && (c & 1) == 0)) {", "if (d <= bd) {"),
+    "fp8_truncates": ("const double d = fabs(orc_fp8_e4m3fn_to_double((uint8_t)c) - a);",
+                      "const double d = orc_fp8_e4m3fn_to_double((uint8_t)c) <= a ? a - orc_fp8_e4m3fn_to_double((uint8_t)c) : INFINITY;"),
 }
 
 
@@ -62,6 +77,15 @@ def run_pins():
         ("gate_rank1", lambda: TG.test_rank1_closed_form(oracle)),
         ("gate_logistic", lambda: TG.test_gate_is_logistic(oracle)),
         ("gate_heads", lambda: TG.test_heads_permute(oracle)),
+        ("fp8_codes", lambda: TW.test_fp8_every_code_round_trips(oracle)),
+        ("fp8_mid", lambda: TW.test_fp8_midpoints_tie_to_even(oracle)),
+        ("fp8_torch", lambda: TW.test_fp8_matches_torch_cast_in_range(oracle)),
+        ("fp8_sat", lambda: TW.test_fp8_saturates(oracle)),
+        ("ln_torch", lambda: TW.test_layer_norm_matches_torch(oracle, 64)),
+        ("ln_const", lambda: TW.test_layer_norm_constant_row_gives_bias(oracle)),
+        ("rope_latent", lambda: TW.test_latent_row_rotates_trailing_pairs(oracle)),
+        ("rope_relpos", lambda: TW.test_rope_relative_position(oracle)),
+        ("rope_key", lambda: TW.test_index_key_rotates_trailing_span(oracle)),
     ]
     for name, fn in cases:
         try:
