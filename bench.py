@@ -333,6 +333,33 @@ def main():
                 "TFLOP/s": gflops / g_s / 1e12, "bf16_mfma_frac": gflops / g_s / 1e12 / BF16_PEAK_TFLOPS}
         del gsets
 
+    # ---- the step before the path: the cache write of the tokens this
+    # workload's queries add (indexer key: LayerNorm, RoPE, fp8 cast; latent
+    # row: copy and RoPE), timed alone over rotating inputs at the workload's
+    # positions, into caches of T rows
+    wpath = None
+    if args.only == "all" and wl.D_v == 512 and wl.name in ("decode_128k", "mtp_verify", "ragged_64", "prefill_1m"):
+        NW = 8
+        D_rope = W.d_rope(wl)
+        table = W.rope_table(max(1, max(nn)), D_rope).to(dev)
+        kc = torch.empty((wl.T, wl.D_I), dtype=torch.uint8, device=dev)
+        kvc = torch.empty((wl.T, wl.D_qk), dtype=torch.bfloat16, device=dev)
+        dst = torch.arange(wl.T, dtype=torch.int64, device=dev)
+        wfns = []
+        for i in range(NW):
+            x = W.write_inputs(wl, i, device=dev, rope=table)
+            tk = ic.Tokens(dst, x.pos, wl.T, table)
+            wfns.append(lambda x=x, tk=tk: ic.write_cache(tk, x.k_pre, x.ln_w, x.ln_b, x.eps, kc, x.kv_pre, kvc))
+        wk = 8 * NW
+        _, wev = timed(runner(wfns), wk, NW)
+        w_s = wev / wk
+        per_tok = 3 * wl.D_I + 4 * wl.D_qk + 4 * D_rope + 12
+        wbytes = wl.T * per_tok + 8 * wl.D_I
+        wpath = {"T": wl.T, "D_I": wl.D_I, "D_qk": wl.D_qk, "D_rope": D_rope, "us": w_s * 1e6,
+                 "bytes_per_token": per_tok, "GB/s": wbytes / w_s / 1e9,
+                 "hbm_frac": wbytes / w_s / 1e9 / HBM_PEAK_GBS}
+        del wfns, table
+
     # ---- CPU baseline: the oracle on this host, on a bounded sample
     cpu = None
     if cpu_wanted:
@@ -409,6 +436,8 @@ def main():
             line[k2] = result[k2]
     if gate is not None:
         line["gated_output"] = gate
+    if wpath is not None:
+        line["write_path"] = wpath
     print(json.dumps(line))
 
 

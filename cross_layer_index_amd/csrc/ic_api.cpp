@@ -2,6 +2,7 @@
 // the HIP kernels. Semantics of every entry point are documented in ic.h.
 #include "ic.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -313,6 +314,59 @@ IC_EXPORT ic_status ic_gated_output(const uint16_t *o, const uint16_t *wv_b, con
     return hip_status(ic::launch_gated_output(o, wv_b, gate, T, H, D_v, D_o, out,
                                               reinterpret_cast<hipStream_t>(stream)),
                       "gated output launch");
+}
+
+IC_EXPORT ic_status ic_write_cache(const ic_tokens *tk, const uint16_t *k_pre, const float *ln_w, const float *ln_b,
+                                   float eps, int32_t D_I, uint8_t *k_idx, const uint16_t *kv_pre, int32_t D_qk,
+                                   uint16_t *kv, void *stream)
+{
+    if (!tk)
+        return fail(IC_ERR_NULL, "write cache: the tokens descriptor is required");
+    if (tk->T < 0 || tk->T > (1 << 24))
+        return fail(IC_ERR_SHAPE, "write cache: T=%d outside [0, 2^24]", tk->T);
+    if (tk->rows < 1)
+        return fail(IC_ERR_SHAPE, "write cache: rows=%lld must be >= 1", (long long)tk->rows);
+    if (tk->reserved != 0)
+        return fail(IC_ERR_SHAPE, "write cache: reserved field must be 0");
+    if (tk->D_rope < 0 || tk->D_rope > 128 || (tk->D_rope & 1))
+        return fail(IC_ERR_SHAPE, "write cache: D_rope=%d must be even and in [0, 128]", tk->D_rope);
+    if (tk->T == 0)
+        return ok();                                   // nothing to write
+    const bool key = k_pre || ln_w || ln_b || k_idx;
+    const bool lat = kv_pre || kv;
+    if (!key && !lat)
+        return fail(IC_ERR_NULL, "write cache: neither the key nor the latent row is given");
+    if (key && (!k_pre || !ln_w || !ln_b || !k_idx))
+        return fail(IC_ERR_NULL, "write cache: k_pre, ln_w, ln_b and k_idx go together");
+    if (lat && (!kv_pre || !kv))
+        return fail(IC_ERR_NULL, "write cache: kv_pre and kv go together");
+    if (key) {
+        if (D_I != 32 && D_I != 64 && D_I != 128)
+            return fail(IC_ERR_UNSUPPORTED, "write cache: D_I=%d not built (32, 64, 128)", D_I);
+        if (!(eps > 0.0f) || !std::isfinite(eps))
+            return fail(IC_ERR_SHAPE, "write cache: eps must be finite and > 0");
+        if (tk->key_rope && tk->D_rope > D_I)
+            return fail(IC_ERR_SHAPE, "write cache: D_rope=%d exceeds D_I=%d", tk->D_rope, D_I);
+    }
+    if (lat && (D_qk < 8 || D_qk > 4096 || D_qk % 8 || tk->D_rope > D_qk || (D_qk - tk->D_rope) % 8))
+        return fail(IC_ERR_UNSUPPORTED, "write cache: D_qk=%d with D_rope=%d not built (D_qk and D_qk - D_rope "
+                    "multiples of 8, D_qk <= 4096)", D_qk, tk->D_rope);
+    const bool rotates = tk->D_rope > 0 && (lat || tk->key_rope);
+    if (rotates && (!tk->rope || tk->n_pos < 1))
+        return fail(IC_ERR_NULL, "write cache: D_rope > 0 needs the rotary table (n_pos >= 1)");
+    if (!tk->row || !tk->pos)
+        return fail(IC_ERR_NULL, "write cache: row and pos are required");
+    const void *ptrs[] = {tk->row, tk->pos, rotates ? tk->rope : nullptr, k_pre, ln_w, ln_b, k_idx, kv_pre, kv};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(IC_ERR_ALIGN, "write cache: device pointers must be 16-byte aligned");
+    // a shared layer without key rotation reads no table: pass D_rope only where it is used
+    const int32_t D_rope = rotates ? tk->D_rope : 0;
+    return hip_status(ic::launch_write_cache(tk->row, tk->pos, tk->T, tk->rows, rotates ? tk->rope : nullptr,
+                                             tk->n_pos, D_rope, key && tk->key_rope ? 1 : 0, key ? k_pre : nullptr,
+                                             ln_w, ln_b, eps, D_I, k_idx, lat ? kv_pre : nullptr, D_qk, kv,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                      "write cache launch");
 }
 
 IC_EXPORT ic_status ic_reuse_map_last_full(int32_t n_layers, const uint8_t *is_full, int32_t *reuse_map)

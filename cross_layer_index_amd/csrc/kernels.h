@@ -54,4 +54,13 @@ bool gated_output_supported(int32_t D_v, int32_t D_o);
 hipError_t launch_gated_output(const uint16_t *o, const uint16_t *wv_b, const uint16_t *gate, int32_t T, int32_t H,
                                int32_t D_v, int32_t D_o, uint16_t *out, hipStream_t stream);
 
+// Cache write of new tokens: indexer key (LayerNorm with bias, optional
+// interleaved RoPE on its trailing span, fp8 cast) and latent row (copy plus
+// interleaved RoPE on the trailing span). k_pre == nullptr skips the key,
+// kv_pre == nullptr the latent row.
+hipError_t launch_write_cache(const int64_t *row, const int32_t *pos, int32_t T, int64_t rows, const float *rope,
+                              int64_t n_pos, int32_t D_rope, int32_t key_rope, const uint16_t *k_pre,
+                              const float *ln_w, const float *ln_b, float eps, int32_t D_I, uint8_t *k_idx,
+                              const uint16_t *kv_pre, int32_t D_qk, uint16_t *kv, hipStream_t stream);
+
 }  // namespace ic

@@ -42,6 +42,11 @@ class ic_layer(ctypes.Structure):
     _fields_ = [("q_idx", _P), ("w", _P), ("k_idx", _P), ("q", _P), ("kv", _P), ("sink", _P), ("out", _P)]
 
 
+class ic_tokens(ctypes.Structure):
+    _fields_ = [("row", _P), ("pos", _P), ("T", _i32), ("D_rope", _i32), ("rows", _i64), ("rope", _P),
+                ("n_pos", _i64), ("key_rope", _i32), ("reserved", _i32)]
+
+
 _QP, _DP = ctypes.POINTER(ic_queries), ctypes.POINTER(ic_dims)
 _SIGS = {
     "ic_indexer_score": ([_P, _P, _P, _QP, _i32, _i32, _P, _i64, _P], _i32),
@@ -50,6 +55,7 @@ _SIGS = {
     "ic_sparse_mla_workspace_size": ([_QP, _DP], _sz),
     "ic_sparse_mla": ([_P, _P, _QP, _P, _P, _f32, _DP, _P, _P, _sz, _P], _i32),
     "ic_gated_output": ([_P, _P, _P, _i32, _i32, _i32, _i32, _P, _P], _i32),
+    "ic_write_cache": ([ctypes.POINTER(ic_tokens), _P, _P, _P, _f32, _i32, _P, _P, _i32, _P, _P], _i32),
     "ic_reuse_map_last_full": ([_i32, _P, _P], _i32),
     "ic_layer_stack_workspace_size": ([_QP, _DP], _sz),
     "ic_layer_stack": ([_i32, ctypes.POINTER(ic_layer), _P, _QP, _DP, _f32, _P, ctypes.POINTER(_i32), _P, _sz,
@@ -242,6 +248,62 @@ def gated_output(o, wv_b, gate, out=None, stream=None):
     _shape(out, (T, H, D_o), "out")
     _check(_lib.ic_gated_output(_ptr(o), _ptr(wv_b), _ptr(gate), T, H, D_v, D_o, _ptr(out), _stream(stream)))
     return out
+
+
+@dataclass
+class Tokens:
+    """New tokens of a cache write (see ic_tokens in include/ic.h)."""
+    row: torch.Tensor       # int64 [T] on device: cache row of token t
+    pos: torch.Tensor       # int32 [T] on device: position of token t
+    rows: int               # rows in the caches written
+    rope: Optional[torch.Tensor] = None   # fp32 [n_pos, D_rope]: cos at [p, i], sin at [p, D_rope/2 + i]
+    key_rope: bool = True   # the key's trailing D_rope entries rotate too
+
+    @property
+    def T(self) -> int:
+        return int(self.row.numel())
+
+    def c(self) -> ic_tokens:
+        _dev(self.row, torch.int64, "row")
+        _dev(self.pos, torch.int32, "pos")
+        if self.pos.numel() != self.T:
+            raise ValueError(f"pos has {self.pos.numel()} entries, row {self.T}")
+        rp = _dev(self.rope, torch.float32, "rope")
+        if rp is not None and rp.dim() != 2:
+            raise ValueError("rope must be [n_pos, D_rope]")
+        D_rope = int(rp.shape[1]) if rp is not None else 0
+        n_pos = int(rp.shape[0]) if rp is not None else 0
+        return ic_tokens(_ptr(self.row), _ptr(self.pos), self.T, D_rope, int(self.rows), _ptr(rp), n_pos,
+                         int(bool(self.key_rope)), 0)
+
+
+def write_cache(tk: Tokens, k_pre=None, ln_w=None, ln_b=None, eps: float = 1e-6, k_idx=None, kv_pre=None, kv=None,
+                stream=None):
+    """Store the new tokens' indexer keys (LayerNorm with bias, interleaved
+    RoPE, fp8 cast) into k_idx [rows, D_I] and their latent rows (interleaved
+    RoPE on the trailing D_rope entries) into kv [rows, D_qk]. Either part may
+    be left out (None)."""
+    T = tk.T
+    D_I = D_qk = 0
+    if k_pre is not None or k_idx is not None:
+        _bf16(k_pre, "k_pre")
+        D_I = int(k_pre.shape[-1])
+        _shape(k_pre, (T, D_I), "k_pre")
+        _dev(ln_w, torch.float32, "ln_w")
+        _dev(ln_b, torch.float32, "ln_b")
+        _shape(ln_w, (D_I,), "ln_w")
+        _shape(ln_b, (D_I,), "ln_b")
+        k_idx = _u8(k_idx, "k_idx")
+        _shape(k_idx, (int(tk.rows), D_I), "k_idx")
+    if kv_pre is not None or kv is not None:
+        _bf16(kv_pre, "kv_pre")
+        D_qk = int(kv_pre.shape[-1])
+        _shape(kv_pre, (T, D_qk), "kv_pre")
+        _bf16(kv, "kv")
+        _shape(kv, (int(tk.rows), D_qk), "kv")
+    c = tk.c()
+    _check(_lib.ic_write_cache(ctypes.byref(c), _ptr(k_pre), _ptr(ln_w), _ptr(ln_b), float(eps), D_I, _ptr(k_idx),
+                               _ptr(kv_pre), D_qk, _ptr(kv), _stream(stream)))
 
 
 def reuse_map_last_full(is_full: Sequence[bool]) -> List[int]:

@@ -34,6 +34,7 @@ import torch
 _TID_QI, _TID_W, _TID_KI, _TID_Q, _TID_KV, _TID_SINK = 1, 2, 3, 4, 5, 6
 _TID_LEN = 0
 _TID_GO, _TID_GW, _TID_GG = 7, 8, 9          # gated head output: o, wv_b, gate
+_TID_WK, _TID_WLW, _TID_WLB, _TID_WKV = 10, 11, 12, 13   # cache write: k_pre, ln_w, ln_b, kv_pre
 
 
 def sub_seed(seed: int, layer: int, tensor_id: int) -> int:
@@ -166,6 +167,63 @@ def gate_inputs(wl: Workload, layer: int, D_o: int = 128, device="cpu") -> GateI
     g = torch.randn((wl.T, wl.H, D_o), generator=_gen(device, sub_seed(s, layer, _TID_GG)), device=device,
                     dtype=torch.float32).mul_(2.0).to(torch.bfloat16)
     return GateInputs(o, w, g)
+
+
+def rope_table(n_pos: int, D_rope: int, base: float = 10000.0) -> torch.Tensor:
+    """fp32 [n_pos, D_rope] rotary table: cos(p * theta_i) at [p, i] and
+    sin(p * theta_i) at [p, D_rope/2 + i], theta_i = base^(-2i / D_rope); the
+    angles are formed in fp64 on the CPU, then rounded once to fp32."""
+    th = torch.pow(torch.tensor(base, dtype=torch.float64),
+                   -torch.arange(0, D_rope, 2, dtype=torch.float64) / D_rope)
+    out = torch.empty((n_pos, D_rope), dtype=torch.float32)
+    step = 1 << 16
+    for a in range(0, n_pos, step):
+        b = min(n_pos, a + step)
+        ang = torch.arange(a, b, dtype=torch.float64)[:, None] * th[None, :]
+        out[a:b, :D_rope // 2] = torch.cos(ang)
+        out[a:b, D_rope // 2:] = torch.sin(ang)
+    return out
+
+
+def d_rope(wl: Workload) -> int:
+    """RoPE entries of the latent row: 64 for the 576-wide row (512 + 64),
+    D_qk - D_v in general."""
+    return wl.D_qk - wl.D_v
+
+
+@dataclass
+class WriteInputs:
+    row: torch.Tensor        # int64 [T]: cache row of each new token
+    pos: torch.Tensor        # int32 [T]: its position
+    rope: torch.Tensor       # fp32 [n_pos, D_rope]
+    k_pre: torch.Tensor      # bf16 [T, D_I]: indexer key before its LayerNorm
+    ln_w: torch.Tensor       # fp32 [D_I]
+    ln_b: torch.Tensor       # fp32 [D_I]
+    kv_pre: torch.Tensor     # bf16 [T, D_qk]: latent row before its RoPE
+    eps: float = 1e-6
+
+
+def write_inputs(wl: Workload, layer: int, device="cpu", rope: Optional[torch.Tensor] = None) -> WriteInputs:
+    """The tokens each query of ``wl`` adds to the caches: query t's own token
+    sits at position n_t - 1, row base_t + n_t - 1 (the cache a query reads
+    already holds its token). k_pre ~ N(0, 4) bf16, LayerNorm weight
+    1 + N(0, 0.01), bias N(0, 0.01), kv_pre ~ N(0, 1) bf16. The rotary table
+    covers every position of the workload (pass ``rope`` to reuse one)."""
+    s = wl.seed
+    n = wl.n_valid().to(torch.int64)
+    pos = (n - 1).to(torch.int32)
+    row = wl.base() + n - 1
+    D_rope = d_rope(wl)
+    if rope is None:
+        rope = rope_table(max(1, int(n.max().item()) if n.numel() else 1), D_rope)
+    k_pre = torch.randn((wl.T, wl.D_I), generator=_gen(device, sub_seed(s, layer, _TID_WK)), device=device,
+                        dtype=torch.float32).mul_(2.0).to(torch.bfloat16)
+    ln_w = torch.randn((wl.D_I,), generator=_gen(device, sub_seed(s, layer, _TID_WLW)), device=device,
+                       dtype=torch.float32).mul_(0.1).add_(1.0)
+    ln_b = torch.randn((wl.D_I,), generator=_gen(device, sub_seed(s, layer, _TID_WLB)), device=device,
+                       dtype=torch.float32).mul_(0.1)
+    kv_pre = _randn_bf16((wl.T, wl.D_qk), _gen(device, sub_seed(s, layer, _TID_WKV)), device)
+    return WriteInputs(row.to(device), pos.to(device), rope.to(device), k_pre, ln_w, ln_b, kv_pre)
 
 
 def layer_inputs(wl: Workload, layer: int, device="cpu", with_indexer=True, variant: int = 0) -> LayerInputs:

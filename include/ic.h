@@ -151,6 +151,52 @@ ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries 
 ic_status ic_gated_output(const uint16_t *o, const uint16_t *wv_b, const uint16_t *gate, int32_t T, int32_t H,
                           int32_t D_v, int32_t D_o, uint16_t *out, void *stream);
 
+/* New tokens for ic_write_cache: where each is stored and the rotary table. */
+typedef struct {
+    const int64_t *row;      /* device [T]: cache row token t is written to;
+                                rows of one call must be distinct             */
+    const int32_t *pos;      /* device [T]: token t's position (a table row)  */
+    int32_t T;               /* number of tokens, >= 0                        */
+    int32_t D_rope;          /* entries per rotated span: even, 0..128; 0 = no
+                                rotation                                      */
+    int64_t rows;            /* host: rows in the caches that are written     */
+    const float *rope;       /* device [n_pos, D_rope] fp32: cos of pair i's
+                                angle at [p, i], its sin at [p, D_rope/2 + i] */
+    int64_t n_pos;           /* rows of the rotary table                      */
+    int32_t key_rope;        /* nonzero: the key's trailing D_rope entries
+                                rotate too                                    */
+    int32_t reserved;        /* must be 0                                     */
+} ic_tokens;
+
+/* Cache write, the step before the path ([G] "Indexer:" bullet: the indexer
+ * key passes through a LayerNorm with bias, eps being the model's RMS-norm
+ * eps; [G] RoPE bullet: the rotary embedding is interleaved, pairing entries
+ * 2i and 2i+1; [G] first paragraph: the latent row is 512 latent entries then
+ * 64 RoPE entries). For every token t with row r = row[t] and position
+ * p = pos[t]:
+ *   indexer key  y = (x - mean x) / sqrt(var x + eps) * ln_w + ln_b over the D_I
+ *                entries of x = k_pre[t] (var: mean squared deviation); if
+ *                key_rope, the trailing D_rope entries of y rotate at p; then
+ *                k_idx[r, :] = fp8 e4m3fn of y (nearest, ties to even,
+ *                saturating at +-448; no scale, as ic_indexer_score reads it);
+ *   latent row   kv[r, :D_qk - D_rope] = kv_pre[t, :D_qk - D_rope] (bit copy);
+ *                the trailing D_rope entries of kv_pre[t] rotate at p and are
+ *                rounded to bf16 (nearest even).
+ *   Rotation of pair i (entries 2i, 2i+1) with c = rope[p, i], s = rope[p, D_rope/2 + i]:
+ *                (a, b) -> (a c - b s, b c + a s).
+ *   k_pre [T, D_I] bf16, ln_w and ln_b [D_I] fp32, k_idx [rows, D_I] fp8
+ *   kv_pre [T, D_qk] bf16, kv [rows, D_qk] bf16
+ * Either part may be skipped: k_pre, ln_w, ln_b and k_idx all NULL (a shared
+ * layer, whose indexer never runs), or kv_pre and kv both NULL. Arithmetic in
+ * fp32. Built: D_I in {32, 64, 128}; D_qk a multiple of 8 up to 4096 with
+ * D_qk - D_rope a multiple of 8. A token whose row lies outside [0, rows) or
+ * whose position lies outside [0, n_pos) (when D_rope > 0) writes nothing;
+ * rows not named by row[] are never touched. T = 0 is a no-op (IC_OK) whatever
+ * the pointers. */
+ic_status ic_write_cache(const ic_tokens *tk, const uint16_t *k_pre, const float *ln_w, const float *ln_b,
+                         float eps, int32_t D_I, uint8_t *k_idx, const uint16_t *kv_pre, int32_t D_qk, uint16_t *kv,
+                         void *stream);
+
 /* One attention layer's tensors for ic_layer_stack. q_idx, w and k_idx are
  * read only on full layers and may be NULL on shared ones. */
 typedef struct {

@@ -28,7 +28,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(ic):
     names = declared_entry_points()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(ic._lib, n), n
     assert sorted(ic.EXPORTED) == names
@@ -218,3 +218,37 @@ def test_gated_output_validation(ic):
     assert f(None, FAKE, FAKE, 1, 128, 512, 128, FAKE, None) == ic.IC_ERR_NULL
     assert f(FAKE, FAKE + 4, FAKE, 1, 128, 512, 128, FAKE, None) == ic.IC_ERR_ALIGN
     assert f(None, None, None, 0, 128, 512, 128, None, None) == ic.IC_OK          # nothing to do
+
+
+def test_write_cache_validation(ic):
+    f = ic._lib.ic_write_cache
+
+    def tk(T=4, D_rope=64, rows=100, rope=FAKE, n_pos=10, key_rope=1, reserved=0, row=FAKE, pos=FAKE):
+        return ctypes.byref(ic.ic_tokens(row, pos, T, D_rope, rows, rope, n_pos, key_rope, reserved))
+
+    key = (FAKE, FAKE, FAKE, 1e-6, 128, FAKE)
+    lat = (FAKE, 576, FAKE)
+    assert f(None, *key, *lat, None) == ic.IC_ERR_NULL
+    assert f(tk(T=0, row=None, pos=None), None, None, None, 1e-6, 128, None, None, 576, None, None) == ic.IC_OK
+    assert f(tk(T=-1), *key, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(rows=0), *key, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(reserved=1), *key, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(D_rope=63), *key, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(D_rope=130), *key, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(), None, None, None, 1e-6, 128, None, None, 576, None, None) == ic.IC_ERR_NULL  # nothing
+    assert f(tk(), FAKE, None, FAKE, 1e-6, 128, FAKE, *lat, None) == ic.IC_ERR_NULL             # ln_w missing
+    assert f(tk(), *key, FAKE, 576, None, None) == ic.IC_ERR_NULL                              # kv missing
+    assert f(tk(), FAKE, FAKE, FAKE, 1e-6, 96, FAKE, *lat, None) == ic.IC_ERR_UNSUPPORTED
+    assert f(tk(), FAKE, FAKE, FAKE, 0.0, 128, FAKE, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(), FAKE, FAKE, FAKE, float("nan"), 128, FAKE, *lat, None) == ic.IC_ERR_SHAPE
+    assert f(tk(D_rope=64), FAKE, FAKE, FAKE, 1e-6, 32, FAKE, None, 0, None, None) == ic.IC_ERR_SHAPE
+    assert f(tk(), *key, FAKE, 572, FAKE, None) == ic.IC_ERR_UNSUPPORTED
+    assert f(tk(D_rope=60), *key, FAKE, 576, FAKE, None) == ic.IC_ERR_UNSUPPORTED             # 516 not % 8
+    assert f(tk(rope=None), *key, *lat, None) == ic.IC_ERR_NULL
+    assert f(tk(n_pos=0), *key, *lat, None) == ic.IC_ERR_NULL
+    assert f(tk(row=None), *key, *lat, None) == ic.IC_ERR_NULL
+    assert f(tk(row=FAKE + 8), *key, *lat, None) == ic.IC_ERR_ALIGN
+    assert f(tk(), FAKE, FAKE, FAKE, 1e-6, 128, FAKE, FAKE + 2, 576, FAKE, None) == ic.IC_ERR_ALIGN
+    assert f(tk(T=0, row=None, pos=None), *key, *lat, None) == ic.IC_OK                        # nothing to do
+    # a key without rotation reads no table
+    assert f(tk(T=3, rope=None, n_pos=0, key_rope=0, row=FAKE + 1), *key, None, 0, None, None) == ic.IC_ERR_ALIGN
