@@ -115,6 +115,16 @@ def reuse_overlap(ic, W, wl, st, rmap, qs, d, dev):
     return {"mean": sum(fr) / len(fr), "shared_layers": len(fr), "expected_independent": wl.k / n}
 
 
+def shared_stacks(ic, sets, rmap, qs, d, scale, dev):
+    """The sets' layers under another reuse map, sharing one workspace (the
+    sets') and one index cache, as the sets themselves do."""
+    out = []
+    for s in sets:
+        out.append(ic.LayerStack(s.layers, rmap, qs, d, scale, device=dev, ws=sets[0].ws,
+                                 index_cache=out[0].index_cache if out else None))
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,7 +193,11 @@ def main():
                 li = W.layer_inputs(wl, l, device=dev, with_indexer=full or wl.name == "stack_78", variant=i)
             out = torch.empty((wl.T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
             lays.append(dict(q_idx=li.q_idx, w=li.w, k_idx=li.k_idx, q=li.q, kv=li.kv, sink=li.sink, out=out))
-        sets.append(ic.LayerStack(lays, rmap, qs, d, wl.scale, device=dev))
+        # one workspace and index cache for every set: steps never overlap,
+        # and a decode loop reuses its scratch each step (only inputs rotate)
+        sets.append(ic.LayerStack(lays, rmap, qs, d, wl.scale, device=dev,
+                                  ws=sets[0].ws if sets else None,
+                                  index_cache=sets[0].index_cache if sets else None))
     torch.cuda.synchronize()
 
     def capture(fns):
@@ -253,7 +267,7 @@ def main():
         result.update(value=wl.T * wl.n_layers * steps / el, ms_per_step=el * 1e3 / steps)
         if wl.name == "stack_78":
             ident = list(range(wl.n_layers))
-            allfull = [ic.LayerStack(s.layers, ident, qs, d, wl.scale, device=dev) for s in sets]
+            allfull = shared_stacks(ic, sets, ident, qs, d, wl.scale, dev)
             el2, _ = timed(runner(allfull), steps, warm)
             result["all_full"] = {"value": wl.T * wl.n_layers * steps / el2, "ms_per_step": el2 * 1e3 / steps,
                                   "indexer_passes": wl.n_layers}
@@ -263,7 +277,7 @@ def main():
             pats = {}
             for name, fl in W.REUSE_PATTERNS.items():
                 m = ic.reuse_map_last_full([l in set(fl) for l in range(wl.n_layers)])
-                st = [ic.LayerStack(s.layers, m, qs, d, wl.scale, device=dev) for s in sets]
+                st = shared_stacks(ic, sets, m, qs, d, wl.scale, dev)
                 elp, _ = timed(runner(st), steps, warm)
                 pats[name] = {"indexer_passes": len(fl), "ms_per_step": elp * 1e3 / steps,
                               "value": wl.T * wl.n_layers * steps / elp, "speedup_vs_all_full": el2 / elp}

@@ -19,16 +19,18 @@
 // take part in the later digits:
 //   * split path (few queries, long rows): P workgroups per query each copy
 //     their chunk's survivors, in position order, into their own slice of the
-//     workspace (topk_survivors_kernel); one workgroup per query then gathers
-//     them in order into LDS and finishes the selection there
-//     (topk_finish_kernel). The kernel boundary orders the two phases.
+//     workspace and add the second digit's histogram of the threshold bin
+//     (topk_survivors_kernel); one workgroup per query then reads the second
+//     digit, gathers in order into LDS only the survivors at or above the
+//     two-digit bound, and finishes the selection there (topk_finish_kernel).
+//     The kernel boundary orders the two phases.
 //   * row path (many queries): one workgroup per query streams its row once
-//     more to collect survivors into LDS and finishes there.
-// When the survivors exceed the LDS list (the threshold fell into a dense
-// first-digit bin), the finishing workgroup histograms the second digit over
-// the survivors kept in global memory and keeps only those at or above the
-// second-digit threshold, which fit; only ties spanning more than the list at
-// 21 bits of the key fall back to digit passes over the full row.
+//     more to collect survivors into LDS and finishes there. When they exceed
+//     the LDS list (the threshold fell into a dense first-digit bin), it
+//     histograms the second digit over the survivors kept in global memory and
+//     keeps only those at or above the second-digit threshold.
+// Only ties spanning more than the list at 21 bits of the key fall back to
+// digit passes over the full row.
 // The first-digit histogram is kept in kHistCopies copies per query (adders
 // pick a copy by workgroup index, which spreads atomic traffic); the workspace
 // holds them zeroed on entry and the finishing workgroup zeroes them again.
@@ -46,7 +48,7 @@ constexpr int kFinishThreads = 1024;
 constexpr int kListCap = 18432;         // survivors held in LDS (split path)
 constexpr int kRowListCap = 8192;       // survivors held in LDS (row path: two workgroups per CU)
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
-static_assert(kListCap % kFinishThreads == 0, "whole runs of list entries per finishing thread");
+constexpr int kGatherPer = 20;          // survivors per finishing thread and gather round
 constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
 
 // Block-wide inclusive scan of one uint32 per thread.
@@ -170,45 +172,6 @@ struct GListSrc {
         for (int e = 0; e < 4; ++e) {
             ok[e] = i + e < n;
             const uint64_t v = ok[e] ? list[i + e] : 0ull;
-            key[e] = (uint32_t)(v >> 32);
-            pos[e] = (int64_t)(uint32_t)v;
-        }
-    }
-};
-
-// The survivor slices of the split path read as one list: element i lives in
-// the last slice whose starting offset (offs, in LDS) is <= i.
-struct SliceSrc {
-    const uint64_t *regions;   // this query's P slices of `chunk` entries
-    const uint32_t *offs;      // [P + 1] exclusive offsets
-    int P;
-    int chunk;
-    int64_t n;
-    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
-    {
-        // one binary search for the first element, then walk forward
-        int lo = 0;
-        if (i < n) {
-            int hi = P;
-            const uint32_t x = (uint32_t)i;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (offs[mid] <= x)
-                    lo = mid;
-                else
-                    hi = mid;
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t x = (uint32_t)(i + e);
-            ok[e] = i + e < n;
-            uint64_t v = 0;
-            if (ok[e]) {
-                while (lo + 1 < P && offs[lo + 1] <= x)
-                    ++lo;
-                v = regions[(int64_t)lo * chunk + (x - offs[lo])];
-            }
             key[e] = (uint32_t)(v >> 32);
             pos[e] = (int64_t)(uint32_t)v;
         }
@@ -517,10 +480,9 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
 }
 
 // Phase 2. grid: T; block: kFinishThreads. The second digit comes from hist1;
-// the survivors of all P slices are gathered in slice order (= position
-// order) into LDS, compacted in place to the keys at or above the two-digit
-// bound (about k of them), and the last digit finishes the selection. Zeroes
-// the query's histograms.
+// the survivors of all P slices at or above the two-digit bound (about k of
+// them) are gathered in slice order (= position order) into LDS, and the last
+// digit finishes the selection. Zeroes the query's histograms.
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
     int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, uint32_t *__restrict__ hist1,
@@ -531,6 +493,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     __shared__ Shared sh;
     __shared__ uint64_t list[kListCap];
     __shared__ uint32_t offs[kMaxSplit + 1];
+    __shared__ uint32_t wave_cnt[kFinishThreads / 64];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t nt = n[t];
@@ -567,32 +530,42 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     if (tid == 0)
         offs[P] = total;
     __syncthreads();
-    const SliceSrc slices{regions + (int64_t)t * P * kSplitChunk, offs, P, kSplitChunk, total};
-    if (total <= (uint32_t)kListCap) {
-        // each thread moves a run of consecutive entries: one search for the
-        // slice of its first entry, then a forward walk with the next slice's
-        // offset in a register; every load is in flight before any store
-        constexpr int kPer = kListCap / NT;
-        const uint32_t per = (total + NT - 1) / NT;
-        const uint32_t i0 = (uint32_t)tid * per;
+    // Gather, in slice order (= position order), only the survivors at or
+    // above the two-digit bound: about k of them, plus the ties of the bound's
+    // bin. Per round each wave takes a contiguous segment, its lanes
+    // interleaved so that one load covers 512 contiguous bytes of a slice; a
+    // lane finds the slice of its first entry by binary search, then walks
+    // forward with the next slice's offset in a register. All loads of a round
+    // are in flight before the compaction: ballot prefix counts inside the
+    // wave, then one exchange of the 16 wave counts.
+    constexpr int NW = NT / 64;
+    const int wv = tid >> 6, lane = tid & 63;
+    const uint64_t *reg_t = regions + (int64_t)t * P * kSplitChunk;
+    uint32_t cnt = 0;
+    for (uint32_t r0 = 0; r0 < total; r0 += (uint32_t)NT * kGatherPer) {
+        const uint32_t part = min(total - r0, (uint32_t)NT * kGatherPer);
+        const uint32_t seg = (part + NW - 1) / NW;            // <= 64 * kGatherPer
+        const uint32_t s0 = r0 + (uint32_t)wv * seg;
+        const uint32_t s1 = min(s0 + seg, r0 + part);
+        const uint32_t x0 = s0 + (uint32_t)lane;
         int lo = 0;
-        if (i0 < total) {
+        if (x0 < s1) {
             int hi = P;
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
-                if (offs[mid] <= i0)
+                if (offs[mid] <= x0)
                     lo = mid;
                 else
                     hi = mid;
             }
         }
         uint32_t next = offs[lo + 1];
-        const uint64_t *reg_t = regions + (int64_t)t * P * kSplitChunk;
-        uint64_t v[kPer];
+        uint64_t v[kGatherPer];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const uint32_t x = i0 + e;
-            if (e < (int)per && x < total) {
+        for (int e = 0; e < kGatherPer; ++e) {
+            const uint32_t x = x0 + 64u * e;
+            v[e] = 0;
+            if (x < s1) {
                 while (next <= x) {               // offs[P] = total > x ends the walk
                     ++lo;
                     next = offs[lo + 1];
@@ -600,24 +573,39 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
                 v[e] = reg_t[(int64_t)lo * kSplitChunk + (x - offs[lo])];
             }
         }
+        uint32_t loc[kGatherPer];
+        bool keep[kGatherPer];
+        uint32_t wcount = 0;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const uint32_t x = i0 + e;
-            if (e < (int)per && x < total)
-                list[x] = v[e];
+        for (int e = 0; e < kGatherPer; ++e) {
+            keep[e] = x0 + 64u * e < s1 && (uint32_t)(v[e] >> 32) >= bound;
+            const uint64_t m = __ballot(keep[e]);
+            loc[e] = wcount + (uint32_t)__popcll(m & __lanemask_lt());
+            wcount += (uint32_t)__popcll(m);
         }
+        if (lane == 0)
+            wave_cnt[wv] = wcount;
         __syncthreads();
-        // in place: a chunk's entries are all read before any of its slots is written
-        const uint32_t cnt = collect<NT>(ListSrc{list, total}, bound, sh, list, (uint32_t)kListCap, nullptr, 0);
-        finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
-    } else {
-        const uint32_t cnt = collect<NT>(slices, bound, sh, list, (uint32_t)kListCap, nullptr, 0);
-        if (cnt <= (uint32_t)kListCap)
-            finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
-        else
-            finish_select<NT>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k,
-                              out);
+        uint32_t woff = 0, tot = 0;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const uint32_t c = wave_cnt[j];
+            woff += j < wv ? c : 0u;
+            tot += c;
+        }
+#pragma unroll
+        for (int e = 0; e < kGatherPer; ++e) {
+            const uint32_t o = cnt + woff + loc[e];
+            if (keep[e] && o < (uint32_t)kListCap)
+                list[o] = v[e];
+        }
+        cnt += tot;
+        __syncthreads();                          // wave_cnt is rewritten next round
     }
+    if (cnt <= (uint32_t)kListCap)
+        finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
+    else                                          // more than kListCap keys share the top two digits
+        finish_select<NT>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
 }
 
 // ---- row path ---------------------------------------------------------------

@@ -318,7 +318,11 @@ class LayerStack:
     """Holds the host-side descriptors of a layer stack so repeated calls (and
     HIP-graph capture) marshal nothing."""
 
-    def __init__(self, layers, reuse_map: Sequence[int], qs: Queries, d: ic_dims, scale: float, device="cuda"):
+    def __init__(self, layers, reuse_map: Sequence[int], qs: Queries, d: ic_dims, scale: float, device="cuda",
+                 ws: Optional[torch.Tensor] = None, index_cache: Optional[torch.Tensor] = None):
+        """``ws`` and ``index_cache`` may be shared between stacks whose calls
+        never overlap (one decode loop reuses them every step); otherwise they
+        are allocated here (the workspace zero-filled, as the library asks)."""
         self.n = len(layers)
         self.layers = layers
         self.qs = qs
@@ -339,9 +343,18 @@ class LayerStack:
                               _ptr(y["out"]))
         self.arr = arr
         self.n_full = sum(1 for l in range(self.n) if reuse_map[l] == l)
-        self.index_cache = torch.empty((max(self.n_full, 1), qs.T, d.k), dtype=torch.int32, device=device)
+        shape = (max(self.n_full, 1), qs.T, d.k)
+        if index_cache is None:
+            index_cache = torch.empty(shape, dtype=torch.int32, device=device)
+        _dev(index_cache, torch.int32, "index_cache")
+        _shape(index_cache, shape, "index_cache")
+        self.index_cache = index_cache
         need = _lib.ic_layer_stack_workspace_size(ctypes.byref(self.qc), ctypes.byref(self.d))
-        self.ws = workspace(need, device)
+        if ws is None:
+            ws = workspace(need, device)
+        if ws.dtype != torch.uint8 or ws.numel() < need:
+            raise ValueError(f"workspace: need {need} bytes of uint8, got {ws.numel()} of {ws.dtype}")
+        self.ws = ws
         self.passes = _i32(-1)
 
     def __call__(self, stream=None) -> int:
