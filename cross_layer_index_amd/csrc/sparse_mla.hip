@@ -7,10 +7,12 @@
 //   s_j = scale * <q[t,h,:], kv[row_j,:]>,  o = sum_j e^{s_j} v_j / (e^{sink_h} + sum_j e^{s_j})
 // with v_j the leading D_v entries of the same row (absorbed-MLA form).
 //
-// Work split: a workgroup (4 waves) owns 64 heads of one query and a range of
-// the index list; each wave owns 16 heads. Selected rows are gathered 32 at a
-// time straight from HBM into a row-major LDS tile by global_load_lds_dwordx4
-// (no registers, no VALU; two tiles, one filling while the other is used).
+// Work split: a workgroup (8 waves) owns 64 heads of one query and a range of
+// the index list; a wave owns 16 heads and one half of the dims (the partner
+// wave with the other half adds its partial scores through LDS). Selected rows
+// are gathered 32 at a time straight from HBM into a row-major LDS tile by
+// global_load_lds_dwordx4 (no registers, no VALU; a ring of three tiles, the
+// next ones filling while one is used).
 // Both products run on v_mfma_f32_16x16x32_bf16:
 //   S^T[j,h] = sum_d K[j,d] Q[h,d]      (A = gathered rows, B = q in registers)
 //   O[h,v]  += sum_j P[h,j] V[j,v]      (A = P straight from the S^T
