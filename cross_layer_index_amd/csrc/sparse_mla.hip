@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t tile0[TG::ELEMS];
     __shared__ __attribute__((aligned(16))) uint16_t tile1[TG::ELEMS];
     __shared__ __attribute__((aligned(16))) uint16_t tile2[TG::ELEMS];
-    __shared__ __attribute__((aligned(16))) f4 sx[kWaves][2][64];   // partial S^T per wave
+    __shared__ __attribute__((aligned(16))) f4 sx[2][kWaves][2][64];   // partial S^T per wave, by tile parity
     __shared__ __attribute__((aligned(16))) int32_t rowid[kMaxRowsPerSplit + kTile];
 
     // Workgroups are dispatched round-robin over the 8 XCDs (linear id mod 8).
@@ -302,14 +302,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const int rb8 = 8 * (g >> 1);
     const bool odd = g & 1;
 
-    auto compute = [&](const uint16_t *K, int j0) {
-        // partial S^T over this half's K-steps; fragments of step i+1 are read
-        // while step i multiplies
+    // partial S^T of one tile over this half's K-steps; fragments are read in
+    // batches of kQkBatch steps ahead of their MFMAs
+    auto qk = [&](const uint16_t *K, f4 &st0, f4 &st1) {
         // both halves have KSH steps when KS is even (the 576-wide rows); an
         // odd KS leaves the second half one step short
         const int nks = (G::KS % 2 == 0) ? KSH : min(KSH, G::KS - ks0);
-        f4 st[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-        // fragments are read in batches of kQkBatch steps ahead of their MFMAs
+        st0 = f4{0.f, 0.f, 0.f, 0.f};
+        st1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i0 = 0; i0 < KSH; i0 += kQkBatch) {
             uint4 fa[kQkBatch][2];
@@ -323,14 +323,17 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 #pragma unroll
             for (int i = 0; i < kQkBatch; ++i) {
                 if (i0 + i < nks) {
-                    st[0] = mfma_bf16_16x16x32(as_bf16x8(fa[i][0]), qf[i0 + i], st[0]);
-                    st[1] = mfma_bf16_16x16x32(as_bf16x8(fa[i][1]), qf[i0 + i], st[1]);
+                    st0 = mfma_bf16_16x16x32(as_bf16x8(fa[i][0]), qf[i0 + i], st0);
+                    st1 = mfma_bf16_16x16x32(as_bf16x8(fa[i][1]), qf[i0 + i], st1);
                 }
             }
         }
+    };
+
+    // softmax of one tile (this wave's half of the scores plus the partner
+    // wave's, exchanged through sx[par]) and its PV product
+    auto softmax_pv = [&](const uint16_t *K, int j0, const f4 st0, const f4 st1, int par) {
         // add the partner wave's half of the dims
-        sx[wave][0][lane] = st[0];
-        sx[wave][1][lane] = st[1];
         const int *rp = &rowid[j0 + rb8 + odd];
         int va[4], vbv[4];
 #pragma unroll
@@ -338,17 +341,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             va[r] = rp[2 * r];
             vbv[r] = rp[16 + 2 * r];
         }
-        lds_barrier();
-        const f4 o0 = sx[wave ^ 4][0][lane];
-        const f4 o1 = sx[wave ^ 4][1][lane];
+        const f4 o0 = sx[par][wave ^ 4][0][lane];
+        const f4 o1 = sx[par][wave ^ 4][1][lane];
         float s[8];
         float mt = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             // a two-term fp32 sum is commutative, so both waves of the pair
             // get identical scores
-            const float t0 = st[0][r] + o0[r];
-            const float t1 = st[1][r] + o1[r];
+            const float t0 = st0[r] + o0[r];
+            const float t1 = st1[r] + o1[r];
             s[r] = va[r] >= 0 ? t0 * scale_log2 : -INFINITY;
             s[4 + r] = vbv[r] >= 0 ? t1 * scale_log2 : -INFINITY;
             mt = fmaxf(mt, fmaxf(s[r], s[4 + r]));
@@ -412,35 +414,57 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         }
     };
 
-    // ring of three tiles: tile i lives in buffer i % 3; tile i+1 is in
-    // flight while tile i is computed. The ring is unrolled by three so that
-    // every access names its buffer.
+    // Ring of three tiles, tile i in buffer i % 3, software-pipelined by one
+    // tile: step i finishes tile i (softmax and PV over the scores exchanged
+    // at the end of the previous step), then computes the partial scores of
+    // tile i+1 and writes them to sx for the partner wave; tile i+2 fills
+    // meanwhile into the buffer tile i-1 left. One barrier per step orders it
+    // all: the next tile's partial scores are in sx, its successor's fills
+    // have landed, and the oldest buffer is free. The only LDS writes come at
+    // the end of a step, so the fills in flight never wait behind them. The
+    // ring is unrolled by three so that every access names its buffer.
     const int ntiles = has_rows ? padded / kTile : 0;
-    if (ntiles > 0)
-        issue(tile0, 0);
-    if (ntiles > 1)
-        issue(tile1, kTile);
     // fill loads a wave issues per tile (the smallest count over the waves)
     constexpr int kPerWave = TG::INSTR / kWaves;
-    auto step = [&](int i, const uint16_t *cur, uint16_t *ahead) {
-        // wait for tile i's fills; the fills of tile i+1 may stay in flight
-        if (i + 1 < ntiles)
-            wait_vmcnt<kPerWave>();
-        else
+    f4 sc0, sc1;                                  // partial scores of the tile to finish
+    if (ntiles > 0) {
+        issue(tile0, 0);
+        if (ntiles > 1) {
+            issue(tile1, kTile);
+            wait_vmcnt<kPerWave>();               // tile 0's fills; tile 1's may stay in flight
+        } else {
             wait_vmcnt<0>();
-        // every wave's fills of tile i are in LDS (each wave waited for its
-        // own above), and `ahead` (tile i-1) is no longer read
+        }
         lds_barrier();
+        qk(tile0, sc0, sc1);
+        sx[0][wave][0][lane] = sc0;
+        sx[0][wave][1][lane] = sc1;
+        wait_vmcnt<0>();                          // tile 1's fills
+        lds_barrier();
+    }
+    auto step = [&](int i, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead) {
         if (i + 2 < ntiles)
             issue(ahead, (i + 2) * kTile);
-        compute(cur, i * kTile);
+        softmax_pv(cur, i * kTile, sc0, sc1, i & 1);
+        qk(nxt, sc0, sc1);
+        sx[(i + 1) & 1][wave][0][lane] = sc0;
+        sx[(i + 1) & 1][wave][1][lane] = sc1;
+        wait_vmcnt<0>();                          // tile i+2's fills
+        lds_barrier();
     };
-    for (int i = 0; i < ntiles; i += 3) {
-        step(i, tile0, tile2);
-        if (i + 1 < ntiles)
-            step(i + 1, tile1, tile0);
+    // (a for loop with guarded steps: a loop with early exits here made the
+    // register allocator spill)
+    for (int i = 0; i + 1 < ntiles; i += 3) {
+        step(i, tile0, tile1, tile2);
         if (i + 2 < ntiles)
-            step(i + 2, tile2, tile1);
+            step(i + 1, tile1, tile2, tile0);
+        if (i + 3 < ntiles)
+            step(i + 2, tile2, tile0, tile1);
+    }
+    if (ntiles > 0) {                             // the last tile has no successor
+        const int last = ntiles - 1;
+        const int b = last % 3;
+        softmax_pv(b == 0 ? tile0 : (b == 1 ? tile1 : tile2), last * kTile, sc0, sc1, last & 1);
     }
 
     if (splits == 1) {
