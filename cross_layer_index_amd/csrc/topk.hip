@@ -47,6 +47,7 @@ constexpr int kRowThreads = 1024;
 constexpr int kFinishThreads = 1024;
 constexpr int kListCap = 18432;         // survivors held in LDS (split path)
 constexpr int kRowListCap = 8192;       // survivors held in LDS (row path: two workgroups per CU)
+constexpr int kRowRuns = 2;             // consecutive groups of 4 scores per thread per collect round
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
 constexpr int kGatherPer = 20;          // survivors per finishing thread and gather round
 constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
@@ -180,35 +181,44 @@ struct GListSrc {
 
 // Ordered compaction of the entries with key >= bound into an LDS list (the
 // first lcap) and, if given, a global list (the first gcap). Returns the count.
-template <int NT, class Src>
+// A thread takes R groups of 4 consecutive entries per round (all their loads
+// in flight before the round's one scan).
+template <int NT, int R = 1, class Src>
 __device__ uint32_t collect(const Src &src, uint32_t bound, Shared &sh, uint64_t *lds, uint32_t lcap,
                             uint64_t *glist, uint32_t gcap)
 {
     uint32_t total = 0;
-    for (int64_t c0 = 0; c0 < src.n; c0 += (int64_t)NT * 4) {
-        uint32_t key[4];
-        int64_t pos[4];
-        bool ok[4];
-        src.get4(c0 + (int64_t)threadIdx.x * 4, key, pos, ok);
-        uint32_t sv[4], ls = 0;
+    for (int64_t c0 = 0; c0 < src.n; c0 += (int64_t)NT * 4 * R) {
+        uint32_t key[R][4];
+        int64_t pos[R][4];
+        bool ok[R][4];
+        const int64_t i0 = c0 + (int64_t)threadIdx.x * 4 * R;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = ok[e] && key[e] >= bound;
-            ls += sv[e];
-        }
+        for (int r = 0; r < R; ++r)
+            src.get4(i0 + 4 * r, key[r], pos[r], ok[r]);
+        uint32_t ls = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ok[r][e] = ok[r][e] && key[r][e] >= bound;
+                ls += ok[r][e];
+            }
         uint32_t tot;
         uint32_t o = total + block_scan<NT>(ls, sh.waves, &tot) - ls;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (sv[e]) {
-                const uint64_t v = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
-                if (o < lcap)
-                    lds[o] = v;
-                if (glist && o < gcap)
-                    glist[o] = v;
-                ++o;
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (ok[r][e]) {
+                    const uint64_t v = ((uint64_t)key[r][e] << 32) | (uint32_t)pos[r][e];
+                    if (o < lcap)
+                        lds[o] = v;
+                    if (glist && o < gcap)
+                        glist[o] = v;
+                    ++o;
+                }
             }
-        }
         total += tot;
     }
     __syncthreads();
@@ -646,9 +656,25 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
             bool ok[4];
             src.get4(i, key, pos, ok);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (ok[e])
-                    atomicAdd(&sh.hist[key[e] >> 21], 1u);
+            for (int e = 0; e < 4; ++e) {
+                // scores crowd into a few first-digit bins, so the lanes of one
+                // LDS atomic mostly hit the same address and serialise: the
+                // wave first adds the first pending lane's bin with one atomic
+                // for all lanes that share it, then the rest one by one
+                const uint32_t b = key[e] >> 21;
+                const uint64_t pm = __ballot(ok[e]);
+                bool rest = ok[e];
+                if (pm) {
+                    const uint32_t lead = __builtin_amdgcn_readlane(b, __builtin_ctzll(pm));
+                    const bool same = ok[e] && b == lead;
+                    const uint64_t m = __ballot(same);
+                    if (same && (m & __lanemask_lt()) == 0)
+                        atomicAdd(&sh.hist[lead], (uint32_t)__popcll(m));
+                    rest = ok[e] && !same;
+                }
+                if (rest)
+                    atomicAdd(&sh.hist[b], 1u);
+            }
         }
         __syncthreads();
     }
@@ -657,8 +683,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
     const uint32_t need = (uint32_t)k - above0;
     // survivors in position order: into LDS, and into this query's global list
     uint64_t *gl = surv + (int64_t)t * kRowSurvCap;
-    const uint32_t total = collect<kRowThreads>(src, d0 << 21, sh, list, (uint32_t)kRowListCap, gl,
-                                                (uint32_t)kRowSurvCap);
+    const uint32_t total = collect<kRowThreads, kRowRuns>(src, d0 << 21, sh, list, (uint32_t)kRowListCap, gl,
+                                                           (uint32_t)kRowSurvCap);
     if (total <= (uint32_t)kRowListCap)
         finish_select<kRowThreads>(ListSrc{list, total}, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
     else if (total <= (uint32_t)kRowSurvCap)
