@@ -656,25 +656,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
             bool ok[4];
             src.get4(i, key, pos, ok);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // scores crowd into a few first-digit bins, so the lanes of one
-                // LDS atomic mostly hit the same address and serialise: the
-                // wave first adds the first pending lane's bin with one atomic
-                // for all lanes that share it, then the rest one by one
-                const uint32_t b = key[e] >> 21;
-                const uint64_t pm = __ballot(ok[e]);
-                bool rest = ok[e];
-                if (pm) {
-                    const uint32_t lead = __builtin_amdgcn_readlane(b, __builtin_ctzll(pm));
-                    const bool same = ok[e] && b == lead;
-                    const uint64_t m = __ballot(same);
-                    if (same && (m & __lanemask_lt()) == 0)
-                        atomicAdd(&sh.hist[lead], (uint32_t)__popcll(m));
-                    rest = ok[e] && !same;
-                }
-                if (rest)
-                    atomicAdd(&sh.hist[b], 1u);
-            }
+            for (int e = 0; e < 4; ++e)
+                hist_add_wave(sh.hist, key[e] >> 21, ok[e]);
         }
         __syncthreads();
     }
