@@ -8,14 +8,20 @@
 // head's value up-projection wv_b; folding wv_b into o_proj would gate in the
 // wrong space.)
 //
-// A workgroup owns one head, a run of 16-query blocks and 64 output columns;
-// each of its 4 waves one 16-column tile. v_mfma_f32_16x16x32_bf16 with queries on M and
-// output columns on N: A lane l holds o[t0 + l%16][h][32*ks + 8*(l/16) .. +8],
-// B lane l holds wv_b[h][e + l%16][32*ks + 8*(l/16) .. +8] -- both contiguous
-// 16-byte loads, since the contraction runs along the rows of o and wv_b.
-// Accumulator element r of lane l is (query 4*(l/16) + r, column l%16).
-// Workgroups of one head share its wv_b rows through one L2: the grid's x
-// extent is a multiple of 8, so a head's workgroups stay on one XCD.
+// A workgroup (8 waves) owns one head, a run of 16-query blocks and up to
+// 128 output columns, each wave one 16-column tile. v_mfma_f32_16x16x32_bf16
+// with queries on M and output columns on N: A lane l holds
+// o[t0 + l%16][h][32*ks + 8*(l/16) .. +8], B lane l holds
+// wv_b[h][e + l%16][32*ks + 8*(l/16) .. +8] (the contraction runs along the
+// rows of o and wv_b). Accumulator element r of lane l is (query
+// 4*(l/16) + r, column l%16). A wave keeps its wv_b fragments in registers
+// for the whole run; each 16-query block of o is read from memory once per
+// workgroup, staged through registers into a padded LDS tile (double
+// buffered: the next block's loads are in flight while the current one
+// multiplies) and read from there by all eight waves. The gate values of a
+// block are loaded with its o. Workgroups of one head share its wv_b rows
+// through one L2: the grid's x extent is a multiple of 8 when H is, so a
+// head's workgroups stay on one XCD.
 #include "kernels.h"
 
 namespace ic {
@@ -24,9 +30,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGateThreads = 256;
-constexpr int kGateRows = 16;          // queries per workgroup
-constexpr int kGateCols = 64;          // output columns per workgroup
+constexpr int kGateRows = 16;          // queries per block
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b)
 {
@@ -40,81 +44,134 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
-// grid: (H * D_o / 64, query chunks); a workgroup takes `blocks` consecutive
-// 16-query blocks of one head and 64 columns. Each wave keeps its wv_b
-// fragments (16 columns x D_v) in registers for the whole chunk and loads the
-// next block's o fragments while the current block multiplies.
-template <int DV>
-__global__ __launch_bounds__(kGateThreads) void gated_output_kernel(const uint16_t *__restrict__ o,
-                                                                    const uint16_t *__restrict__ wv_b,
-                                                                    const uint16_t *__restrict__ gate, int32_t T,
-                                                                    int32_t H, int32_t D_o, int32_t blocks,
-                                                                    uint16_t *__restrict__ out)
+template <int DV, int NT>
+struct GateGeom {
+    static constexpr int KS = DV / 32;                         // K-steps of 32
+    static constexpr int ROWB = DV * 2 + 16;                   // LDS bytes per o row (16 of padding)
+    static constexpr int CH = DV * 2 / 16;                     // 16-byte chunks per o row
+    static constexpr int CHUNKS = kGateRows * CH;              // per block
+    static constexpr int PER = (CHUNKS + NT - 1) / NT;         // chunks per thread
+    static constexpr int COLS = NT / 64 * 16;                  // columns per workgroup
+};
+
+// grid: (H * ceil(D_o / COLS), query chunks); NT threads (NT/64 waves, one
+// 16-column tile each); a workgroup takes `blocks` consecutive 16-query
+// blocks of one head; waves whose tile lies past D_o only help stage o.
+template <int DV, int NT>
+__global__ __launch_bounds__(NT) void gated_output_kernel(const uint16_t *__restrict__ o,
+                                                          const uint16_t *__restrict__ wv_b,
+                                                          const uint16_t *__restrict__ gate, int32_t T, int32_t H,
+                                                          int32_t D_o, int32_t blocks, uint16_t *__restrict__ out)
 {
-    constexpr int KS = DV / 32;
-    const int colblocks = D_o / kGateCols;
-    const int h = blockIdx.x / colblocks;
-    const int e0 = (blockIdx.x % colblocks) * kGateCols + (threadIdx.x >> 6) * 16;
+    using GG = GateGeom<DV, NT>;
+    constexpr int wcols = GG::COLS;
+    __shared__ __attribute__((aligned(16))) unsigned char ob0[kGateRows * GG::ROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char ob1[kGateRows * GG::ROWB];
+    const int groups = (D_o + wcols - 1) / wcols;
+    const int h = blockIdx.x / groups;
+    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int e0 = (blockIdx.x % groups) * wcols + wave * 16;
+    const bool active = e0 < D_o;                 // D_o is a multiple of 16: whole tiles
     const int c = lane & 15;
     const int g = lane >> 4;
-    const int tb0 = blockIdx.y * blocks;                          // first 16-query block
+    const int tb0 = blockIdx.y * blocks;          // first 16-query block
     const int nb = min(blocks, (T + kGateRows - 1) / kGateRows - tb0);
     if (nb <= 0)
         return;
 
-    uint4 bv[KS];
-    const uint16_t *brow = wv_b + ((int64_t)h * D_o + e0 + c) * DV + 8 * g;
+    uint4 bv[GG::KS];
+    {
+        const uint16_t *brow = wv_b + ((int64_t)h * D_o + (active ? e0 : 0) + c) * DV + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        bv[ks] = *reinterpret_cast<const uint4 *>(brow + 32 * ks);
+        for (int ks = 0; ks < GG::KS; ++ks)
+            bv[ks] = *reinterpret_cast<const uint4 *>(brow + 32 * ks);
+    }
 
-    // o fragments of block i: lane row t = 16*(tb0 + i) + c (zero past T)
-    auto load_a = [&](int i, uint4 (&av)[KS]) {
-        const int ta = kGateRows * (tb0 + i) + c;
-        const bool ok = ta < T;
-        const uint16_t *arow = o + ((int64_t)(ok ? ta : 0) * H + h) * DV + 8 * g;
+    // o block i: thread chunk q = row q / CH, 16-byte chunk q % CH (zero past T)
+    uint4 stg[GG::PER];
+    auto fetch = [&](int i) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            av[ks] = ok ? *reinterpret_cast<const uint4 *>(arow + 32 * ks) : make_uint4(0, 0, 0, 0);
+        for (int p = 0; p < GG::PER; ++p) {
+            const int q = threadIdx.x + p * NT;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (q < GG::CHUNKS) {
+                const int t = kGateRows * (tb0 + i) + q / GG::CH;
+                if (t < T)
+                    v = *reinterpret_cast<const uint4 *>(o + ((int64_t)t * H + h) * DV + 8 * (q % GG::CH));
+            }
+            stg[p] = v;
+        }
     };
-    auto block = [&](int i, const uint4 (&av)[KS]) {
-        f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};   // two chains, summed at the end
+    auto stash = [&](unsigned char *buf) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[ks]),
+        for (int p = 0; p < GG::PER; ++p) {
+            const int q = threadIdx.x + p * NT;
+            if (q < GG::CHUNKS)
+                *reinterpret_cast<uint4 *>(buf + (q / GG::CH) * GG::ROWB + 16 * (q % GG::CH)) = stg[p];
+        }
+    };
+    // the gate values of this lane's four outputs of block i
+    auto load_gate = [&](int i, uint16_t (&gv)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = kGateRows * (tb0 + i) + 4 * g + r;
+            gv[r] = (active && t < T) ? gate[((int64_t)t * H + h) * D_o + e0 + c] : (uint16_t)0;
+        }
+    };
+    auto compute = [&](int i, const unsigned char *buf, const uint16_t (&gv)[4]) {
+        if (!active)
+            return;
+        f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};   // two chains, summed at the end
+        const unsigned char *arow = buf + c * GG::ROWB + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < GG::KS; ++ks) {
+            const uint4 av = *reinterpret_cast<const uint4 *>(arow + 64 * ks);
+            acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                                  __builtin_bit_cast(bf16x8, bv[ks]), acc[ks & 1],
                                                                  0, 0, 0);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = kGateRows * (tb0 + i) + 4 * g + r;
             if (t < T) {
-                const int64_t idx = ((int64_t)t * H + h) * D_o + e0 + c;
-                const float x = bf16_to_f32(gate[idx]);
-                const float sg = 1.0f / (1.0f + __expf(-x));
-                out[idx] = f32_to_bf16((acc[0][r] + acc[1][r]) * sg);
+                const float sg = 1.0f / (1.0f + __expf(-bf16_to_f32(gv[r])));
+                out[((int64_t)t * H + h) * D_o + e0 + c] = f32_to_bf16((acc[0][r] + acc[1][r]) * sg);
             }
         }
     };
-    uint4 a0[KS], a1[KS];
-    load_a(0, a0);
-    int i = 0;
-    for (; i + 1 < nb; i += 2) {
-        load_a(i + 1, a1);
-        block(i, a0);
+
+    uint16_t g0[4], g1[4];
+    fetch(0);
+    load_gate(0, g0);
+    stash(ob0);
+    if (nb > 1)
+        fetch(1);
+    __syncthreads();
+    // block i is in LDS and its successor's o in registers; after the
+    // multiply the successor goes to the other buffer and block i+2 is fetched
+    auto iter = [&](int i, const unsigned char *cur, unsigned char *nxt, uint16_t (&gc)[4], uint16_t (&gn)[4]) {
+        if (i + 1 < nb)
+            load_gate(i + 1, gn);
+        compute(i, cur, gc);
+        if (i + 1 < nb)
+            stash(nxt);
         if (i + 2 < nb)
-            load_a(i + 2, a0);
-        block(i + 1, a1);
+            fetch(i + 2);
+        __syncthreads();
+    };
+    for (int i = 0; i < nb; i += 2) {
+        iter(i, ob0, ob1, g0, g1);
+        if (i + 1 < nb)
+            iter(i + 1, ob1, ob0, g1, g0);
     }
-    if (i < nb)
-        block(i, a0);
 }
 
 }  // namespace
 
 bool gated_output_supported(int32_t D_v, int32_t D_o)
 {
-    return (D_v == 512 || D_v == 64) && D_o >= kGateCols && D_o <= 1024 && D_o % kGateCols == 0;
+    return (D_v == 512 || D_v == 64) && D_o >= 64 && D_o <= 1024 && D_o % 64 == 0;
 }
 
 hipError_t launch_gated_output(const uint16_t *o, const uint16_t *wv_b, const uint16_t *gate, int32_t T, int32_t H,
@@ -124,20 +181,34 @@ hipError_t launch_gated_output(const uint16_t *o, const uint16_t *wv_b, const ui
         return hipErrorInvalidValue;
     if (T == 0 || H == 0)
         return hipSuccess;
-    // query blocks per workgroup: one while the grid is small, up to 16 once
-    // there are >= 2048 workgroups of the next size
-    const int64_t cols = (int64_t)H * (D_o / kGateCols);
+    // Few queries (decode): 4-wave workgroups of 64 columns, so that the
+    // wv_b stream spreads over twice as many workgroups; otherwise 8-wave
+    // workgroups of 128 columns, which read each o block once for more
+    // columns. Query blocks per workgroup: one while the grid is small, up to
+    // 16 once there are >= 2048 workgroups of the next size.
     const int64_t tblocks = (T + kGateRows - 1) / kGateRows;
+    const bool narrow = (int64_t)H * ((D_o + 127) / 128) * tblocks < 256;
+    const int wcols = narrow ? 64 : 128;
+    const int64_t cols = (int64_t)H * ((D_o + wcols - 1) / wcols);
     int blocks = 1;
     while (blocks < 16 && cols * ((tblocks + 2 * blocks - 1) / (2 * blocks)) >= 2048)
         blocks *= 2;
     const dim3 grid((unsigned)cols, (unsigned)((tblocks + blocks - 1) / blocks));
-    if (D_v == 512)
-        hipLaunchKernelGGL(gated_output_kernel<512>, grid, dim3(kGateThreads), 0, stream, o, wv_b, gate, T, H, D_o,
-                           blocks, out);
-    else
-        hipLaunchKernelGGL(gated_output_kernel<64>, grid, dim3(kGateThreads), 0, stream, o, wv_b, gate, T, H, D_o,
-                           blocks, out);
+#define IC_GATE_LAUNCH(DVV, NTT)                                                                                  \
+    hipLaunchKernelGGL((gated_output_kernel<DVV, NTT>), grid, dim3(NTT), 0, stream, o, wv_b, gate, T, H, D_o,     \
+                       blocks, out)
+    if (D_v == 512) {
+        if (narrow)
+            IC_GATE_LAUNCH(512, 256);
+        else
+            IC_GATE_LAUNCH(512, 512);
+    } else {
+        if (narrow)
+            IC_GATE_LAUNCH(64, 256);
+        else
+            IC_GATE_LAUNCH(64, 512);
+    }
+#undef IC_GATE_LAUNCH
     return hipGetLastError();
 }
 

@@ -253,10 +253,15 @@ def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc):
 
 # ------------------------------------------------------------ gated output --
 @pytest.mark.parametrize("T,H,D_v,D_o", [(1, 128, 512, 128), (5, 3, 512, 64), (17, 2, 512, 192),
-                                         (33, 4, 64, 64), (40, 1, 512, 1024)])
+                                         (33, 4, 64, 64), (40, 1, 512, 1024),
+                                         (250, 8, 512, 192), (253, 16, 64, 64), (600, 4, 512, 1024),
+                                         (630, 128, 512, 128)])
 def test_gated_output_close(gpu, orc, T, H, D_v, D_o):
     """sigmoid(gate) * (wv_b @ o) per head against the fp64 oracle: partial
-    query blocks (T % 16), several column blocks, both built latent widths."""
+    query blocks (T % 16), several column blocks, both built latent widths,
+    both workgroup shapes (64 columns for few query blocks, 128 otherwise,
+    with a partial last column group at D_o = 192) and runs of several query
+    blocks per workgroup."""
     wl = W.scaled(W.WORKLOADS["decode_128k"], T=T, H=H, D_v=D_v)
     gi = W.gate_inputs(wl, 0, D_o)
     got = gpu.gated_output(gi.o.cuda(), gi.wv_b.cuda(), gi.gate.cuda()).float().cpu().numpy()
