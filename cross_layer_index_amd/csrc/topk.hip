@@ -510,33 +510,37 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     int32_t *out = idx + (int64_t)t * k;
     uint32_t *h0 = hist0 + (int64_t)t * kHistCopies * kBins0;
     uint32_t *h1 = hist1 + (int64_t)t * kBins0;
-    zero_hist0<NT>(h0);                           // no reader of this query's copies remains
     if (nt <= k) {
+        zero_hist0<NT>(h0);                       // no reader of this query's copies remains
         write_all<NT>(out, nt, k);                // hist1 was not touched for this query
         return;
     }
+    // the second-digit histogram, the slice counts and the first digit are
+    // all loaded at once (one round trip), then the first-digit copies cleared
+    static_assert(kBins0 % NT == 0 && kMaxSplit <= NT, "one pass over bins and slices");
+    uint32_t hv[kBins0 / NT];
+#pragma unroll
+    for (int i = 0; i < kBins0 / NT; ++i)
+        hv[i] = h1[tid + i * NT];
+    const uint32_t c0 = tid < P ? counts[(int64_t)t * P + tid] : 0u;
     const uint32_t d0 = digit0[2 * t], above0 = digit0[2 * t + 1];
+    zero_hist0<NT>(h0);                           // no reader of this query's copies remains
     const uint32_t need0 = (uint32_t)k - above0;
     // second digit over the first-digit bin
-    for (int i = tid; i < kBins0; i += NT) {
-        sh.hist[i] = h1[i];
-        h1[i] = 0;
+#pragma unroll
+    for (int i = 0; i < kBins0 / NT; ++i) {
+        sh.hist[tid + i * NT] = hv[i];
+        h1[tid + i * NT] = 0;
     }
     __syncthreads();
     uint32_t d1, above1;
     find_digit<NT>(sh, kBins0, need0, d1, above1);
     const uint32_t bound = (d0 << 21) | (d1 << 10);
-    // slice offsets
-    uint32_t total = 0;
-    for (int w0 = 0; w0 < P; w0 += NT) {
-        const int ww = w0 + tid;
-        const uint32_t c = ww < P ? counts[(int64_t)t * P + ww] : 0u;
-        uint32_t tot;
-        const uint32_t excl = block_scan<NT>(c, sh.waves, &tot) - c;
-        if (ww < P)
-            offs[ww] = total + excl;
-        total += tot;
-    }
+    // slice offsets (P <= NT: one scan)
+    uint32_t total;
+    const uint32_t excl = block_scan<NT>(c0, sh.waves, &total) - c0;
+    if (tid < P)
+        offs[tid] = excl;
     if (tid == 0)
         offs[P] = total;
     __syncthreads();
