@@ -112,6 +112,14 @@ def topk_case(name):
         n = np.full(300, 12000, np.int32)
         n[::7] = 11999
         return rng.integers(24576, 28672, size=(300, 12000)).astype(np.float32), n, 2048
+    # more ties at the two-digit bound than the finishing workgroup's list
+    # holds: the split path falls back to digit passes over the whole row
+    if name == "all_equal_split":
+        n = np.array([131072, 50000], np.int32)
+        s = np.full((2, 131072), 7.0, np.float32)
+        s[:, ::977] = 8.0
+        s[1, 3::1201] = 9.0
+        return s, n, 2048
     if name == "all_equal_row":
         n = np.full(260, 9000, np.int32)
         s = np.full((260, 9000), 7.0, np.float32)
@@ -121,7 +129,7 @@ def topk_case(name):
 
 
 @pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1",
-                                  "dense_bin_split", "dense_bin_row", "all_equal_row"])
+                                  "dense_bin_split", "dense_bin_row", "all_equal_split", "all_equal_row"])
 def test_topk_exact(gpu, orc, name):
     s, n, k = topk_case(name)
     T, L = s.shape
