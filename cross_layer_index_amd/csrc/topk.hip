@@ -42,7 +42,8 @@ namespace {
 
 constexpr int kBins0 = kHistBins0;      // first digit: bits 31..21
 constexpr int kSplitThreads = 256;
-constexpr int kSplitChunk = kSplitThreads * 4;   // scores per split workgroup
+constexpr int kSplitRuns = 2;                      // groups of 4 consecutive scores per survivors thread
+constexpr int kSplitChunk = kSplitThreads * 4 * kSplitRuns;   // scores per split workgroup
 constexpr int kRowThreads = 1024;
 constexpr int kFinishThreads = 1024;
 constexpr int kListCap = 18432;         // survivors held in LDS (split path)
@@ -451,31 +452,38 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
         return;                                   // the finish kernel keeps everything
     const float *row = scores + (int64_t)t * ld;
     // this chunk's scores, issued before the histogram is read
-    const int64_t s = (int64_t)w * kSplitChunk + (int64_t)tid * 4;
-    uint32_t key[4];
-    int64_t pos[4];
-    bool ok[4];
-    RowSrc{row, nt}.get4(s, key, pos, ok);
+    const int64_t s = (int64_t)w * kSplitChunk + (int64_t)tid * 4 * kSplitRuns;
+    uint32_t key[kSplitRuns][4];
+    int64_t pos[kSplitRuns][4];
+    bool ok[kSplitRuns][4];
+#pragma unroll
+    for (int r = 0; r < kSplitRuns; ++r)
+        RowSrc{row, nt}.get4(s + 4 * r, key[r], pos[r], ok[r]);
     for (int i = tid; i < kBins0; i += kSplitThreads)
         sh.hist[i] = 0;
 
     uint32_t d0, above0;
     find_digit0_topdown<kSplitThreads>(sh, hist0 + (int64_t)t * kHistCopies * kBins0, (uint32_t)k, d0, above0);
-    uint32_t sv[4], ls = 0;
+    uint32_t ls = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        sv[e] = ok[e] && (key[e] >> 21) >= d0;
-        ls += sv[e];
-        if (ok[e] && (key[e] >> 21) == d0)
-            atomicAdd(&sh.hist[(key[e] >> 10) & (kBins0 - 1)], 1u);
-    }
+    for (int r = 0; r < kSplitRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool sv = ok[r][e] && (key[r][e] >> 21) >= d0;
+            ls += sv;
+            if (ok[r][e] && (key[r][e] >> 21) == d0)
+                atomicAdd(&sh.hist[(key[r][e] >> 10) & (kBins0 - 1)], 1u);
+            ok[r][e] = sv;
+        }
     uint32_t tot;
     uint32_t o = block_scan<kSplitThreads>(ls, sh.waves, &tot) - ls;   // its barriers also close the histogram
     uint64_t *reg = regions + ((int64_t)t * P + w) * kSplitChunk;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (sv[e])
-            reg[o++] = ((uint64_t)key[e] << 32) | (uint32_t)pos[e];
+    for (int r = 0; r < kSplitRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (ok[r][e])
+                reg[o++] = ((uint64_t)key[r][e] << 32) | (uint32_t)pos[r][e];
     uint32_t *h1 = hist1 + (int64_t)t * kBins0;
     for (int i = tid; i < kBins0; i += kSplitThreads)
         if (sh.hist[i])
