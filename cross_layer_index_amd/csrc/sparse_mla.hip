@@ -527,6 +527,15 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
     const int tid = threadIdx.x;
     const float ms = sink[h] * kLog2e;
     const int64_t pr0 = (int64_t)t * splits * H + h;          // row of split 0
+    // this thread's four columns of the first kCombineBatch splits: they do
+    // not depend on the weights, so they travel with the (m, l) loads
+    const float4 *p = reinterpret_cast<const float4 *>(part_o + pr0 * DV) + tid;
+    const int64_t stride = (int64_t)H * DV / 4;               // float4s between splits
+    float4 x[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+        if (u < splits)
+            x[u] = p[(int64_t)u * stride];
     // global maximum over the sink and the partial maxima
     float m = tid == 0 ? ms : -INFINITY;
     for (int s = tid; s < splits; s += NT)
@@ -563,16 +572,15 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
     for (int i = 1; i < NW; ++i)
         den += red[1][i];
     const float inv = 1.0f / den;
-    // this thread's four columns of every split, kCombineBatch loads in flight
-    const float4 *p = reinterpret_cast<const float4 *>(part_o + pr0 * DV) + tid;
-    const int64_t stride = (int64_t)H * DV / 4;               // float4s between splits
+    // every split's columns, kCombineBatch loads in flight
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
-        float4 x[kCombineBatch];
+        if (s0 > 0) {
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-            if (s0 + u < splits)
-                x[u] = p[(int64_t)(s0 + u) * stride];
+            for (int u = 0; u < kCombineBatch; ++u)
+                if (s0 + u < splits)
+                    x[u] = p[(int64_t)(s0 + u) * stride];
+        }
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u)
             if (s0 + u < splits) {
