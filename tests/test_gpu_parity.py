@@ -3,6 +3,7 @@
 Integer work (scores of integer-valued fp8 inputs, top-k index sets) must match
 bit for bit; attention outputs must be within max-abs 5e-3 of the oracle's
 fp64 result. Inputs come from the seeded generator only."""
+import ctypes
 import math
 
 import numpy as np
@@ -126,6 +127,29 @@ def topk_case(name):
         s[:, ::1000] = 8.0
         return s, n, 2048
     raise KeyError(name)
+
+
+def test_topk_workspace_reuse(gpu, orc):
+    """One workspace serves repeated top-k calls of one shape with new scores
+    each time (every call leaves its counters zero), on the split path and on
+    the row path; between shapes it is zero-filled again, as the C ABI asks."""
+    rng = np.random.default_rng(77)
+    shapes = [(1, 131072, 2048), (3, 5000, 2048), (300, 3000, 64), (5, 300, 7), (2, 70000, 2048)]
+    need = 0
+    for T, L, k in shapes:
+        qs = gpu.make_queries(torch.zeros(T, dtype=torch.int64), torch.full((T,), L, dtype=torch.int32), L)
+        need = max(need, gpu._lib.ic_topk_workspace_size(ctypes.byref(qs.c()), k))
+    ws = gpu.workspace(need)
+    for T, L, k in shapes:
+        ws.zero_()
+        n = rng.integers(max(1, L // 2), L + 1, size=T).astype(np.int32)
+        qs = gpu.make_queries(torch.zeros(T, dtype=torch.int64), torch.from_numpy(n), L)
+        for rep in range(3):
+            s = rng.integers(0, 4000, size=(T, L)).astype(np.float32)
+            buf = np.zeros((T, gpu.score_ld(L)), np.float32)
+            buf[:, :L] = s
+            got = gpu.topk(torch.from_numpy(buf).cuda(), qs, k, ws=ws).cpu().numpy()
+            assert np.array_equal(got, orc.topk(s, n, k)), f"shape {(T, L, k)}, call {rep}"
 
 
 @pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1",
