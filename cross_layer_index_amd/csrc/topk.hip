@@ -631,6 +631,71 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
 }
 
 // ---- row path ---------------------------------------------------------------
+// Long rows skip the full histogram pass: blocks of kSampleBlock scores at
+// every kSampleStride-th block (1/16 of the row) are read twice -- the first
+// digit's histogram, then the second digit's inside the bin that holds the
+// target rank -- and give a two-digit key bound with, among the samples, a
+// quarter more keys at or above it than the k-th largest key is expected to
+// have. One pass then collects every key of the row at or above the bound; if
+// there are at least k of them, the k-th largest key and all its ties are
+// among them, and the selection finishes from that list. Otherwise (or when
+// they exceed the global list) the row takes the exact two-pass path.
+constexpr int kSampleBlock = 256;          // consecutive scores per sampled block
+constexpr int kSampleStride = 16;          // one block in kSampleStride is sampled
+constexpr int64_t kSampleMinN = 65536;     // shorter rows take the two-pass path
+static_assert(kSampleBlock % 4 == 0, "groups of four stay inside a sampled block");
+
+// Returns the bound, or 0 when the samples cannot give one.
+template <int NT>
+__device__ uint32_t sampled_bound(const RowSrc &src, int32_t k, Shared &sh)
+{
+    const int64_t nblocks = (src.n + kSampleBlock - 1) / kSampleBlock;
+    const int64_t slots = (nblocks + kSampleStride - 1) / kSampleStride * kSampleBlock;
+    auto at = [](int64_t s) {                      // row position of sample slot s
+        return s / kSampleBlock * (int64_t)(kSampleBlock * kSampleStride) + s % kSampleBlock;
+    };
+    for (int i = threadIdx.x; i < kBins0; i += NT)
+        sh.hist[i] = 0;
+    __syncthreads();
+    uint32_t mine = 0;
+    for (int64_t s0 = (int64_t)threadIdx.x * 4; s0 < slots; s0 += (int64_t)NT * 4) {
+        uint32_t key[4];
+        int64_t pos[4];
+        bool ok[4];
+        src.get4(at(s0), key, pos, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            mine += ok[e];
+            hist_add_wave(sh.hist, key[e] >> 21, ok[e]);
+        }
+    }
+    uint32_t ns;
+    block_scan<NT>(mine, sh.waves, &ns);           // its barriers also close the histogram
+    // the k-th largest key's expected rank among the samples, plus a quarter and 16
+    const uint64_t tgt = ((uint64_t)k * ns * 5 + (uint64_t)src.n * 4 - 1) / ((uint64_t)src.n * 4) + 16;
+    if (tgt > ns)
+        return 0u;
+    uint32_t b, above;
+    find_digit<NT>(sh, kBins0, (uint32_t)tgt, b, above);
+    for (int i = threadIdx.x; i < kBins0; i += NT)
+        sh.hist[i] = 0;
+    __syncthreads();
+    for (int64_t s0 = (int64_t)threadIdx.x * 4; s0 < slots; s0 += (int64_t)NT * 4) {
+        uint32_t key[4];
+        int64_t pos[4];
+        bool ok[4];
+        src.get4(at(s0), key, pos, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hist_add_wave(sh.hist, (key[e] >> 10) & (kBins0 - 1), ok[e] && (key[e] >> 21) == b);
+    }
+    __syncthreads();
+    uint32_t d1, above1;
+    find_digit<NT>(sh, kBins0, (uint32_t)tgt - above, d1, above1);
+    return (b << 21) | (d1 << 10);
+}
+
+
 // grid: T; block: 1024. With `hist0` non-null the first digit's histogram is
 // taken from it (and zeroed); otherwise it is built here.
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__restrict__ scores, int64_t ld,
@@ -655,10 +720,26 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
             zero_hist0<kRowThreads>(h0);
         return;
     }
+    uint64_t *gl = surv + (int64_t)t * kRowSurvCap;
     if (h0) {
         load_hist0<kRowThreads>(sh, h0);
         zero_hist0<kRowThreads>(h0);
     } else {
+        if (nt >= kSampleMinN) {
+            const uint32_t bound = sampled_bound<kRowThreads>(src, k, sh);
+            if (bound != 0u) {
+                const uint32_t c = collect<kRowThreads, kRowRuns>(src, bound, sh, list, (uint32_t)kRowListCap, gl,
+                                                                  (uint32_t)kRowSurvCap);
+                if (c >= (uint32_t)k && c <= (uint32_t)kRowListCap) {
+                    finish_select<kRowThreads>(ListSrc{list, c}, sh, 0, 0u, 0u, (uint32_t)k, k, out);
+                    return;
+                }
+                if (c >= (uint32_t)k && c <= (uint32_t)kRowSurvCap) {
+                    finish_select<kRowThreads>(GListSrc{gl, c}, sh, 0, 0u, 0u, (uint32_t)k, k, out);
+                    return;
+                }
+            }
+        }
         for (int i = tid; i < kBins0; i += kRowThreads)
             sh.hist[i] = 0;
         __syncthreads();
@@ -677,7 +758,6 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
     find_digit<kRowThreads>(sh, kBins0, (uint32_t)k, d0, above0);
     const uint32_t need = (uint32_t)k - above0;
     // survivors in position order: into LDS, and into this query's global list
-    uint64_t *gl = surv + (int64_t)t * kRowSurvCap;
     const uint32_t total = collect<kRowThreads, kRowRuns>(src, d0 << 21, sh, list, (uint32_t)kRowListCap, gl,
                                                            (uint32_t)kRowSurvCap);
     if (total <= (uint32_t)kRowListCap)

@@ -121,6 +121,25 @@ def topk_case(name):
         s[:, ::977] = 8.0
         s[1, 3::1201] = 9.0
         return s, n, 2048
+    # long rows on the row path: the k-th key is bounded from 1/16 of the row
+    # (every 16th block of 256 scores), then one pass collects the keys above
+    if name == "sampled_row":
+        n = rng.integers(65536, 70001, size=260).astype(np.int32)
+        return rng.integers(0, 4000, size=(260, 70000)).astype(np.float32), n, 2048
+    # the sampled blocks hold the largest scores: fewer than k keys reach the
+    # bound, so the exact two-pass path runs
+    if name == "sampled_row_fallback":
+        n = np.full(260, 65536, np.int32)
+        s = rng.integers(0, 1000, size=(260, 65536)).astype(np.float32)
+        blk = (np.arange(65536) // 256) % 16 == 0
+        s[:, blk] = 1000.0
+        return s, n, 8192
+    # every sample equal: all keys reach the bound and overflow the list
+    if name == "sampled_all_equal_row":
+        n = np.full(256, 66000, np.int32)
+        s = np.full((256, 66000), 7.0, np.float32)
+        s[:, 5::997] = 8.0
+        return s, n, 2048
     if name == "all_equal_row":
         n = np.full(260, 9000, np.int32)
         s = np.full((260, 9000), 7.0, np.float32)
@@ -153,7 +172,8 @@ def test_topk_workspace_reuse(gpu, orc):
 
 
 @pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1",
-                                  "dense_bin_split", "dense_bin_row", "all_equal_split", "all_equal_row"])
+                                  "dense_bin_split", "dense_bin_row", "all_equal_split", "all_equal_row",
+                                  "sampled_row", "sampled_row_fallback", "sampled_all_equal_row"])
 def test_topk_exact(gpu, orc, name):
     s, n, k = topk_case(name)
     T, L = s.shape
