@@ -145,8 +145,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not supported "
-                                   "(the path shards by sequence, see the design notes)"}))
+        print(json.dumps({"error": "bench.py measures one GPU only; runs on several GPUs are not supported "
+                                   "(decode shards by sequence with no exchange, so one GPU's figure is its share)"}))
         sys.exit(2)
 
     import torch
