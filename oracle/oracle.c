@@ -274,6 +274,8 @@ uint8_t orc_encode_fp8_e4m3fn(double x)
     if (isnan(x))
         return 0x7F;
     const int sign = signbit(x) ? 0x80 : 0;
+    if (isinf(x))
+        return (uint8_t)(sign | 0x7E);              /* no infinity: the largest finite magnitude */
     const double a = fabs(x);
     int best = 0;
     double bd = INFINITY;

@@ -75,8 +75,8 @@ def test_fp8_matches_torch_cast_in_range(orc):
 
 def test_fp8_saturates(orc):
     """The format has no infinity: the cast saturates at +-448 (code 0x7E)."""
-    got = orc.encode_fp8([448.0, 449.0, 464.0, 500.0, 1e30, -449.0, -1e30])
-    assert list(got) == [0x7E] * 5 + [0xFE] * 2
+    got = orc.encode_fp8([448.0, 449.0, 464.0, 500.0, 1e30, np.inf, -449.0, -1e30, -np.inf])
+    assert list(got) == [0x7E] * 6 + [0xFE] * 3
 
 
 # ------------------------------------------------------------- LayerNorm ----
