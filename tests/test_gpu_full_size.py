@@ -177,3 +177,30 @@ def test_prefill_1m_full(gpu, orc):
     # every row: a valid index set of the right size
     assert (idx_all >= 0).all() and (np.diff(idx_all, axis=1) > 0).all()
     assert (idx_all < n[:, None]).all()
+    # every row against its own scores (recomputed by the indexer, exact):
+    # no unselected score above a selected one, ties at the threshold taken
+    # in position order
+    sc = gpu.indexer_score(lays[0]["q_idx"], lays[0]["w"], lays[0]["k_idx"], qs)
+    topk_invariants_gpu(sc, torch.from_numpy(n).cuda(), st.index_cache[0].long())
+
+
+def topk_invariants_gpu(sc, n, idx, rows=256):
+    """Row-by-row (in chunks) check of a top-k index set on the device."""
+    T, ld = sc.shape
+    pos = torch.arange(ld, device=sc.device)
+    for r0 in range(0, T, rows):
+        r1 = min(T, r0 + rows)
+        s = sc[r0:r1]
+        valid = pos[None, :] < n[r0:r1, None]
+        sel = torch.zeros_like(valid)
+        sel.scatter_(1, idx[r0:r1], True)
+        assert not bool((sel & ~valid).any()), f"rows {r0}..{r1}: index outside the visible tokens"
+        lo_sel = torch.where(sel, s, torch.full_like(s, float("inf"))).amin(1)
+        hi_rest = torch.where(valid & ~sel, s, torch.full_like(s, float("-inf"))).amax(1)
+        assert bool((lo_sel >= hi_rest).all()), f"rows {r0}..{r1}: an unselected score exceeds a selected one"
+        tie = lo_sel == hi_rest
+        if bool(tie.any()):
+            at = s == lo_sel[:, None]
+            last_sel = torch.where(sel & at, pos[None, :], torch.full_like(pos[None, :], -1)).amax(1)
+            first_rest = torch.where(valid & ~sel & at, pos[None, :], torch.full_like(pos[None, :], ld)).amin(1)
+            assert bool((last_sel[tie] < first_rest[tie]).all()), f"rows {r0}..{r1}: tie rule violated"
