@@ -456,8 +456,10 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
         if (reuse_map[l] == l) {
             slot[l] = next_slot++;
             int32_t *idx = index_cache + slot[l] * slot_elems;
-            // the per-query key stream also fills the top-k's first-digit histogram
-            const bool fused_hist = qs->max_n > 0 && !use_prefill_indexer(qs, d->H_I, d->D_I);
+            // the per-query key stream also fills the top-k's first-digit
+            // histogram when the selection reads it
+            const bool fused_hist = qs->max_n > 0 && !use_prefill_indexer(qs, d->H_I, d->D_I) &&
+                                    ic::topk_reads_hist0(qs->T, qs->max_n);
             if (qs->max_n > 0) {
                 hipError_t e = launch_indexer(y.q_idx, y.w, y.k_idx, qs, d->H_I, d->D_I, scores, L.ld,
                                               fused_hist ? ic::topk_hist0(topk_ws) : nullptr, st);

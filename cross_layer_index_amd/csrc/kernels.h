@@ -32,6 +32,9 @@ bool indexer_prefill_supported(int32_t H_I, int32_t D_I);
 // (uint32, zero on entry and on return); topk_hist0() points at them.
 size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t k);
 uint32_t *topk_hist0(void *ws);
+// Whether the selection for this shape reads those histograms (a producer
+// need not fill them otherwise).
+bool topk_reads_hist0(int32_t T, int64_t max_n);
 // hist_ready: the histograms were filled while the scores were produced.
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
                        int32_t k, int32_t *idx, void *ws, bool hist_ready, hipStream_t stream);

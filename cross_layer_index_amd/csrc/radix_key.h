@@ -19,20 +19,24 @@ __device__ __forceinline__ uint32_t ord_key(float x)
 
 // Adds one count to LDS histogram bin `b` for every lane with `live` set.
 // Scores crowd into a few first-digit bins, so the lanes of one LDS atomic
-// mostly hit the same address and serialise: the wave first adds the first
-// live lane's bin with one atomic for all lanes that share it, then the rest
-// one by one. It uses ballots: lanes that do not execute it add nothing.
+// mostly hit the same address and serialise: the wave adds the bin of its
+// first remaining live lane with one atomic for all lanes that share it, twice
+// over, then the rest one by one. It uses ballots: lanes that do not execute it
+// add nothing.
 __device__ __forceinline__ void hist_add_wave(uint32_t *hist, uint32_t b, bool live)
 {
-    const uint64_t pm = __ballot(live);
     bool rest = live;
-    if (pm) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint64_t pm = __ballot(rest);
+        if (pm == 0)
+            break;
         const uint32_t lead = __builtin_amdgcn_readlane(b, __builtin_ctzll(pm));
-        const bool same = live && b == lead;
+        const bool same = rest && b == lead;
         const uint64_t m = __ballot(same);
         if (same && (m & __lanemask_lt()) == 0)
             atomicAdd(&hist[lead], (uint32_t)__popcll(m));
-        rest = live && !same;
+        rest = rest && !same;
     }
     if (rest)
         atomicAdd(&hist[b], 1u);

@@ -13,24 +13,30 @@
 // min(#equal keys before it, need) -- a prefix sum of packed (above, equal)
 // counts.
 //
-// The first digit's histogram is built while the scores are produced (the
-// indexer kernel can add into it) or by topk_hist_kernel. Only keys whose
-// first digit is >= the threshold digit ("survivors", about k plus one bin)
-// take part in the later digits:
-//   * split path (few queries, long rows): P workgroups per query each copy
-//     their chunk's survivors, in position order, into their own slice of the
-//     workspace and add the second digit's histogram of the threshold bin
-//     (topk_survivors_kernel); one workgroup per query then reads the second
-//     digit, gathers in order into LDS only the survivors at or above the
-//     two-digit bound, and finishes the selection there (topk_finish_kernel).
-//     The kernel boundary orders the two phases.
-//   * row path (many queries): one workgroup per query streams its row once
-//     more to collect survivors into LDS and finishes there. When they exceed
-//     the LDS list (the threshold fell into a dense first-digit bin), it
-//     histograms the second digit over the survivors kept in global memory and
-//     keeps only those at or above the second-digit threshold.
-// Only ties spanning more than the list at 21 bits of the key fall back to
-// digit passes over the full row.
+// Only keys at or above a bound on the k-th largest key (about k of them)
+// take part in the digits, in LDS:
+//   * split path (few queries, long rows): P workgroups per query each read
+//     a fixed sample of the row (blocks of 32 scores spread over it), derive
+//     from it the same two-digit bound, which at least k keys reach with high
+//     probability, and copy their chunk's keys at or above it, in position
+//     order, into their own slice of the workspace (topk_collect_kernel); one
+//     workgroup per query gathers those into LDS and finishes there
+//     (topk_finish_kernel), or over the whole row when fewer than k keys
+//     reached the bound. The kernel boundary orders the two phases.
+//     Scores spanning less than a factor of two share a handful of
+//     first-digit bins (the digit holds two mantissa bits), so a bound from
+//     the first digit alone could keep half a row.
+//   * row path (many queries): one workgroup per query. Rows of at least
+//     kSampleMinN scores take the same kind of bound from 1/16 of the row;
+//     shorter ones, and rows whose sampled bound fails, take the first digit's
+//     histogram (built while the scores were produced -- the indexer kernel can
+//     add into it -- or by one pass here), then stream the row once more to
+//     collect its survivors into LDS and finish there. When those exceed the
+//     LDS list (the threshold fell into a dense first-digit bin), the second
+//     digit's histogram over the survivors kept in global memory keeps only
+//     those at or above the second-digit threshold.
+// Only ties spanning more than a list fall back to digit passes over the
+// full row.
 // The first-digit histogram is kept in kHistCopies copies per query (adders
 // pick a copy by workgroup index, which spreads atomic traffic); the workspace
 // holds them zeroed on entry and the finishing workgroup zeroes them again.
@@ -41,7 +47,7 @@ namespace ic {
 namespace {
 
 constexpr int kBins0 = kHistBins0;      // first digit: bits 31..21
-constexpr int kSplitThreads = 256;
+constexpr int kSplitThreads = 1024;
 constexpr int kSplitRuns = 2;                      // groups of 4 consecutive scores per survivors thread
 constexpr int kSplitChunk = kSplitThreads * 4 * kSplitRuns;   // scores per split workgroup
 constexpr int kRowThreads = 1024;
@@ -50,84 +56,123 @@ constexpr int kListCap = 18432;         // survivors held in LDS (split path)
 constexpr int kRowListCap = 8192;       // survivors held in LDS (row path: two workgroups per CU)
 constexpr int kRowRuns = 2;             // consecutive groups of 4 scores per thread per collect round
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
-constexpr int kGatherPer = 20;          // survivors per finishing thread and gather round
+constexpr int kSpec = 8;                // slice entries per finishing thread loaded ahead of the counts
 constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
 
+// Workgroup barrier. The full form is __syncthreads, whose release fence
+// also waits for every global store and load in flight; the LDS form (this
+// wave's LDS operations complete, then s_barrier) orders LDS traffic only and
+// serves kernels that read back none of their own global stores. The memory
+// clobber keeps the compiler from moving memory operations across it.
+template <bool LdsOnly>
+__device__ __forceinline__ void wg_barrier()
+{
+    if constexpr (LdsOnly)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        __syncthreads();
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in registers (DPP): row
+// shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then the last lane of row
+// 0 is added to row 1 and that of row 2 to row 3, and the last lane of row 1
+// to rows 2 and 3. Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v)
+{
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+    return (uint32_t)x;
+}
+
 // Block-wide inclusive scan of one uint32 per thread.
-template <int NT>
+template <int NT, bool LB = false>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *lds_waves, uint32_t *total)
 {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(v, off);
-        if (lane >= off)
-            v += o;
-    }
+    v = wave_scan(v);
     if (lane == 63)
         lds_waves[wave] = v;
-    __syncthreads();
+    wg_barrier<LB>();
     if (wave == 0) {
-        uint32_t x = lane < NW ? lds_waves[lane] : 0u;
-#pragma unroll
-        for (int off = 1; off < NW; off <<= 1) {
-            const uint32_t o = __shfl_up(x, off);
-            if (lane >= off)
-                x += o;
-        }
+        const uint32_t x = wave_scan(lane < NW ? lds_waves[lane] : 0u);
         if (lane < NW)
             lds_waves[lane] = x;
     }
-    __syncthreads();
+    wg_barrier<LB>();
     const uint32_t before = wave ? lds_waves[wave - 1] : 0u;
     if (total)
         *total = lds_waves[NW - 1];
-    __syncthreads();
+    wg_barrier<LB>();
     return v + before;
 }
 
 struct Shared {
     uint32_t hist[kBins0];
     uint32_t waves[16];
-    uint32_t digit, above;
+    uint32_t digit, above, count;
 };
 
-// Given a histogram of `nb` bins (in LDS), find the digit of the bin holding
-// the need-th largest key; returns it with the count of keys in higher bins.
-template <int NT>
+// Given a histogram of `nb` (1024 or 2048) bins in LDS, complete before the
+// call, find the digit of the bin holding the need-th largest key; returns it
+// with the count of keys in higher bins (and, in sh.count, the bin's own
+// count). One wave scans: lane l owns nb/64
+// consecutive bins, lane 0 the highest; a wave prefix sum of their totals
+// names the lane whose range holds the need-th key, and a second one over
+// that range, one bin per lane from the top, names the bin. One barrier
+// publishes the result (a barrier before the next call separates these reads
+// from its writes). Digit 0 and 0 when the counts never reach `need`.
+template <int NT, bool LB = false>
 __device__ __forceinline__ void find_digit(Shared &sh, int nb, uint32_t need, uint32_t &digit, uint32_t &above)
 {
-    constexpr int PER = kBins0 / NT;             // bins per thread (descending)
-    uint32_t c[PER];
-    uint32_t local = 0;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int per = nb >> 6;                       // bins per lane: 32 or 16
+        const int quads = per >> 2;
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(&sh.hist[nb - (lane + 1) * per]);
+        uint32_t local = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int b = nb - 1 - (PER * (int)threadIdx.x + i);
-        c[i] = b >= 0 ? sh.hist[b] : 0u;
-        local += c[i];
-    }
-    const uint32_t incl = block_scan<NT>(local, sh.waves, nullptr);
-    uint32_t run = incl - local;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int b = nb - 1 - (PER * (int)threadIdx.x + i);
-        if (b >= 0 && run < need && run + c[i] >= need) {
-            sh.digit = (uint32_t)b;
-            sh.above = run;
+        for (int j = 0; j < 8; ++j)
+            if (j < quads) {
+                const uint4 c = h4[j];
+                local += c.x + c.y + c.z + c.w;
+            }
+        const uint32_t incl = wave_scan(local);
+        const uint64_t hit = __ballot(incl - local < need && incl >= need);
+        if (hit == 0) {
+            if (lane == 0) {
+                sh.digit = 0;
+                sh.above = 0;
+                sh.count = 0;
+            }
+        } else {
+            const int L = __builtin_ctzll(hit);
+            const uint32_t run = __builtin_amdgcn_readlane(incl - local, L);
+            const int b = nb - L * per - 1 - lane;     // lane i takes the range's i-th bin from the top
+            const uint32_t x = lane < per ? sh.hist[b] : 0u;
+            const uint32_t in2 = run + wave_scan(x);
+            if (lane < per && in2 - x < need && in2 >= need) {
+                sh.digit = (uint32_t)b;
+                sh.above = in2 - x;
+                sh.count = x;
+            }
         }
-        run += c[i];
     }
-    __syncthreads();
+    wg_barrier<LB>();
     digit = sh.digit;
     above = sh.above;
-    __syncthreads();
 }
 
 // Key sources: a row of fp32 scores (position = index) or an LDS list of
 // (key << 32 | position) entries in position order.
 struct RowSrc {
+    static constexpr bool kLds = false;
     const float *row;
     int64_t n;
     __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
@@ -150,6 +195,36 @@ struct RowSrc {
 };
 
 struct ListSrc {
+    static constexpr bool kLds = true;
+    const uint64_t *list;                          // 16-byte aligned
+    int64_t n;
+    // i is a multiple of 4: two 16-byte reads
+    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
+    {
+        uint64_t v[4] = {0ull, 0ull, 0ull, 0ull};
+        if (i + 3 < n) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(list + i);
+            const uint4 b = *reinterpret_cast<const uint4 *>(list + i + 2);
+            v[0] = a.x | ((uint64_t)a.y << 32), v[1] = a.z | ((uint64_t)a.w << 32);
+            v[2] = b.x | ((uint64_t)b.y << 32), v[3] = b.z | ((uint64_t)b.w << 32);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (i + e < n)
+                    v[e] = list[i + e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ok[e] = i + e < n;
+            key[e] = (uint32_t)(v[e] >> 32);
+            pos[e] = (int64_t)(uint32_t)v[e];
+        }
+    }
+};
+
+// A contiguous (key << 32 | position) list in global memory, position order.
+struct GListSrc {
+    static constexpr bool kLds = false;
     const uint64_t *list;
     int64_t n;
     __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
@@ -164,21 +239,36 @@ struct ListSrc {
     }
 };
 
-// A contiguous (key << 32 | position) list in global memory, position order.
-struct GListSrc {
-    const uint64_t *list;
-    int64_t n;
-    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
-    {
+// Calls f(key, live) once for every entry of `src`, in no particular order,
+// with every lane of the wave taking part in each call (f may use ballots).
+// An LDS list is read interleaved (lane i takes entry i, i + NT, ...), which
+// keeps the lanes of one read on distinct banks; other sources are read four
+// consecutive entries per thread.
+template <int NT, class Src, class F>
+__device__ __forceinline__ void for_each_key(const Src &src, F f)
+{
+    if constexpr (Src::kLds) {
+        for (int64_t i0 = 0; i0 < src.n; i0 += (int64_t)NT * 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ok[e] = i + e < n;
-            const uint64_t v = ok[e] ? list[i + e] : 0ull;
-            key[e] = (uint32_t)(v >> 32);
-            pos[e] = (int64_t)(uint32_t)v;
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = i0 + threadIdx.x + (int64_t)NT * e;
+                const bool ok = i < src.n;
+                const uint64_t v = ok ? src.list[i] : 0ull;
+                f((uint32_t)(v >> 32), ok);
+            }
+        }
+    } else {
+        for (int64_t i = (int64_t)threadIdx.x * 4; i < src.n; i += (int64_t)NT * 4) {
+            uint32_t key[4];
+            int64_t pos[4];
+            bool ok[4];
+            src.get4(i, key, pos, ok);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f(key[e], ok[e]);
         }
     }
-};
+}
 
 // Ordered compaction of the entries with key >= bound into an LDS list (the
 // first lcap) and, if given, a global list (the first gcap). Returns the count.
@@ -226,8 +316,9 @@ __device__ uint32_t collect(const Src &src, uint32_t bound, Shared &sh, uint64_t
     return total;
 }
 
-// Digit passes `first`..2 over `src`, then the ordered compaction into out[0..k).
-template <int NT, class Src>
+// Digit passes `first`..2 over `src` (none when first is 3: then `prefix` is
+// the threshold key itself), then the ordered compaction into out[0..k).
+template <int NT, bool LB = false, class Src>
 __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t prefix, uint32_t pmask,
                               uint32_t need, int32_t k, int32_t *__restrict__ out)
 {
@@ -237,20 +328,20 @@ __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t pr
         const int nb = pass == 2 ? 1024 : 2048;
         for (int i = tid; i < nb; i += NT)
             sh.hist[i] = 0;
-        __syncthreads();
-        for (int64_t i = (int64_t)tid * 4; i < src.n; i += (int64_t)NT * 4) {
-            uint32_t key[4];
-            int64_t pos[4];
-            bool ok[4];
-            src.get4(i, key, pos, ok);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (ok[e] && (key[e] & pmask) == prefix)
-                    atomicAdd(&sh.hist[(key[e] >> shf) & (nb - 1)], 1u);
-        }
-        __syncthreads();
+        wg_barrier<LB>();
+        // first digits crowd into a few bins (aggregated adds); later ones
+        // spread out (plain adds)
+        for_each_key<NT>(src, [&](uint32_t key, bool ok) {
+            const bool live = ok && (key & pmask) == prefix;
+            const uint32_t b = (key >> shf) & (nb - 1);
+            if (pass == 0)
+                hist_add_wave(sh.hist, b, live);
+            else if (live)
+                atomicAdd(&sh.hist[b], 1u);
+        });
+        wg_barrier<LB>();
         uint32_t digit, above;
-        find_digit<NT>(sh, nb, need, digit, above);
+        find_digit<NT, LB>(sh, nb, need, digit, above);
         prefix |= digit << shf;
         pmask |= (uint32_t)(nb - 1) << shf;
         need -= above;
@@ -271,7 +362,7 @@ __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t pr
         const uint32_t lg = gt[0] + gt[1] + gt[2] + gt[3];
         const uint32_t le = eq[0] + eq[1] + eq[2] + eq[3];
         uint32_t tot;
-        const uint32_t incl = block_scan<NT>(lg | (le << 16), sh.waves, &tot);
+        const uint32_t incl = block_scan<NT, LB>(lg | (le << 16), sh.waves, &tot);
         const uint32_t excl = incl - (lg | (le << 16));
         uint32_t gb = run_gt + (excl & 0xFFFFu);
         uint32_t eb = run_eq + (excl >> 16);
@@ -310,16 +401,9 @@ __device__ void finish_from_overflow(const Src &src, const Fallback &row, Shared
     for (int i = threadIdx.x; i < kBins0; i += NT)
         sh.hist[i] = 0;
     __syncthreads();
-    for (int64_t i = (int64_t)threadIdx.x * 4; i < src.n; i += (int64_t)NT * 4) {
-        uint32_t key[4];
-        int64_t pos[4];
-        bool ok[4];
-        src.get4(i, key, pos, ok);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (ok[e] && (key[e] & 0xFFE00000u) == p0)
-                atomicAdd(&sh.hist[(key[e] >> 10) & 2047], 1u);
-    }
+    for_each_key<NT>(src, [&](uint32_t key, bool ok) {
+        hist_add_wave(sh.hist, (key >> 10) & 2047, ok && (key & 0xFFE00000u) == p0);
+    });
     __syncthreads();
     uint32_t d1, above1;
     find_digit<NT>(sh, 2048, need0, d1, above1);
@@ -361,87 +445,79 @@ __device__ void zero_hist0(uint32_t *h)
         *reinterpret_cast<uint4 *>(h + i) = make_uint4(0, 0, 0, 0);
 }
 
-// ---- first-digit histogram of a score row (standalone top-k) -------------
-// grid: (chunks, T); block: 256.
-__global__ __launch_bounds__(256) void topk_hist_kernel(const float *__restrict__ scores, int64_t ld,
-                                                        const int32_t *__restrict__ n, int64_t chunk,
-                                                        uint32_t *__restrict__ hist0)
-{
-    __shared__ uint32_t h[kBins0];
-    const int t = blockIdx.y;
-    const int64_t nt = n[t];
-    const int64_t s0 = (int64_t)blockIdx.x * chunk;
-    if (s0 >= nt)
-        return;
-    const int64_t s1 = min(nt, s0 + chunk);
-    for (int i = threadIdx.x; i < kBins0; i += 256)
-        h[i] = 0;
-    __syncthreads();
-    const float *row = scores + (int64_t)t * ld;
-    for (int64_t i = s0 + (int64_t)threadIdx.x * 4; i < s1; i += 256 * 4) {
-        if (i + 3 < s1) {
-            const float4 v = *reinterpret_cast<const float4 *>(row + i);
-            atomicAdd(&h[ord_key(v.x) >> 21], 1u);
-            atomicAdd(&h[ord_key(v.y) >> 21], 1u);
-            atomicAdd(&h[ord_key(v.z) >> 21], 1u);
-            atomicAdd(&h[ord_key(v.w) >> 21], 1u);
-        } else {
-            for (int64_t e = i; e < s1; ++e)
-                atomicAdd(&h[ord_key(row[e]) >> 21], 1u);
-        }
-    }
-    __syncthreads();
-    uint32_t *g = hist0 + ((int64_t)t * kHistCopies + (blockIdx.x % kHistCopies)) * kBins0;
-    for (int i = threadIdx.x; i < kBins0; i += 256)
-        if (h[i])
-            atomicAdd(&g[i], h[i]);
-}
-
 // ---- split path -------------------------------------------------------------
-// First digit from the query's histogram copies, read from the top bin down
-// NT bins at a time (the threshold sits in the highest bins, so one round
-// usually suffices). Falls back to digit 0 (everything survives) if the
-// counts never reach `need`.
+// The row's sample for the bound: blocks of kSplitSampleBlock consecutive
+// scores, one every G blocks, G = ceil(n / kSplitSamples): the whole row when
+// n <= kSplitSamples, otherwise between kSplitSamples / 2 and kSplitSamples
+// scores spread over all of it.
+constexpr int kSplitSampleBlock = 32;
+constexpr int kSplitSamples = 4096;
+static_assert(kSplitSamples % (kSplitThreads * 4) == 0, "whole groups of four samples per thread");
+static_assert(kSplitSampleBlock % 4 == 0, "groups of four stay inside a sampled block");
+
+// Two-digit key bound that at least k keys of the row reach with high
+// probability: the bound of the key whose rank among the samples is 1.5 times
+// the k-th largest key's expected rank, plus 16 (the finishing workgroup
+// checks the count). 0 (every key) when the sample is too small for that.
 template <int NT>
-__device__ void find_digit0_topdown(Shared &sh, const uint32_t *h, uint32_t need, uint32_t &digit, uint32_t &above)
+__device__ uint32_t split_bound(const float *row, int64_t n, int32_t k, Shared &sh)
 {
-    uint32_t run = 0;
-    digit = 0;
-    above = 0;
-    for (int top = kBins0; top > 0; top -= NT) {
-        const int b = top - 1 - (int)threadIdx.x;          // thread 0 takes the highest bin
-        uint32_t c = 0;
-        if (b >= 0) {
+    constexpr int G = kSplitSamples / (NT * 4);     // groups of four samples per thread
+    const int64_t sb = (n + kSplitSamples - 1) / kSplitSamples * kSplitSampleBlock;   // block spacing
+    const RowSrc src{row, n};
+    uint32_t key[G][4];
+    int64_t pos[G][4];
+    bool ok[G][4];
 #pragma unroll
-            for (int cp = 0; cp < kHistCopies; ++cp)
-                c += h[cp * kBins0 + b];
-        }
-        uint32_t tot;
-        const uint32_t incl = block_scan<NT>(c, sh.waves, &tot);
-        if (run + tot >= need) {                           // uniform: the bin is in this round
-            if (b >= 0 && run + incl - c < need && run + incl >= need) {
-                sh.digit = (uint32_t)b;
-                sh.above = run + incl - c;
-            }
-            __syncthreads();
-            digit = sh.digit;
-            above = sh.above;
-            __syncthreads();
-            return;
-        }
-        run += tot;
+    for (int g = 0; g < G; ++g) {
+        const int64_t s = ((int64_t)threadIdx.x + (int64_t)NT * g) * 4;     // first sample slot
+        src.get4(s / kSplitSampleBlock * sb + s % kSplitSampleBlock, key[g], pos[g], ok[g]);
     }
+    for (int i = threadIdx.x; i < kBins0; i += NT)
+        sh.hist[i] = 0;
+    __syncthreads();
+    uint32_t mine = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            mine += ok[g][e];
+            hist_add_wave(sh.hist, key[g][e] >> 21, ok[g][e]);
+        }
+    uint32_t ns;
+    block_scan<NT>(mine, sh.waves, &ns);          // its barriers also close the histogram
+    const uint64_t tgt = ((uint64_t)k * ns * 3 + (uint64_t)n * 2 - 1) / ((uint64_t)n * 2) + 16;
+    if (tgt > ns)
+        return 0u;
+    uint32_t b, above;
+    find_digit<NT>(sh, kBins0, (uint32_t)tgt, b, above);
+    for (int i = threadIdx.x; i < kBins0; i += NT)
+        sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (ok[g][e] && (key[g][e] >> 21) == b)
+                atomicAdd(&sh.hist[(key[g][e] >> 10) & (kBins0 - 1)], 1u);
+    __syncthreads();
+    uint32_t d1, above1;
+    find_digit<NT>(sh, kBins0, (uint32_t)tgt - above, d1, above1);
+    return (b << 21) | (d1 << 10);
 }
 
-// Phase 1. grid: (P, T); block: 256; kSplitChunk scores per workgroup. Copies
-// the chunk's survivors (first digit >= the threshold digit), in position
-// order, into the workgroup's slice of `regions`, and their count to counts;
-// adds the second-digit histogram of its threshold-bin keys to hist1.
-__global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
-    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
-    const uint32_t *__restrict__ hist0, uint32_t *__restrict__ hist1, uint32_t *__restrict__ counts,
-    uint64_t *__restrict__ regions, uint32_t *__restrict__ digit0)
+// Phase 1. grid: (P, T); block: kSplitThreads; kSplitChunk scores per
+// workgroup. Every workgroup of a query derives the same bound from the same
+// sample, then copies its chunk's keys at or above it, in position order,
+// into its slice of `regions`, and their count to counts; workgroup 0
+// publishes the bound.
+__global__ __launch_bounds__(kSplitThreads) void topk_collect_kernel(const float *__restrict__ scores, int64_t ld,
+                                                                     const int32_t *__restrict__ n, int32_t k,
+                                                                     uint32_t *__restrict__ counts,
+                                                                     uint64_t *__restrict__ regions,
+                                                                     uint32_t *__restrict__ bounds)
 {
+    constexpr int NT = kSplitThreads;
     __shared__ Shared sh;
     const int t = blockIdx.y;
     const int w = blockIdx.x;
@@ -451,7 +527,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
     if (nt <= k)
         return;                                   // the finish kernel keeps everything
     const float *row = scores + (int64_t)t * ld;
-    // this chunk's scores, issued before the histogram is read
+    // this chunk's scores, issued before the sample
     const int64_t s = (int64_t)w * kSplitChunk + (int64_t)tid * 4 * kSplitRuns;
     uint32_t key[kSplitRuns][4];
     int64_t pos[kSplitRuns][4];
@@ -459,24 +535,17 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
 #pragma unroll
     for (int r = 0; r < kSplitRuns; ++r)
         RowSrc{row, nt}.get4(s + 4 * r, key[r], pos[r], ok[r]);
-    for (int i = tid; i < kBins0; i += kSplitThreads)
-        sh.hist[i] = 0;
-
-    uint32_t d0, above0;
-    find_digit0_topdown<kSplitThreads>(sh, hist0 + (int64_t)t * kHistCopies * kBins0, (uint32_t)k, d0, above0);
+    const uint32_t bound = split_bound<NT>(row, nt, k, sh);
     uint32_t ls = 0;
 #pragma unroll
     for (int r = 0; r < kSplitRuns; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool sv = ok[r][e] && (key[r][e] >> 21) >= d0;
-            ls += sv;
-            if (ok[r][e] && (key[r][e] >> 21) == d0)
-                atomicAdd(&sh.hist[(key[r][e] >> 10) & (kBins0 - 1)], 1u);
-            ok[r][e] = sv;
+            ok[r][e] = ok[r][e] && key[r][e] >= bound;
+            ls += ok[r][e];
         }
     uint32_t tot;
-    uint32_t o = block_scan<kSplitThreads>(ls, sh.waves, &tot) - ls;   // its barriers also close the histogram
+    uint32_t o = block_scan<NT>(ls, sh.waves, &tot) - ls;
     uint64_t *reg = regions + ((int64_t)t * P + w) * kSplitChunk;
 #pragma unroll
     for (int r = 0; r < kSplitRuns; ++r)
@@ -484,150 +553,154 @@ __global__ __launch_bounds__(kSplitThreads) void topk_survivors_kernel(
         for (int e = 0; e < 4; ++e)
             if (ok[r][e])
                 reg[o++] = ((uint64_t)key[r][e] << 32) | (uint32_t)pos[r][e];
-    uint32_t *h1 = hist1 + (int64_t)t * kBins0;
-    for (int i = tid; i < kBins0; i += kSplitThreads)
-        if (sh.hist[i])
-            atomicAdd(&h1[i], sh.hist[i]);
     if (tid == 0) {
         counts[(int64_t)t * P + w] = tot;
-        if (w == 0) {                             // every workgroup found the same digit
-            digit0[2 * t] = d0;
-            digit0[2 * t + 1] = above0;
-        }
+        if (w == 0)
+            bounds[t] = bound;                    // every workgroup found the same bound
     }
 }
 
-// Phase 2. grid: T; block: kFinishThreads. The second digit comes from hist1;
-// the survivors of all P slices at or above the two-digit bound (about k of
-// them) are gathered in slice order (= position order) into LDS, and the last
-// digit finishes the selection. Zeroes the query's histograms.
+// Phase 2. grid: T; block: kFinishThreads. The first C = min(kSpec * NT / P,
+// kSplitChunk) entries of every slice are loaded together with the slice
+// counts, before these are known (one round trip, instead of a second one
+// once the counts are scanned). Each key is stored at its rank in the LDS
+// list (slice order = position order), slices longer than C adding the rest.
+// If at least k keys reached the bound, the k-th largest key and all its ties
+// are among them and the three digits finish from the list; with fewer, or
+// more than the list holds, they finish from the whole row. Zeroes the
+// first-digit histograms when given. The kernel reads back none of its
+// global stores, so its barriers order LDS traffic only.
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
-    int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, uint32_t *__restrict__ hist1,
-    const uint32_t *__restrict__ counts, const uint64_t *__restrict__ regions, int32_t P,
-    const uint32_t *__restrict__ digit0)
+    int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, const uint32_t *__restrict__ counts,
+    const uint64_t *__restrict__ regions, int32_t P, const uint32_t *__restrict__ bounds)
 {
     constexpr int NT = kFinishThreads;
+    constexpr bool LB = true;
     __shared__ Shared sh;
-    __shared__ uint64_t list[kListCap];
+    __shared__ __align__(16) uint64_t list[kListCap];
     __shared__ uint32_t offs[kMaxSplit + 1];
-    __shared__ uint32_t wave_cnt[kFinishThreads / 64];
+    __shared__ uint32_t long_slice;
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t nt = n[t];
     int32_t *out = idx + (int64_t)t * k;
-    uint32_t *h0 = hist0 + (int64_t)t * kHistCopies * kBins0;
-    uint32_t *h1 = hist1 + (int64_t)t * kBins0;
+    uint32_t *h0 = hist0 ? hist0 + (int64_t)t * kHistCopies * kBins0 : nullptr;
     if (nt <= k) {
-        zero_hist0<NT>(h0);                       // no reader of this query's copies remains
-        write_all<NT>(out, nt, k);                // hist1 was not touched for this query
+        if (h0)
+            zero_hist0<NT>(h0);
+        write_all<NT>(out, nt, k);
         return;
     }
-    // the second-digit histogram, the slice counts and the first digit are
-    // all loaded at once (one round trip), then the first-digit copies cleared
-    static_assert(kBins0 % NT == 0 && kMaxSplit <= NT, "one pass over bins and slices");
-    uint32_t hv[kBins0 / NT];
-#pragma unroll
-    for (int i = 0; i < kBins0 / NT; ++i)
-        hv[i] = h1[tid + i * NT];
+    // loads first (slice counts, slice prefixes), then the stores that clear
+    // the histograms
+    static_assert(kMaxSplit <= NT, "one scan over the slices");
+    static_assert((NT * kSpec) / kMaxSplit >= 1 && kSplitChunk <= 8192 && NT * kSpec <= 8192,
+                  "C >= 1; slice and entry fit 13 bits each");
     const uint32_t c0 = tid < P ? counts[(int64_t)t * P + tid] : 0u;
-    const uint32_t d0 = digit0[2 * t], above0 = digit0[2 * t + 1];
-    zero_hist0<NT>(h0);                           // no reader of this query's copies remains
-    const uint32_t need0 = (uint32_t)k - above0;
-    // second digit over the first-digit bin
+    const uint32_t bound = bounds[t];
+    const uint64_t *reg_t = regions + (int64_t)t * P * kSplitChunk;
+    const uint32_t C = min((uint32_t)(NT * kSpec) / (uint32_t)P, (uint32_t)kSplitChunk);
+    uint64_t sv[kSpec];
+    uint32_t slot[kSpec];                         // slice << 13 | entry
 #pragma unroll
-    for (int i = 0; i < kBins0 / NT; ++i) {
-        sh.hist[tid + i * NT] = hv[i];
-        h1[tid + i * NT] = 0;
+    for (int e = 0; e < kSpec; ++e) {
+        const uint32_t f = (uint32_t)tid + (uint32_t)NT * e;
+        const uint32_t sl = f / C, j = f - sl * C;
+        slot[e] = (sl << 13) | j;
+        sv[e] = sl < (uint32_t)P ? reg_t[(int64_t)sl * kSplitChunk + j] : 0ull;
     }
-    __syncthreads();
-    uint32_t d1, above1;
-    find_digit<NT>(sh, kBins0, need0, d1, above1);
-    const uint32_t bound = (d0 << 21) | (d1 << 10);
+    if (h0)
+        zero_hist0<NT>(h0);
     // slice offsets (P <= NT: one scan)
+    if (tid == 0)
+        long_slice = 0;
+    wg_barrier<LB>();
+    if (tid < P && c0 > C)
+        long_slice = 1;
     uint32_t total;
-    const uint32_t excl = block_scan<NT>(c0, sh.waves, &total) - c0;
+    const uint32_t excl = block_scan<NT, LB>(c0, sh.waves, &total) - c0;
     if (tid < P)
         offs[tid] = excl;
     if (tid == 0)
         offs[P] = total;
-    __syncthreads();
-    // Gather, in slice order (= position order), only the survivors at or
-    // above the two-digit bound: about k of them, plus the ties of the bound's
-    // bin. Per round each wave takes a contiguous segment, its lanes
-    // interleaved so that one load covers 512 contiguous bytes of a slice; a
-    // lane finds the slice of its first entry by binary search, then walks
-    // forward with the next slice's offset in a register. All loads of a round
-    // are in flight before the compaction: ballot prefix counts inside the
-    // wave, then one exchange of the 16 wave counts.
-    constexpr int NW = NT / 64;
-    const int wv = tid >> 6, lane = tid & 63;
-    const uint64_t *reg_t = regions + (int64_t)t * P * kSplitChunk;
-    uint32_t cnt = 0;
-    for (uint32_t r0 = 0; r0 < total; r0 += (uint32_t)NT * kGatherPer) {
-        const uint32_t part = min(total - r0, (uint32_t)NT * kGatherPer);
-        const uint32_t seg = (part + NW - 1) / NW;            // <= 64 * kGatherPer
-        const uint32_t s0 = r0 + (uint32_t)wv * seg;
-        const uint32_t s1 = min(s0 + seg, r0 + part);
-        const uint32_t x0 = s0 + (uint32_t)lane;
-        int lo = 0;
-        if (x0 < s1) {
-            int hi = P;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (offs[mid] <= x0)
-                    lo = mid;
-                else
-                    hi = mid;
-            }
-        }
-        uint32_t next = offs[lo + 1];
-        uint64_t v[kGatherPer];
-#pragma unroll
-        for (int e = 0; e < kGatherPer; ++e) {
-            const uint32_t x = x0 + 64u * e;
-            v[e] = 0;
-            if (x < s1) {
-                while (next <= x) {               // offs[P] = total > x ends the walk
-                    ++lo;
-                    next = offs[lo + 1];
-                }
-                v[e] = reg_t[(int64_t)lo * kSplitChunk + (x - offs[lo])];
-            }
-        }
-        uint32_t loc[kGatherPer];
-        bool keep[kGatherPer];
-        uint32_t wcount = 0;
-#pragma unroll
-        for (int e = 0; e < kGatherPer; ++e) {
-            keep[e] = x0 + 64u * e < s1 && (uint32_t)(v[e] >> 32) >= bound;
-            const uint64_t m = __ballot(keep[e]);
-            loc[e] = wcount + (uint32_t)__popcll(m & __lanemask_lt());
-            wcount += (uint32_t)__popcll(m);
-        }
-        if (lane == 0)
-            wave_cnt[wv] = wcount;
-        __syncthreads();
-        uint32_t woff = 0, tot = 0;
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            const uint32_t c = wave_cnt[j];
-            woff += j < wv ? c : 0u;
-            tot += c;
-        }
-#pragma unroll
-        for (int e = 0; e < kGatherPer; ++e) {
-            const uint32_t o = cnt + woff + loc[e];
-            if (keep[e] && o < (uint32_t)kListCap)
-                list[o] = v[e];
-        }
-        cnt += tot;
-        __syncthreads();                          // wave_cnt is rewritten next round
+    wg_barrier<LB>();
+    if (total < (uint32_t)k || total > (uint32_t)kListCap) {
+        finish_select<NT, LB>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 0, 0u, 0u, (uint32_t)k, k, out);
+        return;
     }
-    if (cnt <= (uint32_t)kListCap)
-        finish_select<NT>(ListSrc{list, cnt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
-    else                                          // more than kListCap keys share the top two digits
-        finish_select<NT>(RowSrc{scores + (int64_t)t * ld, nt}, sh, 2, bound, 0xFFFFFC00u, need0 - above1, k, out);
+#pragma unroll
+    for (int e = 0; e < kSpec; ++e) {
+        const uint32_t sl = slot[e] >> 13, j = slot[e] & 0x1FFFu;
+        if (sl < (uint32_t)P) {
+            const uint32_t o = offs[sl];
+            if (j < offs[sl + 1] - o)
+                list[o + j] = sv[e];
+        }
+    }
+    if (long_slice) {
+        // the entries past C of the longer slices, by rank among them; their
+        // offsets go to sh.hist, free until the first digit
+        const uint32_t rem = tid < P && c0 > C ? c0 - C : 0u;
+        uint32_t rtot;
+        const uint32_t rex = block_scan<NT, LB>(rem, sh.waves, &rtot) - rem;
+        if (tid < P)
+            sh.hist[tid] = rex;
+        wg_barrier<LB>();
+        for (uint32_t r0 = 0; r0 < rtot; r0 += (uint32_t)NT * 4) {
+            uint64_t v[4];
+            uint32_t dst[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t r = r0 + (uint32_t)tid + (uint32_t)NT * u;
+                dst[u] = 0xFFFFFFFFu;
+                if (r < rtot) {
+                    int lo = 0, hi = P;                   // last slice whose rest starts at or before r
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (sh.hist[mid] <= r)
+                            lo = mid;
+                        else
+                            hi = mid;
+                    }
+                    const uint32_t j = C + (r - sh.hist[lo]);
+                    dst[u] = offs[lo] + j;
+                    v[u] = reg_t[(int64_t)lo * kSplitChunk + j];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (dst[u] != 0xFFFFFFFFu)
+                    list[dst[u]] = v[u];
+        }
+    }
+    wg_barrier<LB>();
+    // The listed keys' top 22 bits, less the bound's, rarely span 2048 bins:
+    // one histogram of that difference (the last bin taking everything from
+    // 2047 up) gives the k-th key's two leading digits, unless it lands in
+    // the last bin; then the digits run from the first.
+    const ListSrc src{list, total};
+    const uint32_t b22 = bound >> 10;
+    for (int i = tid; i < kBins0; i += NT)
+        sh.hist[i] = 0;
+    wg_barrier<LB>();
+    for_each_key<NT>(src, [&](uint32_t key, bool ok) {
+        if (ok)
+            atomicAdd(&sh.hist[min((key >> 10) - b22, (uint32_t)kBins0 - 1)], 1u);
+    });
+    wg_barrier<LB>();
+    uint32_t rel, above;
+    find_digit<NT, LB>(sh, kBins0, (uint32_t)k, rel, above);
+    const uint32_t in_bin = sh.count;
+    const uint32_t pre = (b22 + rel) << 10;
+    if (rel == (uint32_t)kBins0 - 1)
+        finish_select<NT, LB>(src, sh, 0, 0u, 0u, (uint32_t)k, k, out);
+    else if (in_bin == (uint32_t)k - above && pre != 0u)
+        // every key of the k-th key's bin is kept: the selection is the keys
+        // at or above the bin's lowest key, no last digit needed
+        finish_select<NT, LB>(src, sh, 3, pre - 1u, 0xFFFFFFFFu, 0u, k, out);
+    else
+        finish_select<NT, LB>(src, sh, 2, pre, 0xFFFFFC00u, (uint32_t)k - above, k, out);
 }
 
 // ---- row path ---------------------------------------------------------------
@@ -705,7 +778,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
                                                                uint64_t *__restrict__ surv)
 {
     __shared__ Shared sh;
-    __shared__ uint64_t list[kRowListCap];
+    __shared__ __align__(16) uint64_t list[kRowListCap];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t nt = n[t];
@@ -772,7 +845,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
 struct TopkLayout {
     bool split;
     int64_t P;
-    size_t hist_off, hist1_off, counts_off, digit_off, regions_off, total;
+    size_t hist_off, counts_off, bounds_off, regions_off, total;
 };
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -786,14 +859,12 @@ TopkLayout topk_layout(int32_t T, int64_t max_n)
     // split when the queries alone cannot fill the chip and the survivor
     // slices stay small
     L.split = T < 256 && (int64_t)T * L.P * kSplitChunk <= ((int64_t)1 << 26) && L.P <= kMaxSplit;
-    // counters that start and end at zero: first-digit histogram copies and
-    // the second-digit histogram of the split path
+    // first-digit histogram copies (counters that start and end at zero)
     L.hist_off = 0;
-    L.hist1_off = up256((size_t)T * kHistCopies * kBins0 * 4);
-    L.counts_off = L.hist1_off + up256((size_t)T * kBins0 * 4);
+    L.counts_off = up256((size_t)T * kHistCopies * kBins0 * 4);
     if (L.split) {
-        L.digit_off = L.counts_off + up256((size_t)T * L.P * 4);
-        L.regions_off = L.digit_off + up256((size_t)T * 8);
+        L.bounds_off = L.counts_off + up256((size_t)T * L.P * 4);
+        L.regions_off = L.bounds_off + up256((size_t)T * 4);
         L.total = L.regions_off + up256((size_t)T * L.P * kSplitChunk * 8);
     } else {
         L.regions_off = L.counts_off;
@@ -808,6 +879,8 @@ size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t) { return topk_lay
 
 uint32_t *topk_hist0(void *ws) { return reinterpret_cast<uint32_t *>(ws); }
 
+bool topk_reads_hist0(int32_t T, int64_t max_n) { return !topk_layout(T, max_n).split; }
+
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n, int32_t k,
                        int32_t *idx, void *ws, bool hist_ready, hipStream_t stream)
 {
@@ -819,23 +892,15 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
     if (L.split) {
         uint32_t *counts = reinterpret_cast<uint32_t *>(base + L.counts_off);
         uint64_t *regions = reinterpret_cast<uint64_t *>(base + L.regions_off);
-        if (!hist_ready && max_n > 0) {
-            const int64_t chunk = 8192;
-            hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)((max_n + chunk - 1) / chunk), (unsigned)T),
-                               dim3(256), 0, stream, scores, ld, n, chunk, hist0);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess)
-                return e;
-        }
-        uint32_t *digit0 = reinterpret_cast<uint32_t *>(base + L.digit_off);
-        uint32_t *hist1 = reinterpret_cast<uint32_t *>(base + L.hist1_off);
-        hipLaunchKernelGGL(topk_survivors_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0,
-                           stream, scores, ld, n, k, hist0, hist1, counts, regions, digit0);
+        uint32_t *bounds = reinterpret_cast<uint32_t *>(base + L.bounds_off);
+        hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream,
+                           scores, ld, n, k, counts, regions, bounds);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
+        // histograms filled by the producer are not needed here; they are cleared
         hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kFinishThreads), 0, stream, scores, ld, n,
-                           k, idx, hist0, hist1, counts, regions, (int32_t)L.P, digit0);
+                           k, idx, hist_ready ? hist0 : nullptr, counts, regions, (int32_t)L.P, bounds);
     } else {
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
                            hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));

@@ -140,6 +140,27 @@ def topk_case(name):
         s = np.full((256, 66000), 7.0, np.float32)
         s[:, 5::997] = 8.0
         return s, n, 2048
+    # split path, every slice holding more keys at or above the bound than the
+    # finishing workgroup loads ahead of the counts (four values, so the bound
+    # keeps half the row: 1024 of 2048 per slice), all of them together still
+    # fitting its list; the second row is ragged
+    if name == "long_slices_split":
+        n = np.array([32768, 30001], np.int32)
+        return rng.integers(0, 4, size=(2, 32768)).astype(np.float32), n, 5000
+    # split path, the sampled positions (32 of every 1024) hold the largest
+    # scores: fewer than k keys reach the sampled bound and the selection
+    # finishes from the whole row
+    if name == "sampled_split_fallback":
+        n = np.array([131072], np.int32)
+        s = rng.integers(0, 1000, size=(1, 131072)).astype(np.float32)
+        s[:, (np.arange(131072) % 1024) < 32] = 1000.0
+        return s, n, 8192
+    # split path, the winners clustered in the first two slices
+    if name == "clustered_split":
+        n = np.array([131072], np.int32)
+        s = rng.standard_normal((1, 131072)).astype(np.float32)
+        s[0, 100:3100] += 10.0
+        return s, n, 2048
     if name == "all_equal_row":
         n = np.full(260, 9000, np.int32)
         s = np.full((260, 9000), 7.0, np.float32)
@@ -173,7 +194,8 @@ def test_topk_workspace_reuse(gpu, orc):
 
 @pytest.mark.parametrize("name", ["ties_int", "ties_pm1", "normal", "signed_zero", "edges", "k1",
                                   "dense_bin_split", "dense_bin_row", "all_equal_split", "all_equal_row",
-                                  "sampled_row", "sampled_row_fallback", "sampled_all_equal_row"])
+                                  "sampled_row", "sampled_row_fallback", "sampled_all_equal_row",
+                                  "long_slices_split", "clustered_split", "sampled_split_fallback"])
 def test_topk_exact(gpu, orc, name):
     s, n, k = topk_case(name)
     T, L = s.shape
