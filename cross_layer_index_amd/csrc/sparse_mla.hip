@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
     const float *__restrict__ sink, float scale_log2,
     int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
-    float *__restrict__ part_o, float *__restrict__ part_ml)
+    uint16_t *__restrict__ part_o, float *__restrict__ part_ml)
 {
     using G = MlaGeom<DQK, DV>;
     using TG = TileGeom<DQK, DV>;
@@ -489,30 +489,52 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             }
         }
     } else {
+        // The split's partial, normalised by its own denominator: a convex
+        // combination of value rows, stored as fp16 (2^-11 relative, finer
+        // than the bf16 output). Values are scaled by 2^-e per (head, half),
+        // e > 0 only when the half's largest magnitude reaches 2^14, so that
+        // none leaves the fp16 range; (m, l, e_half0, e_half1) go beside it.
         const int64_t prow = ((int64_t)t * splits + split) * H;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+            const float l = __shfl(l_run, 4 * g + r);   // O rows are heads 4*g + r
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            float mx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NTH; ++i)
+                mx = fmaxf(mx, fabsf(o[i][r] * inv));
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1)      // over the 16 lanes of the row group
+                mx = fmaxf(mx, __shfl_xor(mx, off));
+            const int e = mx >= 16384.0f ? ilogbf(mx) - 13 : 0;
+            const float scl = ldexpf(inv, -e);
             const int h = h0 + 4 * g + r;
             if (h >= H)
                 continue;
 #pragma unroll
             for (int i = 0; i < NTH; ++i)
-                part_o[(prow + h) * DV + 16 * (nt0 + i) + c] = o[i][r];
+                part_o[(prow + h) * DV + 16 * (nt0 + i) + c] =
+                    __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl));
+            if (c == 0)
+                part_ml[(prow + h) * 4 + 2 + half] = (float)e;
         }
         if (half == 0 && g == 0 && hc < H) {
-            part_ml[(prow + hc) * 2 + 0] = m_run;
-            part_ml[(prow + hc) * 2 + 1] = l_run;
+            part_ml[(prow + hc) * 4 + 0] = m_run;
+            part_ml[(prow + hc) * 4 + 1] = l_run;
         }
     }
 }
 
-// grid: (H, T); block: DV/4 threads, one float4 of value columns each.
-// Merges the per-split partials and adds the sink.
+// grid: (H, T); block: DV/4 threads, four value columns each. Merges the
+// per-split partials (fp16, normalised by the split's own denominator and
+// scaled by 2^-e) and adds the sink:
+//   out = sum_s 2^(m_s - m) l_s 2^e_s p_s / (2^(sink - m) + sum_s 2^(m_s - m) l_s)
 constexpr int kMaxSplits = 256;
 constexpr int kCombineBatch = 16;           // partial loads in flight per thread
+constexpr int64_t kResidentWGs = 256;       // one per CU (the tile ring's LDS)
 
 template <int DV>
-__global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__restrict__ part_o,
+__global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__restrict__ part_o,
                                                              const float *__restrict__ part_ml,
                                                              const float *__restrict__ sink, int32_t H,
                                                              int32_t splits, void *__restrict__ out,
@@ -520,18 +542,19 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
 {
     constexpr int NT = DV / 4;
     constexpr int NW = (NT + 63) / 64;
-    __shared__ float wgt[kMaxSplits];
+    __shared__ float wgt[2][kMaxSplits];        // per half of the value columns
     __shared__ float red[2][NW];
     const int h = blockIdx.x;
     const int t = blockIdx.y;
     const int tid = threadIdx.x;
+    const int hf = 4 * tid >= DV / 2;           // the half this thread's columns lie in
     const float ms = sink[h] * kLog2e;
     const int64_t pr0 = (int64_t)t * splits * H + h;          // row of split 0
     // this thread's four columns of the first kCombineBatch splits: they do
     // not depend on the weights, so they travel with the (m, l) loads
-    const float4 *p = reinterpret_cast<const float4 *>(part_o + pr0 * DV) + tid;
-    const int64_t stride = (int64_t)H * DV / 4;               // float4s between splits
-    float4 x[kCombineBatch];
+    const uint2 *p = reinterpret_cast<const uint2 *>(part_o + pr0 * DV) + tid;
+    const int64_t stride = (int64_t)H * DV / 4;               // uint2s between splits
+    uint2 x[kCombineBatch];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u)
         if (u < splits)
@@ -539,7 +562,7 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
     // global maximum over the sink and the partial maxima
     float m = tid == 0 ? ms : -INFINITY;
     for (int s = tid; s < splits; s += NT)
-        m = fmaxf(m, part_ml[(pr0 + (int64_t)s * H) * 2]);
+        m = fmaxf(m, part_ml[(pr0 + (int64_t)s * H) * 4]);
     // butterfly over the active lanes of a wave (a block of DV/4 < 64 threads
     // fills only part of one)
     constexpr int kFirstOff = (NT < 64 ? NT : 64) / 2;
@@ -556,10 +579,11 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
     // per-split weights and the denominator
     float dsum = tid == 0 ? exp2f(ms - m) : 0.0f;
     for (int s = tid; s < splits; s += NT) {
-        const int64_t pr = pr0 + (int64_t)s * H;
-        const float wv = exp2f(part_ml[pr * 2] - m);
-        wgt[s] = wv;
-        dsum += part_ml[pr * 2 + 1] * wv;
+        const float4 ml = *reinterpret_cast<const float4 *>(part_ml + (pr0 + (int64_t)s * H) * 4);
+        const float wl = exp2f(ml.x - m) * ml.y;
+        wgt[0][s] = ldexpf(wl, (int)ml.z);
+        wgt[1][s] = ldexpf(wl, (int)ml.w);
+        dsum += wl;
     }
 #pragma unroll
     for (int off = kFirstOff; off > 0; off >>= 1)
@@ -573,6 +597,7 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
         den += red[1][i];
     const float inv = 1.0f / den;
     // every split's columns, kCombineBatch loads in flight
+    auto h2f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
         if (s0 > 0) {
@@ -584,11 +609,11 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const float *__rest
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u)
             if (s0 + u < splits) {
-                const float wv = wgt[s0 + u];
-                acc.x = fmaf(x[u].x, wv, acc.x);
-                acc.y = fmaf(x[u].y, wv, acc.y);
-                acc.z = fmaf(x[u].z, wv, acc.z);
-                acc.w = fmaf(x[u].w, wv, acc.w);
+                const float wv = wgt[hf][s0 + u];
+                acc.x = fmaf(h2f(x[u].x & 0xFFFFu), wv, acc.x);
+                acc.y = fmaf(h2f(x[u].x >> 16), wv, acc.y);
+                acc.z = fmaf(h2f(x[u].y & 0xFFFFu), wv, acc.z);
+                acc.w = fmaf(h2f(x[u].y >> 16), wv, acc.w);
             }
     }
     const int64_t oi = ((int64_t)t * H + h) * DV + 4 * tid;
@@ -608,10 +633,11 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
                         int32_t out_f32, const MlaPlan &plan, void *ws, hipStream_t stream)
 {
     const int hg = (H + kHeadsPerWG - 1) / kHeadsPerWG;
-    float *part_o = nullptr, *part_ml = nullptr;
+    uint16_t *part_o = nullptr;
+    float *part_ml = nullptr;
     if (plan.splits > 1) {
-        part_o = reinterpret_cast<float *>(ws);
-        part_ml = part_o + (size_t)T * plan.splits * H * DV;
+        part_o = reinterpret_cast<uint16_t *>(ws);
+        part_ml = reinterpret_cast<float *>(part_o + (size_t)T * plan.splits * H * DV);
     }
     hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
                        q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
@@ -645,6 +671,13 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     s = s < 1 ? 1 : s;
     if (s < (k + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit)
         s = (k + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit;
+    // a small grid takes twice the splits (two tiles each at least) while
+    // they still fit on the chip at once (one workgroup per CU): shorter
+    // tile loops outweigh the larger partials there, not once a second
+    // round of workgroups is needed
+    const int64_t max_splits2 = (k + 2 * kTile - 1) / (2 * kTile);
+    if (base_wgs * 2 * s <= kResidentWGs && 2 * s <= max_splits2 && 2 * s <= kMaxSplits)
+        s *= 2;
     int64_t rps = (k + s - 1) / s;
     rps = (rps + kTile - 1) / kTile * kTile;
     s = (k + rps - 1) / rps;
@@ -652,7 +685,7 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
         s = 1;
     p.splits = (int32_t)s;
     p.rows_per_split = (int32_t)rps;
-    p.ws_bytes = s > 1 ? (size_t)T * s * H * (D_v + 2) * sizeof(float) : 0;
+    p.ws_bytes = s > 1 ? (size_t)T * s * H * ((size_t)D_v * 2 + 4 * sizeof(float)) : 0;
     return p;
 }
 

@@ -252,6 +252,28 @@ def test_sparse_mla_close(gpu, orc, name, out_f32):
     assert np.all(got[idx.max(1) < 0] == 0)                                      # empty rows are zero
 
 
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_sparse_mla_large_values(gpu, orc, out_f32):
+    """Latent rows scaled by 1e5 (and q by 1e-5, so the scores stay as they
+    were): the split partials, stored in fp16 with a per-(head, half)
+    power-of-two scale, must stay in range; the error bound scales with the
+    values."""
+    wl, idx = mla_case("decode_split")
+    li = W.layer_inputs(wl, 0, with_indexer=False)
+    big = 1.0e5
+    kv = (li.kv.float() * big).to(torch.bfloat16)
+    q = (li.q.float() / big).to(torch.bfloat16)
+    qs = qs_of(gpu, wl)
+    got = gpu.sparse_mla(q.cuda(), kv.cuda(), qs, torch.from_numpy(idx).cuda(), li.sink.cuda(), wl.scale, wl.D_v,
+                         out_f32=out_f32).float().cpu().numpy()
+    ref = orc.sparse_mla(q, kv, wl.base(), idx, li.sink, wl.scale, wl.D_v)
+    assert np.isfinite(got).all()
+    assert np.abs(ref).max() > 16384.0                                          # the scaled range is in use
+    tol = ATOL * big + (0.0 if out_f32 else half_ulp_bf16(ref))
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), f"max abs error {err.max()} (scaled tolerance {ATOL * big})"
+
+
 def test_sparse_mla_deterministic(gpu):
     wl, idx = mla_case("decode_split")
     d = dev(W.layer_inputs(wl, 0, with_indexer=False))
