@@ -533,6 +533,45 @@ constexpr int kMaxSplits = 256;
 constexpr int kCombineBatch = 16;           // partial loads in flight per thread
 constexpr int64_t kResidentWGs = 256;       // one per CU (the tile ring's LDS)
 
+// Max / sum over the first n lanes of a wave (n = 16 or 64), in registers
+// (DPP): row shifts by 1, 2, 4 and 8 reduce each row of 16 lanes into its last
+// lane, the row broadcasts carry rows 0 and 2 into rows 1 and 3 and row 1 into
+// rows 2 and 3; lane n-1 then holds the result, read back as a scalar.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v)
+{
+    constexpr int kNegInf = (int)0xFF800000u;   // lanes without a source take -inf
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), CTRL, ROWS, 0xf, false)));
+}
+
+template <int N>
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = dpp_max_step<0x111, 0xf>(v);            // row_shr:1
+    v = dpp_max_step<0x112, 0xf>(v);            // row_shr:2
+    v = dpp_max_step<0x114, 0xf>(v);            // row_shr:4
+    v = dpp_max_step<0x118, 0xf>(v);            // row_shr:8
+    if (N > 16) {
+        v = dpp_max_step<0x142, 0xa>(v);        // row_bcast:15 into rows 1 and 3
+        v = dpp_max_step<0x143, 0xc>(v);        // row_bcast:31 into rows 2 and 3
+    }
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), N - 1));
+}
+
+template <int N>
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    if (N > 16) {
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    }
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), N - 1));
+}
+
 template <int DV>
 __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__restrict__ part_o,
                                                              const float *__restrict__ part_ml,
@@ -541,14 +580,14 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
                                                              int32_t out_f32)
 {
     constexpr int NT = DV / 4;
-    constexpr int NW = (NT + 63) / 64;
+    constexpr int NL = NT < 64 ? NT : 64;       // lanes of the first wave
+    static_assert(NL == 16 || NL == 64, "one row or one full wave");
     __shared__ float wgt[2][kMaxSplits];        // per half of the value columns
-    __shared__ float red[2][NW];
+    __shared__ float inv_den;
     const int h = blockIdx.x;
     const int t = blockIdx.y;
     const int tid = threadIdx.x;
     const int hf = 4 * tid >= DV / 2;           // the half this thread's columns lie in
-    const float ms = sink[h] * kLog2e;
     const int64_t pr0 = (int64_t)t * splits * H + h;          // row of split 0
     // this thread's four columns of the first kCombineBatch splits: they do
     // not depend on the weights, so they travel with the (m, l) loads
@@ -559,43 +598,39 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
     for (int u = 0; u < kCombineBatch; ++u)
         if (u < splits)
             x[u] = p[(int64_t)u * stride];
-    // global maximum over the sink and the partial maxima
-    float m = tid == 0 ? ms : -INFINITY;
-    for (int s = tid; s < splits; s += NT)
-        m = fmaxf(m, part_ml[(pr0 + (int64_t)s * H) * 4]);
-    // butterfly over the active lanes of a wave (a block of DV/4 < 64 threads
-    // fills only part of one)
-    constexpr int kFirstOff = (NT < 64 ? NT : 64) / 2;
+    // the first wave: (m, l, e0, e1) of splits tid, tid + NL, ... in one
+    // round trip; the maximum over them and the sink, the weights into LDS,
+    // the denominator
+    if (tid < NL) {
+        constexpr int R = kMaxSplits / NL;
+        const float ms = sink[h] * kLog2e;
+        float4 ml[R];
+        float m = ms;
 #pragma unroll
-    for (int off = kFirstOff; off > 0; off >>= 1)
-        m = fmaxf(m, __shfl_xor(m, off));
-    if ((tid & 63) == 0)
-        red[0][tid >> 6] = m;
-    __syncthreads();
-    m = red[0][0];
+        for (int r = 0; r < R; ++r) {
+            const int s = tid + NL * r;
+            ml[r] = s < splits ? *reinterpret_cast<const float4 *>(part_ml + (pr0 + (int64_t)s * H) * 4)
+                               : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+            m = fmaxf(m, ml[r].x);
+        }
+        m = wave_max<NL>(m);
+        float d = tid == 0 ? exp2f(ms - m) : 0.0f;
 #pragma unroll
-    for (int i = 1; i < NW; ++i)
-        m = fmaxf(m, red[0][i]);
-    // per-split weights and the denominator
-    float dsum = tid == 0 ? exp2f(ms - m) : 0.0f;
-    for (int s = tid; s < splits; s += NT) {
-        const float4 ml = *reinterpret_cast<const float4 *>(part_ml + (pr0 + (int64_t)s * H) * 4);
-        const float wl = exp2f(ml.x - m) * ml.y;
-        wgt[0][s] = ldexpf(wl, (int)ml.z);
-        wgt[1][s] = ldexpf(wl, (int)ml.w);
-        dsum += wl;
+        for (int r = 0; r < R; ++r) {
+            const int s = tid + NL * r;
+            if (s < splits) {
+                const float wl = exp2f(ml[r].x - m) * ml[r].y;
+                wgt[0][s] = ldexpf(wl, (int)ml[r].z);
+                wgt[1][s] = ldexpf(wl, (int)ml[r].w);
+                d += wl;
+            }
+        }
+        d = wave_sum<NL>(d);
+        if (tid == 0)
+            inv_den = 1.0f / d;
     }
-#pragma unroll
-    for (int off = kFirstOff; off > 0; off >>= 1)
-        dsum += __shfl_xor(dsum, off);
-    if ((tid & 63) == 0)
-        red[1][tid >> 6] = dsum;
     __syncthreads();
-    float den = red[1][0];
-#pragma unroll
-    for (int i = 1; i < NW; ++i)
-        den += red[1][i];
-    const float inv = 1.0f / den;
+    const float inv = inv_den;
     // every split's columns, kCombineBatch loads in flight
     auto h2f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
