@@ -455,24 +455,42 @@ constexpr int kSplitSamples = 4096;
 static_assert(kSplitSamples % (kSplitThreads * 4) == 0, "whole groups of four samples per thread");
 static_assert(kSplitSampleBlock % 4 == 0, "groups of four stay inside a sampled block");
 
+// The sample's slots of this thread: geometry from `n_geo` (the longest row of
+// the call, known before the row's own length arrives), loads bounded by the
+// row's capacity `cap`; split_bound masks them by the row's length.
+template <int NT>
+struct SplitSample {
+    static constexpr int G = kSplitSamples / (NT * 4);     // groups of four samples per thread
+    uint32_t key[G][4];
+    int64_t pos[G][4];
+    bool ok[G][4];
+    __device__ void load(const float *row, int64_t cap, int64_t n_geo)
+    {
+        const int64_t sb = (n_geo + kSplitSamples - 1) / kSplitSamples * kSplitSampleBlock;   // block spacing
+        const RowSrc src{row, cap};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int64_t s = ((int64_t)threadIdx.x + (int64_t)NT * g) * 4;     // first sample slot
+            src.get4(s / kSplitSampleBlock * sb + s % kSplitSampleBlock, key[g], pos[g], ok[g]);
+        }
+    }
+};
+
 // Two-digit key bound that at least k keys of the row reach with high
 // probability: the bound of the key whose rank among the samples is 1.5 times
 // the k-th largest key's expected rank, plus 16 (the finishing workgroup
 // checks the count). 0 (every key) when the sample is too small for that.
 template <int NT>
-__device__ uint32_t split_bound(const float *row, int64_t n, int32_t k, Shared &sh)
+__device__ uint32_t split_bound(SplitSample<NT> &sp, int64_t n, int32_t k, Shared &sh)
 {
-    constexpr int G = kSplitSamples / (NT * 4);     // groups of four samples per thread
-    const int64_t sb = (n + kSplitSamples - 1) / kSplitSamples * kSplitSampleBlock;   // block spacing
-    const RowSrc src{row, n};
-    uint32_t key[G][4];
-    int64_t pos[G][4];
-    bool ok[G][4];
+    constexpr int G = SplitSample<NT>::G;
+    auto &key = sp.key;
+    auto &ok = sp.ok;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int64_t s = ((int64_t)threadIdx.x + (int64_t)NT * g) * 4;     // first sample slot
-        src.get4(s / kSplitSampleBlock * sb + s % kSplitSampleBlock, key[g], pos[g], ok[g]);
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            ok[g][e] = ok[g][e] && sp.pos[g][e] < n;
     for (int i = threadIdx.x; i < kBins0; i += NT)
         sh.hist[i] = 0;
     __syncthreads();
@@ -512,8 +530,8 @@ __device__ uint32_t split_bound(const float *row, int64_t n, int32_t k, Shared &
 // into its slice of `regions`, and their count to counts; workgroup 0
 // publishes the bound.
 __global__ __launch_bounds__(kSplitThreads) void topk_collect_kernel(const float *__restrict__ scores, int64_t ld,
-                                                                     const int32_t *__restrict__ n, int32_t k,
-                                                                     uint32_t *__restrict__ counts,
+                                                                     const int32_t *__restrict__ n, int64_t max_n,
+                                                                     int32_t k, uint32_t *__restrict__ counts,
                                                                      uint64_t *__restrict__ regions,
                                                                      uint32_t *__restrict__ bounds)
 {
@@ -523,25 +541,29 @@ __global__ __launch_bounds__(kSplitThreads) void topk_collect_kernel(const float
     const int w = blockIdx.x;
     const int P = gridDim.x;
     const int tid = threadIdx.x;
-    const int64_t nt = n[t];
-    if (nt <= k)
-        return;                                   // the finish kernel keeps everything
     const float *row = scores + (int64_t)t * ld;
-    // this chunk's scores, issued before the sample
+    // this chunk's scores and the sample, issued before the row's length
+    // arrives (loads stay inside the row's capacity ld; positions at or past
+    // the length are dropped once it is known)
     const int64_t s = (int64_t)w * kSplitChunk + (int64_t)tid * 4 * kSplitRuns;
     uint32_t key[kSplitRuns][4];
     int64_t pos[kSplitRuns][4];
     bool ok[kSplitRuns][4];
 #pragma unroll
     for (int r = 0; r < kSplitRuns; ++r)
-        RowSrc{row, nt}.get4(s + 4 * r, key[r], pos[r], ok[r]);
-    const uint32_t bound = split_bound<NT>(row, nt, k, sh);
+        RowSrc{row, ld}.get4(s + 4 * r, key[r], pos[r], ok[r]);
+    SplitSample<NT> sp;
+    sp.load(row, ld, max_n);
+    const int64_t nt = n[t];
+    if (nt <= k)
+        return;                                   // the finish kernel keeps everything
+    const uint32_t bound = split_bound<NT>(sp, nt, k, sh);
     uint32_t ls = 0;
 #pragma unroll
     for (int r = 0; r < kSplitRuns; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            ok[r][e] = ok[r][e] && key[r][e] >= bound;
+            ok[r][e] = ok[r][e] && pos[r][e] < nt && key[r][e] >= bound;
             ls += ok[r][e];
         }
     uint32_t tot;
@@ -583,17 +605,11 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     __shared__ uint32_t long_slice;
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
-    const int64_t nt = n[t];
     int32_t *out = idx + (int64_t)t * k;
     uint32_t *h0 = hist0 ? hist0 + (int64_t)t * kHistCopies * kBins0 : nullptr;
-    if (nt <= k) {
-        if (h0)
-            zero_hist0<NT>(h0);
-        write_all<NT>(out, nt, k);
-        return;
-    }
-    // loads first (slice counts, slice prefixes), then the stores that clear
-    // the histograms
+    // loads first (slice counts, slice prefixes: inside the workspace whatever
+    // the row's length, which they do not wait for), then the stores that
+    // clear the histograms
     static_assert(kMaxSplit <= NT, "one scan over the slices");
     static_assert((NT * kSpec) / kMaxSplit >= 1 && kSplitChunk <= 8192 && NT * kSpec <= 8192,
                   "C >= 1; slice and entry fit 13 bits each");
@@ -609,6 +625,13 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
         const uint32_t sl = f / C, j = f - sl * C;
         slot[e] = (sl << 13) | j;
         sv[e] = sl < (uint32_t)P ? reg_t[(int64_t)sl * kSplitChunk + j] : 0ull;
+    }
+    const int64_t nt = n[t];
+    if (nt <= k) {
+        if (h0)
+            zero_hist0<NT>(h0);
+        write_all<NT>(out, nt, k);
+        return;
     }
     if (h0)
         zero_hist0<NT>(h0);
@@ -894,7 +917,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
         uint64_t *regions = reinterpret_cast<uint64_t *>(base + L.regions_off);
         uint32_t *bounds = reinterpret_cast<uint32_t *>(base + L.bounds_off);
         hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream,
-                           scores, ld, n, k, counts, regions, bounds);
+                           scores, ld, n, max_n, k, counts, regions, bounds);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
