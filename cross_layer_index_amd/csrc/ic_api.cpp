@@ -451,9 +451,17 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
     std::vector<int32_t> slot(n_layers, -1);
     int32_t next_slot = 0;
     const size_t slot_elems = (size_t)qs->T * d->k;
+    // When the top-k takes its split path and the MLA grid fits on the chip at
+    // once, a full layer's MLA workgroups finish the selection themselves
+    // from the split phase's collected keys (one launch and one round trip
+    // fewer) and write the layer's index list for the shared layers.
+    ic::TopkSplitView view{};
+    const bool selecting = qs->max_n > 0 && ic::topk_split_view(topk_ws, qs->T, qs->max_n, &view) &&
+                           ic::sparse_mla_selecting_supported(plan, qs->T, d->H, view);
     for (int32_t l = 0; l < n_layers; ++l) {
         const ic_layer &y = layers[l];
-        if (reuse_map[l] == l) {
+        const bool full = reuse_map[l] == l;
+        if (full) {
             slot[l] = next_slot++;
             int32_t *idx = index_cache + slot[l] * slot_elems;
             // the per-query key stream also fills the top-k's first-digit
@@ -466,14 +474,21 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
                 if (e != hipSuccess)
                     return hip_status(e, "layer stack: indexer launch");
             }
-            hipError_t e = ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx, topk_ws,
-                                           fused_hist, st);
+            hipError_t e = selecting ? ic::launch_topk_collect(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k,
+                                                               topk_ws, st)
+                                     : ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx,
+                                                       topk_ws, fused_hist, st);
             if (e != hipSuccess)
                 return hip_status(e, "layer stack: top-k launch");
         }
-        const int32_t *idx = index_cache + slot[reuse_map[l]] * slot_elems;
-        hipError_t e = ic::launch_sparse_mla(y.q, y.kv, qs->base, qs->n_valid, idx, qs->T, d->H, d->k, d->D_qk, d->D_v, y.sink,
-                                             scale, y.out, d->out_dtype == IC_OUT_F32, plan, mla_ws, st);
+        int32_t *idx = index_cache + slot[reuse_map[l]] * slot_elems;
+        const int32_t f32 = d->out_dtype == IC_OUT_F32;
+        hipError_t e = full && selecting
+                           ? ic::launch_sparse_mla_selecting(y.q, y.kv, qs->base, qs->n_valid, qs->T, d->H, d->k,
+                                                             d->D_qk, d->D_v, y.sink, scale, y.out, f32, plan, mla_ws,
+                                                             scores, L.ld, view, idx, st)
+                           : ic::launch_sparse_mla(y.q, y.kv, qs->base, qs->n_valid, idx, qs->T, d->H, d->k, d->D_qk,
+                                                   d->D_v, y.sink, scale, y.out, f32, plan, mla_ws, st);
         if (e != hipSuccess)
             return hip_status(e, "layer stack: sparse MLA launch");
     }

@@ -39,6 +39,21 @@ bool topk_reads_hist0(int32_t T, int64_t max_n);
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
                        int32_t k, int32_t *idx, void *ws, bool hist_ready, hipStream_t stream);
 
+// Split path in two launches around a consumer that selects itself: the
+// first phase (the collected keys at or above a sampled bound, per query, in
+// position-ordered slices) and where it leaves them in the workspace.
+struct TopkSplitView {
+    const uint32_t *counts;   // [T][P] keys per slice
+    const uint64_t *regions;  // [T][P][stride] (key << 32 | position)
+    const uint32_t *bounds;   // [T] key bound
+    int32_t P;
+    int64_t stride;
+};
+// false when this shape takes the row path (no split phase to share)
+bool topk_split_view(void *ws, int32_t T, int64_t max_n, TopkSplitView *v);
+hipError_t launch_topk_collect(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
+                               int32_t k, void *ws, hipStream_t stream);
+
 // ---- sparse MLA -----------------------------------------------------------
 struct MlaPlan {
     int32_t splits;          // k-splits per (query, head group)
@@ -51,6 +66,17 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_
                              const int32_t *n_valid, const int32_t *idx, int32_t T, int32_t H, int32_t k, int32_t D_qk,
                              int32_t D_v, const float *sink, float scale, void *out, int32_t out_f32,
                              const MlaPlan &plan, void *ws, hipStream_t stream);
+
+// Sparse MLA whose workgroups select their own rows from the split phase's
+// collected keys (each the slots of its split; workgroups of head group 0
+// also write the query's index list to idx_out [T, k]). Only for grids that
+// fit on the chip at once.
+bool sparse_mla_selecting_supported(const MlaPlan &plan, int32_t T, int32_t H, const TopkSplitView &v);
+hipError_t launch_sparse_mla_selecting(const uint16_t *q, const uint16_t *kv, const int64_t *base,
+                                       const int32_t *n_valid, int32_t T, int32_t H, int32_t k, int32_t D_qk,
+                                       int32_t D_v, const float *sink, float scale, void *out, int32_t out_f32,
+                                       const MlaPlan &plan, void *ws, const float *scores, int64_t ld,
+                                       const TopkSplitView &v, int32_t *idx_out, hipStream_t stream);
 
 // Gated head output: out = sigmoid(gate) * (wv_b @ o) per head.
 bool gated_output_supported(int32_t D_v, int32_t D_o);

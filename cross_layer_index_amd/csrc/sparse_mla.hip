@@ -27,6 +27,7 @@
 // unnormalised partial (m, l, o) and a combine kernel merges them and adds the
 // sink once.
 #include "kernels.h"
+#include "select.h"
 
 namespace ic {
 namespace {
@@ -159,13 +160,23 @@ __device__ __forceinline__ void wait_vmcnt()
 // partner wave's through LDS), then PV over its half of the 512 value dims.
 // Halving the q fragments and the O accumulators per wave lets two waves share
 // each SIMD, which hides LDS latency.
-template <int DQK, int DV>
+// The selection fused into the kernel (SEL): the split phase's view, the
+// score rows (for the whole-row fallback) and the index list to write.
+struct SelArgs {
+    TopkSplitView v;
+    const float *scores;
+    int64_t ld;
+    int32_t *idx_out;
+};
+constexpr int kSelPerThread = 16;           // collected keys per thread (512 threads: 8192 per query)
+
+template <int DQK, int DV, bool SEL>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const int64_t *__restrict__ base,
     const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
     const float *__restrict__ sink, float scale_log2,
     int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_ml)
+    uint16_t *__restrict__ part_o, float *__restrict__ part_ml, const SelArgs sa)
 {
     using G = MlaGeom<DQK, DV>;
     using TG = TileGeom<DQK, DV>;
@@ -222,13 +233,24 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     // the split's index list in LDS, padded with empty slots to whole tiles;
     // an entry outside [0, n_valid[t]) counts as empty (it never addresses memory)
     const int padded = (nrows + kTile - 1) / kTile * kTile;
+    // with SEL, the split phase's loads go out first: this thread's slice
+    // count, the bound and its share of the collected keys
+    uint32_t sel_c0 = 0, sel_bound = 0;
+    SplitSel<kMlaThreads, kSelPerThread> sel;
+    if constexpr (SEL) {
+        sel_c0 = tid < sa.v.P ? sa.v.counts[(int64_t)t * sa.v.P + tid] : 0u;
+        sel_bound = sa.v.bounds[t];
+        sel.load(sa.v.regions + (int64_t)t * sa.v.P * sa.v.stride, sa.v.stride, sa.v.P);
+    }
     const int32_t nt = n_valid[t];
     int any_valid = 0;
-    for (int i = tid; i < padded; i += kMlaThreads) {
-        int r = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
-        r = (r >= 0 && r < nt) ? r : -1;
-        rowid[i] = r;
-        any_valid |= r >= 0;
+    if constexpr (!SEL) {
+        for (int i = tid; i < padded; i += kMlaThreads) {
+            int r = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
+            r = (r >= 0 && r < nt) ? r : -1;
+            rowid[i] = r;
+            any_valid |= r >= 0;
+        }
     }
 
     // q fragments of this half: lane (head hc, group g) holds d = 32*ks + 8*g .. +8
@@ -254,7 +276,41 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     // empty one: zero output, or m = kMInit and l = 0). Otherwise the query
     // has at least one row, row 0 exists, and empty slots (and the spare
     // chunk of each LDS row) read row 0: finite data the math never uses.
-    const bool has_rows = __syncthreads_or(any_valid);
+    bool has_rows;
+    if constexpr (SEL) {
+        // this split's rows are the slots [j_begin, j_end) of the query's
+        // selection (position order); the selection's LDS (histograms, slice
+        // counts) borrows the score-exchange buffer, unused until the tile loop
+        Shared &sh = *reinterpret_cast<Shared *>(&sx[0][0][0][0]);
+        uint32_t *cnt = reinterpret_cast<uint32_t *>(&sh + 1);
+        int32_t *iout = hg == 0 && sa.idx_out ? sa.idx_out + (int64_t)t * k : nullptr;
+        if (nt <= k) {                            // every position, in order
+            for (int i = tid; i < padded; i += kMlaThreads) {
+                const int j = j_begin + i;
+                rowid[i] = i < nrows && j < nt ? j : -1;
+            }
+        } else {
+            for (int i = nrows + tid; i < padded; i += kMlaThreads)
+                rowid[i] = -1;
+            auto emit = [&](uint32_t slot, int32_t p) {
+                const uint32_t i = slot - (uint32_t)j_begin;
+                if (i < (uint32_t)nrows)
+                    rowid[i] = p;
+            };
+            sel.select(RowSrc{sa.scores + (int64_t)t * sa.ld, nt}, k, sel_c0, sel_bound, sa.v.P, sh, cnt,
+                       (uint32_t)j_begin, (uint32_t)j_end, emit);
+        }
+        __syncthreads();                          // rowid complete, sx free
+        // the slots of this split go to the layer's index list in one
+        // coalesced pass (stores per selected key would each cost a vector
+        // memory instruction for a handful of lanes)
+        if (iout)
+            for (int i = tid; i < nrows; i += kMlaThreads)
+                iout[j_begin + i] = rowid[i];
+        has_rows = nrows > 0 && j_begin < min(nt, k);
+    } else {
+        has_rows = __syncthreads_or(any_valid);
+    }
     // byte offset of each fill's 16-byte chunk within its row
     int fill_boff[kFillPerWave];
 #pragma unroll
@@ -661,11 +717,11 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
     }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool SEL>
 hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *base, const int32_t *n_valid,
                         const int32_t *idx,
                         int32_t T, int32_t H, int32_t k, const float *sink, float scale, void *out,
-                        int32_t out_f32, const MlaPlan &plan, void *ws, hipStream_t stream)
+                        int32_t out_f32, const MlaPlan &plan, void *ws, const SelArgs &sa, hipStream_t stream)
 {
     const int hg = (H + kHeadsPerWG - 1) / kHeadsPerWG;
     uint16_t *part_o = nullptr;
@@ -674,9 +730,9 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
         part_o = reinterpret_cast<uint16_t *>(ws);
         part_ml = reinterpret_cast<float *>(part_o + (size_t)T * plan.splits * H * DV);
     }
-    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
+    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
                        q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
-                       out_f32, part_o, part_ml);
+                       out_f32, part_o, part_ml, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
@@ -731,10 +787,37 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_
 {
     if (T == 0 || H == 0)
         return hipSuccess;
+    const SelArgs none{};
     if (D_qk == 576 && D_v == 512)
-        return launch_shape<576, 512>(q, kv, base, n_valid, idx, T, H, k, sink, scale, out, out_f32, plan, ws, stream);
+        return launch_shape<576, 512, false>(q, kv, base, n_valid, idx, T, H, k, sink, scale, out, out_f32, plan, ws,
+                                             none, stream);
     if (D_qk == 80 && D_v == 64)
-        return launch_shape<80, 64>(q, kv, base, n_valid, idx, T, H, k, sink, scale, out, out_f32, plan, ws, stream);
+        return launch_shape<80, 64, false>(q, kv, base, n_valid, idx, T, H, k, sink, scale, out, out_f32, plan, ws,
+                                           none, stream);
+    return hipErrorInvalidValue;
+}
+
+bool sparse_mla_selecting_supported(const MlaPlan &plan, int32_t T, int32_t H, const TopkSplitView &v)
+{
+    const int64_t wgs = (int64_t)plan.splits * ((H + kHeadsPerWG - 1) / kHeadsPerWG) * T;
+    return wgs <= kResidentWGs && v.P >= 1 && v.P <= kMlaThreads;
+}
+
+hipError_t launch_sparse_mla_selecting(const uint16_t *q, const uint16_t *kv, const int64_t *base,
+                                       const int32_t *n_valid, int32_t T, int32_t H, int32_t k, int32_t D_qk,
+                                       int32_t D_v, const float *sink, float scale, void *out, int32_t out_f32,
+                                       const MlaPlan &plan, void *ws, const float *scores, int64_t ld,
+                                       const TopkSplitView &v, int32_t *idx_out, hipStream_t stream)
+{
+    if (T == 0 || H == 0)
+        return hipSuccess;
+    const SelArgs sa{v, scores, ld, idx_out};
+    if (D_qk == 576 && D_v == 512)
+        return launch_shape<576, 512, true>(q, kv, base, n_valid, nullptr, T, H, k, sink, scale, out, out_f32, plan,
+                                            ws, sa, stream);
+    if (D_qk == 80 && D_v == 64)
+        return launch_shape<80, 64, true>(q, kv, base, n_valid, nullptr, T, H, k, sink, scale, out, out_f32, plan,
+                                          ws, sa, stream);
     return hipErrorInvalidValue;
 }
 

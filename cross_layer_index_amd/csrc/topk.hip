@@ -42,11 +42,11 @@
 // holds them zeroed on entry and the finishing workgroup zeroes them again.
 #include "kernels.h"
 #include "radix_key.h"
+#include "select.h"
 
 namespace ic {
 namespace {
 
-constexpr int kBins0 = kHistBins0;      // first digit: bits 31..21
 constexpr int kSplitThreads = 1024;
 constexpr int kSplitRuns = 2;                      // groups of 4 consecutive scores per survivors thread
 constexpr int kSplitChunk = kSplitThreads * 4 * kSplitRuns;   // scores per split workgroup
@@ -58,335 +58,6 @@ constexpr int kRowRuns = 2;             // consecutive groups of 4 scores per th
 constexpr int kMaxSplit = 1024;         // workgroups per query on the split path
 constexpr int kSpec = 8;                // slice entries per finishing thread loaded ahead of the counts
 constexpr int kRowSurvCap = 32768;      // survivors kept in global memory per query (row path)
-
-// Workgroup barrier. The full form is __syncthreads, whose release fence
-// also waits for every global store and load in flight; the LDS form (this
-// wave's LDS operations complete, then s_barrier) orders LDS traffic only and
-// serves kernels that read back none of their own global stores. The memory
-// clobber keeps the compiler from moving memory operations across it.
-template <bool LdsOnly>
-__device__ __forceinline__ void wg_barrier()
-{
-    if constexpr (LdsOnly)
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-        __syncthreads();
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave, in registers (DPP): row
-// shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then the last lane of row
-// 0 is added to row 1 and that of row 2 to row 3, and the last lane of row 1
-// to rows 2 and 3. Lanes without a source add 0.
-__device__ __forceinline__ uint32_t wave_scan(uint32_t v)
-{
-    int x = (int)v;
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
-    return (uint32_t)x;
-}
-
-// Block-wide inclusive scan of one uint32 per thread.
-template <int NT, bool LB = false>
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *lds_waves, uint32_t *total)
-{
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    v = wave_scan(v);
-    if (lane == 63)
-        lds_waves[wave] = v;
-    wg_barrier<LB>();
-    if (wave == 0) {
-        const uint32_t x = wave_scan(lane < NW ? lds_waves[lane] : 0u);
-        if (lane < NW)
-            lds_waves[lane] = x;
-    }
-    wg_barrier<LB>();
-    const uint32_t before = wave ? lds_waves[wave - 1] : 0u;
-    if (total)
-        *total = lds_waves[NW - 1];
-    wg_barrier<LB>();
-    return v + before;
-}
-
-struct Shared {
-    uint32_t hist[kBins0];
-    uint32_t waves[16];
-    uint32_t digit, above, count;
-};
-
-// Given a histogram of `nb` (1024 or 2048) bins in LDS, complete before the
-// call, find the digit of the bin holding the need-th largest key; returns it
-// with the count of keys in higher bins (and, in sh.count, the bin's own
-// count). One wave scans: lane l owns nb/64
-// consecutive bins, lane 0 the highest; a wave prefix sum of their totals
-// names the lane whose range holds the need-th key, and a second one over
-// that range, one bin per lane from the top, names the bin. One barrier
-// publishes the result (a barrier before the next call separates these reads
-// from its writes). Digit 0 and 0 when the counts never reach `need`.
-template <int NT, bool LB = false>
-__device__ __forceinline__ void find_digit(Shared &sh, int nb, uint32_t need, uint32_t &digit, uint32_t &above)
-{
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const int per = nb >> 6;                       // bins per lane: 32 or 16
-        const int quads = per >> 2;
-        const uint4 *h4 = reinterpret_cast<const uint4 *>(&sh.hist[nb - (lane + 1) * per]);
-        uint32_t local = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < quads) {
-                const uint4 c = h4[j];
-                local += c.x + c.y + c.z + c.w;
-            }
-        const uint32_t incl = wave_scan(local);
-        const uint64_t hit = __ballot(incl - local < need && incl >= need);
-        if (hit == 0) {
-            if (lane == 0) {
-                sh.digit = 0;
-                sh.above = 0;
-                sh.count = 0;
-            }
-        } else {
-            const int L = __builtin_ctzll(hit);
-            const uint32_t run = __builtin_amdgcn_readlane(incl - local, L);
-            const int b = nb - L * per - 1 - lane;     // lane i takes the range's i-th bin from the top
-            const uint32_t x = lane < per ? sh.hist[b] : 0u;
-            const uint32_t in2 = run + wave_scan(x);
-            if (lane < per && in2 - x < need && in2 >= need) {
-                sh.digit = (uint32_t)b;
-                sh.above = in2 - x;
-                sh.count = x;
-            }
-        }
-    }
-    wg_barrier<LB>();
-    digit = sh.digit;
-    above = sh.above;
-}
-
-// Key sources: a row of fp32 scores (position = index) or an LDS list of
-// (key << 32 | position) entries in position order.
-struct RowSrc {
-    static constexpr bool kLds = false;
-    const float *row;
-    int64_t n;
-    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
-    {
-        if (i + 3 < n) {
-            const float4 v = *reinterpret_cast<const float4 *>(row + i);
-            key[0] = ord_key(v.x), key[1] = ord_key(v.y), key[2] = ord_key(v.z), key[3] = ord_key(v.w);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                pos[e] = i + e, ok[e] = true;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ok[e] = i + e < n;
-                key[e] = ok[e] ? ord_key(row[i + e]) : 0u;
-                pos[e] = i + e;
-            }
-        }
-    }
-};
-
-struct ListSrc {
-    static constexpr bool kLds = true;
-    const uint64_t *list;                          // 16-byte aligned
-    int64_t n;
-    // i is a multiple of 4: two 16-byte reads
-    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
-    {
-        uint64_t v[4] = {0ull, 0ull, 0ull, 0ull};
-        if (i + 3 < n) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(list + i);
-            const uint4 b = *reinterpret_cast<const uint4 *>(list + i + 2);
-            v[0] = a.x | ((uint64_t)a.y << 32), v[1] = a.z | ((uint64_t)a.w << 32);
-            v[2] = b.x | ((uint64_t)b.y << 32), v[3] = b.z | ((uint64_t)b.w << 32);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (i + e < n)
-                    v[e] = list[i + e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ok[e] = i + e < n;
-            key[e] = (uint32_t)(v[e] >> 32);
-            pos[e] = (int64_t)(uint32_t)v[e];
-        }
-    }
-};
-
-// A contiguous (key << 32 | position) list in global memory, position order.
-struct GListSrc {
-    static constexpr bool kLds = false;
-    const uint64_t *list;
-    int64_t n;
-    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
-    {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ok[e] = i + e < n;
-            const uint64_t v = ok[e] ? list[i + e] : 0ull;
-            key[e] = (uint32_t)(v >> 32);
-            pos[e] = (int64_t)(uint32_t)v;
-        }
-    }
-};
-
-// Calls f(key, live) once for every entry of `src`, in no particular order,
-// with every lane of the wave taking part in each call (f may use ballots).
-// An LDS list is read interleaved (lane i takes entry i, i + NT, ...), which
-// keeps the lanes of one read on distinct banks; other sources are read four
-// consecutive entries per thread.
-template <int NT, class Src, class F>
-__device__ __forceinline__ void for_each_key(const Src &src, F f)
-{
-    if constexpr (Src::kLds) {
-        for (int64_t i0 = 0; i0 < src.n; i0 += (int64_t)NT * 4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t i = i0 + threadIdx.x + (int64_t)NT * e;
-                const bool ok = i < src.n;
-                const uint64_t v = ok ? src.list[i] : 0ull;
-                f((uint32_t)(v >> 32), ok);
-            }
-        }
-    } else {
-        for (int64_t i = (int64_t)threadIdx.x * 4; i < src.n; i += (int64_t)NT * 4) {
-            uint32_t key[4];
-            int64_t pos[4];
-            bool ok[4];
-            src.get4(i, key, pos, ok);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                f(key[e], ok[e]);
-        }
-    }
-}
-
-// Ordered compaction of the entries with key >= bound into an LDS list (the
-// first lcap) and, if given, a global list (the first gcap). Returns the count.
-// A thread takes R groups of 4 consecutive entries per round (all their loads
-// in flight before the round's one scan).
-template <int NT, int R = 1, class Src>
-__device__ uint32_t collect(const Src &src, uint32_t bound, Shared &sh, uint64_t *lds, uint32_t lcap,
-                            uint64_t *glist, uint32_t gcap)
-{
-    uint32_t total = 0;
-    for (int64_t c0 = 0; c0 < src.n; c0 += (int64_t)NT * 4 * R) {
-        uint32_t key[R][4];
-        int64_t pos[R][4];
-        bool ok[R][4];
-        const int64_t i0 = c0 + (int64_t)threadIdx.x * 4 * R;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            src.get4(i0 + 4 * r, key[r], pos[r], ok[r]);
-        uint32_t ls = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ok[r][e] = ok[r][e] && key[r][e] >= bound;
-                ls += ok[r][e];
-            }
-        uint32_t tot;
-        uint32_t o = total + block_scan<NT>(ls, sh.waves, &tot) - ls;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (ok[r][e]) {
-                    const uint64_t v = ((uint64_t)key[r][e] << 32) | (uint32_t)pos[r][e];
-                    if (o < lcap)
-                        lds[o] = v;
-                    if (glist && o < gcap)
-                        glist[o] = v;
-                    ++o;
-                }
-            }
-        total += tot;
-    }
-    __syncthreads();
-    return total;
-}
-
-// Digit passes `first`..2 over `src` (none when first is 3: then `prefix` is
-// the threshold key itself), then the ordered compaction into out[0..k).
-template <int NT, bool LB = false, class Src>
-__device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t prefix, uint32_t pmask,
-                              uint32_t need, int32_t k, int32_t *__restrict__ out)
-{
-    const int tid = threadIdx.x;
-    for (int pass = first; pass < 3; ++pass) {
-        const int shf = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nb = pass == 2 ? 1024 : 2048;
-        for (int i = tid; i < nb; i += NT)
-            sh.hist[i] = 0;
-        wg_barrier<LB>();
-        // first digits crowd into a few bins (aggregated adds); later ones
-        // spread out (plain adds)
-        for_each_key<NT>(src, [&](uint32_t key, bool ok) {
-            const bool live = ok && (key & pmask) == prefix;
-            const uint32_t b = (key >> shf) & (nb - 1);
-            if (pass == 0)
-                hist_add_wave(sh.hist, b, live);
-            else if (live)
-                atomicAdd(&sh.hist[b], 1u);
-        });
-        wg_barrier<LB>();
-        uint32_t digit, above;
-        find_digit<NT, LB>(sh, nb, need, digit, above);
-        prefix |= digit << shf;
-        pmask |= (uint32_t)(nb - 1) << shf;
-        need -= above;
-    }
-    const uint32_t thr = prefix;
-    uint32_t run_gt = 0, run_eq = 0;
-    for (int64_t c0 = 0; c0 < src.n; c0 += (int64_t)NT * 4) {
-        uint32_t key[4];
-        int64_t pos[4];
-        bool ok[4];
-        src.get4(c0 + (int64_t)tid * 4, key, pos, ok);
-        uint32_t gt[4], eq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            gt[e] = ok[e] && key[e] > thr;
-            eq[e] = ok[e] && key[e] == thr;
-        }
-        const uint32_t lg = gt[0] + gt[1] + gt[2] + gt[3];
-        const uint32_t le = eq[0] + eq[1] + eq[2] + eq[3];
-        uint32_t tot;
-        const uint32_t incl = block_scan<NT, LB>(lg | (le << 16), sh.waves, &tot);
-        const uint32_t excl = incl - (lg | (le << 16));
-        uint32_t gb = run_gt + (excl & 0xFFFFu);
-        uint32_t eb = run_eq + (excl >> 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // slots are < k by construction; the check keeps any inconsistent
-            // input (NaN scores) from writing outside the row
-            if (gt[e]) {
-                const uint32_t slot = gb + min(eb, need);
-                if (slot < (uint32_t)k)
-                    out[slot] = (int32_t)pos[e];
-            } else if (eq[e] && eb < need) {
-                if (gb + eb < (uint32_t)k)
-                    out[gb + eb] = (int32_t)pos[e];
-            }
-            gb += gt[e];
-            eb += eq[e];
-        }
-        run_gt += tot & 0xFFFFu;
-        run_eq += tot >> 16;
-        if (run_gt + min(run_eq, need) >= (uint32_t)k)
-            break;
-    }
-}
 
 // Finish from a survivor list `src` (keys with first digit >= d0, position
 // order, `total` entries) that does not fit the LDS list: histogram the second
@@ -903,6 +574,36 @@ size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t) { return topk_lay
 uint32_t *topk_hist0(void *ws) { return reinterpret_cast<uint32_t *>(ws); }
 
 bool topk_reads_hist0(int32_t T, int64_t max_n) { return !topk_layout(T, max_n).split; }
+
+bool topk_split_view(void *ws, int32_t T, int64_t max_n, TopkSplitView *v)
+{
+    const TopkLayout L = topk_layout(T, max_n);
+    if (!L.split)
+        return false;
+    char *base = static_cast<char *>(ws);
+    v->counts = reinterpret_cast<const uint32_t *>(base + L.counts_off);
+    v->regions = reinterpret_cast<const uint64_t *>(base + L.regions_off);
+    v->bounds = reinterpret_cast<const uint32_t *>(base + L.bounds_off);
+    v->P = (int32_t)L.P;
+    v->stride = kSplitChunk;
+    return true;
+}
+
+hipError_t launch_topk_collect(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
+                               int32_t k, void *ws, hipStream_t stream)
+{
+    const TopkLayout L = topk_layout(T, max_n);
+    if (T == 0)
+        return hipSuccess;
+    if (!L.split)
+        return hipErrorInvalidValue;
+    char *base = static_cast<char *>(ws);
+    hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream, scores,
+                       ld, n, max_n, k, reinterpret_cast<uint32_t *>(base + L.counts_off),
+                       reinterpret_cast<uint64_t *>(base + L.regions_off),
+                       reinterpret_cast<uint32_t *>(base + L.bounds_off));
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n, int32_t k,
                        int32_t *idx, void *ws, bool hist_ready, hipStream_t stream)

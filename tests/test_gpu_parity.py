@@ -342,10 +342,15 @@ def run_stack(ic, wl, layers_dev, rmap, out_f32=False):
     return outs, cache, passes
 
 
-@pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer"])
+@pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer", "ties_3layer"])
 def test_layer_stack_small(gpu, orc, case):
     if case == "tiny":
         wl = W.WORKLOADS["tiny_2layer"]
+    elif case == "ties_3layer":
+        # every key row equal: a query's scores all tie, every key reaches the
+        # bound and the lowest positions win (past 8192 keys the selection
+        # runs over the whole row; at 5000 the ties resolve from the list)
+        wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=3, full_layers=[0, 2], T=3, lengths=[20000, 5000, 2049])
     elif case == "small_5layer":
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=5, full_layers=[0, 3], T=3, lengths=[3000, 2048, 100])
     elif case == "every6_13layer":
@@ -355,6 +360,9 @@ def test_layer_stack_small(gpu, orc, case):
     else:
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=4, full_layers=[0], T=2, k=64, lengths=[300, 50], H=8)
     host = [W.layer_inputs(wl, l) for l in range(wl.n_layers)]
+    if case == "ties_3layer":
+        for x in host:
+            x.k_idx.copy_(x.k_idx[0:1].expand_as(x.k_idx))
     rmap = gpu.reuse_map_last_full(wl.is_full())
     outs, cache, passes = run_stack(gpu, wl, [dev(x) for x in host], rmap, out_f32=True)
     base, n = wl.base().numpy(), wl.n_valid().numpy()
