@@ -342,10 +342,18 @@ def run_stack(ic, wl, layers_dev, rmap, out_f32=False):
     return outs, cache, passes
 
 
-@pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer", "ties_3layer"])
+@pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer", "ties_3layer",
+                                  "clustered_2layer"])
 def test_layer_stack_small(gpu, orc, case):
     if case == "tiny":
         wl = W.WORKLOADS["tiny_2layer"]
+    elif case == "clustered_2layer":
+        # key rows 0..4999 all equal to +-8 along the weighted sum of the
+        # query's heads: those positions tie above every other score and all
+        # fall in the first chunk of the split path, more than a workgroup's
+        # share of one slice when the sparse MLA selects its own rows (then
+        # the selection runs over the whole row)
+        wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=2, full_layers=[0], T=1, lengths=[20000])
     elif case == "ties_3layer":
         # every key row equal: a query's scores all tie, every key reaches the
         # bound and the lowest positions win (past 8192 keys the selection
@@ -363,6 +371,10 @@ def test_layer_stack_small(gpu, orc, case):
     if case == "ties_3layer":
         for x in host:
             x.k_idx.copy_(x.k_idx[0:1].expand_as(x.k_idx))
+    if case == "clustered_2layer":
+        for x in host:
+            v = (x.w[0, :, None].double() * x.q_idx[0].view(torch.float8_e4m3fn).double()).sum(0)
+            x.k_idx[:5000] = torch.where(v >= 0, 0x50, 0xD0).to(torch.uint8)    # e4m3fn codes of +8, -8
     rmap = gpu.reuse_map_last_full(wl.is_full())
     outs, cache, passes = run_stack(gpu, wl, [dev(x) for x in host], rmap, out_f32=True)
     base, n = wl.base().numpy(), wl.n_valid().numpy()
