@@ -86,7 +86,7 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxThreads = kIdxWaves * 64;
 constexpr int kIdxUnroll = 2;                                  // 32-token groups per wave step
 constexpr int kIdxStep = kIdxWaves * 32 * kIdxUnroll;          // tokens per WG step
-constexpr int kIdxMaxChunk = 1024;                             // tokens per WG, upper bound
+constexpr int kIdxMaxChunk = 512;                              // tokens per WG, upper bound
 constexpr int64_t kIdxResident = 2 * 256;                      // resident WGs: 2 per CU x 256 CUs
 
 // One wave step's key fragments: kIdxUnroll groups of 32 tokens, each lane

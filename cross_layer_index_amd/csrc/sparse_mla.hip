@@ -762,6 +762,14 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     s = s < 1 ? 1 : s;
     if (s < (k + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit)
         s = (k + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit;
+    // a grid that needs two rounds of workgroups takes one round instead
+    // while its splits stay within 16 tiles (one round pays the prologue and
+    // epilogue once per CU and lets the layer stack select rows inside it)
+    if (base_wgs * s > kResidentWGs && base_wgs <= kResidentWGs) {
+        const int64_t s1 = kResidentWGs / base_wgs;
+        if (s1 >= 1 && (k + s1 - 1) / s1 <= 16 * kTile)
+            s = s1;
+    }
     // a small grid takes twice the splits (two tiles each at least) while
     // they still fit on the chip at once (one workgroup per CU): shorter
     // tile loops outweigh the larger partials there, not once a second
