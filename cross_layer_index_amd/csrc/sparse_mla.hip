@@ -551,17 +551,31 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // e > 0 only when the half's largest magnitude reaches 2^14, so that
         // none leaves the fp16 range; (m, l, e_half0, e_half1) go beside it.
         const int64_t prow = ((int64_t)t * splits + split) * H;
+        float inv4[4], mx4[4];
+        bool big = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float l = __shfl(l_run, 4 * g + r);   // O rows are heads 4*g + r
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            inv4[r] = l > 0.0f ? 1.0f / l : 0.0f;
             float mx = 0.0f;
 #pragma unroll
             for (int i = 0; i < NTH; ++i)
-                mx = fmaxf(mx, fabsf(o[i][r] * inv));
+                mx = fmaxf(mx, fabsf(o[i][r] * inv4[r]));
+            mx4[r] = mx;
+            big |= !(mx < 16384.0f);
+        }
+        // the maximum over the row group's 16 lanes only where some value of
+        // the wave reaches the scaled range (otherwise every e is 0)
+        const bool any_big = __any(big);
 #pragma unroll
-            for (int off = 8; off > 0; off >>= 1)      // over the 16 lanes of the row group
-                mx = fmaxf(mx, __shfl_xor(mx, off));
+        for (int r = 0; r < 4; ++r) {
+            const float inv = inv4[r];
+            float mx = mx4[r];
+            if (any_big) {
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1)  // over the 16 lanes of the row group
+                    mx = fmaxf(mx, __shfl_xor(mx, off));
+            }
             const int e = mx >= 16384.0f ? ilogbf(mx) - 13 : 0;
             const float scl = ldexpf(inv, -e);
             const int h = h0 + 4 * g + r;
