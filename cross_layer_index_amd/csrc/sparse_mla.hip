@@ -368,8 +368,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // both halves have KSH steps when KS is even (the 576-wide rows); an
         // odd KS leaves the second half one step short
         const int nks = (G::KS % 2 == 0) ? KSH : min(KSH, G::KS - ks0);
-        st0 = f4{0.f, 0.f, 0.f, 0.f};
-        st1 = f4{0.f, 0.f, 0.f, 0.f};
+        // even and odd K-steps accumulate separately: four independent
+        // matrix-instruction chains instead of two dependent ones
+        f4 acc[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+            acc[a][0] = acc[a][1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i0 = 0; i0 < KSH; i0 += kQkBatch) {
             uint4 fa[kQkBatch][2];
@@ -383,11 +387,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 #pragma unroll
             for (int i = 0; i < kQkBatch; ++i) {
                 if (i0 + i < nks) {
-                    st0 = mfma_bf16_16x16x32(as_bf16x8(fa[i][0]), qf[i0 + i], st0);
-                    st1 = mfma_bf16_16x16x32(as_bf16x8(fa[i][1]), qf[i0 + i], st1);
+                    f4(&c)[2] = acc[(i0 + i) & 1];
+                    c[0] = mfma_bf16_16x16x32(as_bf16x8(fa[i][0]), qf[i0 + i], c[0]);
+                    c[1] = mfma_bf16_16x16x32(as_bf16x8(fa[i][1]), qf[i0 + i], c[1]);
                 }
             }
         }
+        st0 = acc[0][0] + acc[1][0];
+        st1 = acc[0][1] + acc[1][1];
     };
 
     // softmax of one tile (this wave's half of the scores plus the partner
