@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
     const float *__restrict__ sink, float scale_log2,
     int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_ml, const SelArgs sa)
+    uint16_t *__restrict__ part_o, float *__restrict__ part_ml, int32_t stream_parts, const SelArgs sa)
 {
     using G = MlaGeom<DQK, DV>;
     using TG = TileGeom<DQK, DV>;
@@ -561,6 +561,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // than the bf16 output). Values are scaled by 2^-e per (head, half),
         // e > 0 only when the half's largest magnitude reaches 2^14, so that
         // none leaves the fp16 range; (m, l, e_half0, e_half1) go beside it.
+        // A small partial set (stream_parts) goes out with streaming stores:
+        // dirty L2 lines would otherwise be written back at the kernel
+        // boundary, on the critical path; a large one is better merged into
+        // whole lines in the L2 first.
         const int64_t prow = ((int64_t)t * splits + split) * H;
         float inv4[4], mx4[4];
         bool big = false;
@@ -592,10 +596,17 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             const int h = h0 + 4 * g + r;
             if (h >= H)
                 continue;
+            uint16_t *po = part_o + (prow + h) * DV + 16 * nt0 + c;
+            if (stream_parts) {
 #pragma unroll
-            for (int i = 0; i < NTH; ++i)
-                part_o[(prow + h) * DV + 16 * (nt0 + i) + c] =
-                    __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl));
+                for (int i = 0; i < NTH; ++i)
+                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl)),
+                                                po + 16 * i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NTH; ++i)
+                    po[16 * i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl));
+            }
             if (c == 0)
                 part_ml[(prow + h) * 4 + 2 + half] = (float)e;
         }
@@ -611,8 +622,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 // scaled by 2^-e) and adds the sink:
 //   out = sum_s 2^(m_s - m) l_s 2^e_s p_s / (2^(sink - m) + sum_s 2^(m_s - m) l_s)
 constexpr int kMaxSplits = 256;
-constexpr int kCombineBatch = 16;           // partial loads in flight per thread
+// partial loads in flight per thread: 32 where a head has more than 16
+// splits (one round trip instead of two), else 16 (fewer registers)
+constexpr int kCombineBatchMax = 32;
 constexpr int64_t kResidentWGs = 256;       // one per CU (the tile ring's LDS)
+constexpr size_t kStreamPartsMax = (size_t)8 << 20;   // partial sets stored with streaming stores
 
 // Max / sum over the first n lanes of a wave (n = 16 or 64), in registers
 // (DPP): row shifts by 1, 2, 4 and 8 reduce each row of 16 lanes into its last
@@ -653,7 +667,7 @@ __device__ __forceinline__ float wave_sum(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), N - 1));
 }
 
-template <int DV>
+template <int DV, int CB>
 __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__restrict__ part_o,
                                                              const float *__restrict__ part_ml,
                                                              const float *__restrict__ sink, int32_t H,
@@ -670,13 +684,13 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
     const int tid = threadIdx.x;
     const int hf = 4 * tid >= DV / 2;           // the half this thread's columns lie in
     const int64_t pr0 = (int64_t)t * splits * H + h;          // row of split 0
-    // this thread's four columns of the first kCombineBatch splits: they do
+    // this thread's four columns of the first CB splits: they do
     // not depend on the weights, so they travel with the (m, l) loads
     const uint2 *p = reinterpret_cast<const uint2 *>(part_o + pr0 * DV) + tid;
     const int64_t stride = (int64_t)H * DV / 4;               // uint2s between splits
-    uint2 x[kCombineBatch];
+    uint2 x[CB];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u)
+    for (int u = 0; u < CB; ++u)
         if (u < splits)
             x[u] = p[(int64_t)u * stride];
     // the first wave: (m, l, e0, e1) of splits tid, tid + NL, ... in one
@@ -712,18 +726,18 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
     }
     __syncthreads();
     const float inv = inv_den;
-    // every split's columns, kCombineBatch loads in flight
+    // every split's columns, CB loads in flight
     auto h2f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
+    for (int s0 = 0; s0 < splits; s0 += CB) {
         if (s0 > 0) {
 #pragma unroll
-            for (int u = 0; u < kCombineBatch; ++u)
+            for (int u = 0; u < CB; ++u)
                 if (s0 + u < splits)
                     x[u] = p[(int64_t)(s0 + u) * stride];
         }
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
+        for (int u = 0; u < CB; ++u)
             if (s0 + u < splits) {
                 const float wv = wgt[hf][s0 + u];
                 acc.x = fmaf(h2f(x[u].x & 0xFFFFu), wv, acc.x);
@@ -757,12 +771,16 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
     }
     hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
                        q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
-                       out_f32, part_o, part_ml, sa);
+                       out_f32, part_o, part_ml, (int32_t)plan.stream_parts, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
-    hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3(H, T), dim3(DV / 4), 0, stream, part_o, part_ml, sink, H,
-                       plan.splits, out, out_f32);
+    if (plan.splits > kCombineBatchMax / 2)
+        hipLaunchKernelGGL((mla_combine_kernel<DV, kCombineBatchMax>), dim3(H, T), dim3(DV / 4), 0, stream, part_o,
+                           part_ml, sink, H, plan.splits, out, out_f32);
+    else
+        hipLaunchKernelGGL((mla_combine_kernel<DV, kCombineBatchMax / 2>), dim3(H, T), dim3(DV / 4), 0, stream, part_o,
+                           part_ml, sink, H, plan.splits, out, out_f32);
     return hipGetLastError();
 }
 
@@ -810,6 +828,7 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     p.splits = (int32_t)s;
     p.rows_per_split = (int32_t)rps;
     p.ws_bytes = s > 1 ? (size_t)T * s * H * ((size_t)D_v * 2 + 4 * sizeof(float)) : 0;
+    p.stream_parts = p.ws_bytes <= kStreamPartsMax;
     return p;
 }
 
