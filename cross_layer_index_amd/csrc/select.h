@@ -106,6 +106,7 @@ struct Shared {
     uint32_t hist[kBins0];
     uint32_t waves[16];
     uint32_t digit, above, count;
+    uint32_t list_n;                 // entries of a short key list kept in hist
 };
 
 // Given a histogram of `nb` (1024 or 2048) bins in LDS, complete before the
@@ -466,6 +467,8 @@ struct SplitSel {
         const uint32_t b22 = bound >> 10;
         for (int i = tid; i < kBins0; i += NT)
             sh.hist[i] = 0;
+        if (tid == 0)
+            sh.list_n = 0;
         wg_barrier<LB>();
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -474,12 +477,41 @@ struct SplitSel {
         wg_barrier<LB>();
         uint32_t rel, above;
         find_digit<NT, LB>(sh, kBins0, (uint32_t)k, rel, above);
-        const uint32_t in_bin = sh.count;
+        const uint32_t in_bin = __builtin_amdgcn_readfirstlane(sh.count);
         const uint32_t pre = (b22 + rel) << 10;
         uint32_t thr, need;
         if (rel < (uint32_t)kBins0 - 1 && in_bin == (uint32_t)k - above && pre != 0u) {
             thr = pre - 1u;                           // every key of the bin is kept
             need = 0;
+        } else if (rel < (uint32_t)kBins0 - 1 && in_bin <= 64u) {
+            // A bin of at most a wave's width: its keys go to a list (the
+            // histogram's words, read by no one any more) and wave 0 ranks
+            // them. The threshold is the key with fewer than k - above
+            // greater keys in the bin and at least k - above greater or
+            // equal ones; of the keys equal to it, the first k - above -
+            // (greater ones) in position order are kept.
+            const uint32_t want = (uint32_t)k - above;  // in [1, in_bin]
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if ((valid >> e & 1u) && (key[e] >> 10) - b22 == rel)
+                    sh.hist[atomicAdd(&sh.list_n, 1u)] = key[e];
+            wg_barrier<LB>();
+            if (tid < 64) {
+                const uint32_t kv = (uint32_t)tid < in_bin ? sh.hist[tid] : 0u;
+                uint32_t gt = 0, eq = 0;
+                for (uint32_t j = 0; j < in_bin; ++j) {
+                    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)kv, (int)j);
+                    gt += o > kv;
+                    eq += o == kv;
+                }
+                if ((uint32_t)tid < in_bin && gt < want && gt + eq >= want) {
+                    sh.digit = kv;                    // every lane holding the key writes the same
+                    sh.above = want - gt;
+                }
+            }
+            wg_barrier<LB>();
+            thr = sh.digit;
+            need = sh.above;
         } else {
             uint32_t prefix = 0, pmask = 0;
             int first = 0;
