@@ -509,11 +509,23 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         wait_vmcnt<0>();                          // tile 1's fills
         lds_barrier();
     }
+    // The two waves of a pair share a SIMD (waves w and w + 4); they take the
+    // step's two halves in opposite orders, so that one's matrix products
+    // overlap the other's LDS reads and exponentials. (Both orders are
+    // legal: tile i+1's scores go to the other sx buffer than tile i's.)
     auto step = [&](int i, const uint16_t *cur, const uint16_t *nxt, uint16_t *ahead) {
         if (i + 2 < ntiles)
             issue(ahead, (i + 2) * kTile);
-        softmax_pv(cur, i * kTile, sc0, sc1, i & 1);
-        qk(nxt, sc0, sc1);
+        if (half == 0) {
+            softmax_pv(cur, i * kTile, sc0, sc1, i & 1);
+            qk(nxt, sc0, sc1);
+        } else {
+            f4 n0, n1;
+            qk(nxt, n0, n1);
+            softmax_pv(cur, i * kTile, sc0, sc1, i & 1);
+            sc0 = n0;
+            sc1 = n1;
+        }
         sx[(i + 1) & 1][wave][0][lane] = sc0;
         sx[(i + 1) & 1][wave][1][lane] = sc1;
         wait_vmcnt<0>();                          // tile i+2's fills
