@@ -59,7 +59,7 @@ struct MlaPlan {
     int32_t splits;          // k-splits per (query, head group)
     int32_t rows_per_split;  // multiple of the row tile
     size_t ws_bytes;         // partial results when splits > 1
-    bool stream_parts;       // partials small enough to bypass the L2 on the way out
+    bool direct_parts;       // partials few enough to store straight from the registers
 };
 bool sparse_mla_supported(int32_t D_qk, int32_t D_v);
 MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v);

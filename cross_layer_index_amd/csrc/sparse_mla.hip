@@ -84,6 +84,7 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Reductions over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48)
 // inside the VGPRs: v_permlane16_swap pairs rows (0,1) and (2,3),
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
     const float *__restrict__ sink, float scale_log2,
     int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
-    uint16_t *__restrict__ part_o, float *__restrict__ part_ml, int32_t stream_parts, const SelArgs sa)
+    uint16_t *__restrict__ part_o, float *__restrict__ part_ml, int32_t direct_parts, const SelArgs sa)
 {
     using G = MlaGeom<DQK, DV>;
     using TG = TileGeom<DQK, DV>;
@@ -573,10 +574,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // than the bf16 output). Values are scaled by 2^-e per (head, half),
         // e > 0 only when the half's largest magnitude reaches 2^14, so that
         // none leaves the fp16 range; (m, l, e_half0, e_half1) go beside it.
-        // A small partial set (stream_parts) goes out with streaming stores:
-        // dirty L2 lines would otherwise be written back at the kernel
-        // boundary, on the critical path; a large one is better merged into
-        // whole lines in the L2 first.
+        // Partials go out with streaming stores: dirty L2 lines would
+        // otherwise be written back at the kernel boundary, on the critical
+        // path. A small set (direct_parts: one short round of workgroups,
+        // where the epilogue's latency counts) is stored from the registers,
+        // a large one is first staged into whole rows.
         const int64_t prow = ((int64_t)t * splits + split) * H;
         float inv4[4], mx4[4];
         bool big = false;
@@ -594,9 +596,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // the maximum over the row group's 16 lanes only where some value of
         // the wave reaches the scaled range (otherwise every e is 0)
         const bool any_big = __any(big);
+        float scl4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float inv = inv4[r];
             float mx = mx4[r];
             if (any_big) {
 #pragma unroll
@@ -604,23 +606,47 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
                     mx = fmaxf(mx, __shfl_xor(mx, off));
             }
             const int e = mx >= 16384.0f ? ilogbf(mx) - 13 : 0;
-            const float scl = ldexpf(inv, -e);
+            scl4[r] = ldexpf(inv4[r], -e);
             const int h = h0 + 4 * g + r;
-            if (h >= H)
-                continue;
-            uint16_t *po = part_o + (prow + h) * DV + 16 * nt0 + c;
-            if (stream_parts) {
-#pragma unroll
-                for (int i = 0; i < NTH; ++i)
-                    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl)),
-                                                po + 16 * i);
-            } else {
-#pragma unroll
-                for (int i = 0; i < NTH; ++i)
-                    po[16 * i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl));
-            }
-            if (c == 0)
+            if (c == 0 && h < H)
                 part_ml[(prow + h) * 4 + 2 + half] = (float)e;
+        }
+        if (direct_parts) {
+            // a small partial set: straight from the registers
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (h0 + 4 * g + r >= H)
+                    continue;
+                uint16_t *po = part_o + (prow + h0 + 4 * g + r) * DV + 16 * nt0 + c;
+#pragma unroll
+                for (int i = 0; i < NTH; ++i)
+                    __builtin_nontemporal_store(
+                        __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl4[r])), po + 16 * i);
+            }
+        } else {
+            // A large one: the wave's 16 x DV/2 block goes through LDS (the tile
+            // buffers, free once every wave has left the tile loop) and leaves in
+            // whole rows, 16-byte stores, 32 lanes per 512-byte row.
+            constexpr int SROW = DV / 2 + 16;          // staging row stride (elements)
+            static_assert(4 * 16 * SROW <= TG::ELEMS, "staging fits a tile buffer");
+            lds_barrier();
+            uint16_t *stg = (half == 0 ? tile0 : tile1) + hgrp * 16 * SROW;
+#pragma unroll
+            for (int i = 0; i < NTH; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    stg[(4 * g + r) * SROW + 16 * i + c] =
+                        __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl4[r]));
+            constexpr int RCH = DV / 16;               // 16-byte chunks per staged row
+#pragma unroll
+            for (int j = 0; j < DV / 64; ++j) {
+                const int q = lane + 64 * j;
+                const int row = q / RCH, ch = q - row * RCH;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + row * SROW + 8 * ch);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(part_o + (prow + h0 + row) * DV + (DV / 2) * half + 8 * ch);
+                if (h0 + row < H)
+                    __builtin_nontemporal_store(v, dst);
+            }
         }
         if (half == 0 && g == 0 && hc < H) {
             part_ml[(prow + hc) * 4 + 0] = m_run;
@@ -638,7 +664,7 @@ constexpr int kMaxSplits = 256;
 // splits (one round trip instead of two), else 16 (fewer registers)
 constexpr int kCombineBatchMax = 32;
 constexpr int64_t kResidentWGs = 256;       // one per CU (the tile ring's LDS)
-constexpr size_t kStreamPartsMax = (size_t)8 << 20;   // partial sets stored with streaming stores
+constexpr size_t kDirectPartsMax = (size_t)8 << 20;   // partial sets stored straight from the registers
 
 // Max / sum over the first n lanes of a wave (n = 16 or 64), in registers
 // (DPP): row shifts by 1, 2, 4 and 8 reduce each row of 16 lanes into its last
@@ -783,7 +809,7 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
     }
     hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
                        q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
-                       out_f32, part_o, part_ml, (int32_t)plan.stream_parts, sa);
+                       out_f32, part_o, part_ml, (int32_t)plan.direct_parts, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
@@ -840,7 +866,7 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     p.splits = (int32_t)s;
     p.rows_per_split = (int32_t)rps;
     p.ws_bytes = s > 1 ? (size_t)T * s * H * ((size_t)D_v * 2 + 4 * sizeof(float)) : 0;
-    p.stream_parts = p.ws_bytes <= kStreamPartsMax;
+    p.direct_parts = p.ws_bytes <= kDirectPartsMax;
     return p;
 }
 
