@@ -84,24 +84,23 @@ __device__ __forceinline__ void load_run(const uint8_t *p, v8i (&frag)[IdxGeom<D
 
 constexpr int kIdxWaves = 4;
 constexpr int kIdxThreads = kIdxWaves * 64;
-constexpr int kIdxUnroll = 2;                                  // 32-token groups per wave step
-constexpr int kIdxStep = kIdxWaves * 32 * kIdxUnroll;          // tokens per WG step
+constexpr int kIdxStep = kIdxWaves * 32 * 2;                  // tokens per WG step of two groups
 constexpr int kIdxMaxChunk = 512;                              // tokens per WG, upper bound
 constexpr int64_t kIdxResident = 2 * 256;                      // resident WGs: 2 per CU x 256 CUs
 
-// One wave step's key fragments: kIdxUnroll groups of 32 tokens, each lane
-// holding its run of one token row (rows past the query's end are clamped to
-// its last row; their scores are never stored).
-template <int DI>
+// One wave step's key fragments: U groups of 32 tokens, each lane holding its
+// run of one token row (rows past the query's end are clamped to its last
+// row; their scores are never stored).
+template <int DI, int U>
 struct KeyStep {
-    v8i b[kIdxUnroll][IdxGeom<DI>::KS];
+    v8i b[U][IdxGeom<DI>::KS];
 };
 
-template <int DI>
-__device__ __forceinline__ void load_step(KeyStep<DI> &ks, const uint8_t *krows, int64_t s0, int j, int64_t nt)
+template <int DI, int U>
+__device__ __forceinline__ void load_step(KeyStep<DI, U> &ks, const uint8_t *krows, int64_t s0, int j, int64_t nt)
 {
 #pragma unroll
-    for (int u = 0; u < kIdxUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         int64_t s = s0 + 32 * u + j;
         s = s < nt ? s : nt - 1;
         load_run<DI>(krows + s * DI, ks.b[u]);
@@ -109,13 +108,13 @@ __device__ __forceinline__ void load_step(KeyStep<DI> &ks, const uint8_t *krows,
 }
 
 // grid: (token chunks, T); block: 256 threads. A workgroup scores `chunk`
-// consecutive tokens of one query; each wave takes every fourth step of 64
+// consecutive tokens of one query; each wave takes every fourth step of 32 U
 // tokens and keeps the next step's key rows in flight while it scores the
 // current one. Head weights come from LDS as float4 (four consecutive heads
 // per accumulator quad), q fragments stay in registers. With `hist0` set the
 // workgroup also counts the first radix digit of its scores and adds its
 // counts to copy (blockIdx.x mod kHistCopies) of the query's histogram.
-template <int DI, int MT>
+template <int DI, int MT, int U>
 __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
     const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
     const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t H_I,
@@ -160,9 +159,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
 
     // the wave's first key rows go out before the weights are staged (the
     // LDS store waits for the weight load; the key loads need not)
-    int64_t s0 = s_begin + (int64_t)wave * 32 * kIdxUnroll;
-    KeyStep<DI> x, y;
-    load_step<DI>(x, krows, s0 < s_end ? s0 : s_begin, j, nt);
+    constexpr int64_t WS = kIdxWaves * 32 * U;    // tokens per workgroup step
+    int64_t s0 = s_begin + (int64_t)wave * 32 * U;
+    KeyStep<DI, U> x, y;
+    load_step<DI, U>(x, krows, s0 < s_end ? s0 : s_begin, j, nt);
     if (threadIdx.x < MT * 32)
         wsh[threadIdx.x] = wv;
     if (hist0)
@@ -171,9 +171,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
     __syncthreads();
     const float4 *w4 = reinterpret_cast<const float4 *>(wsh);
 
-    auto score_step = [&](const KeyStep<DI> &ks, int64_t s0) {
+    auto score_step = [&](const KeyStep<DI, U> &ks, int64_t s0) {
 #pragma unroll
-        for (int u = 0; u < kIdxUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             float sum = 0.0f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -205,21 +205,21 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
     // step's loads are always issued before the current step is scored, and
     // every load in the loop is unconditional so the compiler's wait counts
     // stay exact (a conditional load makes it wait for everything)
-    const int nsteps = s0 < s_end ? (int)((s_end - s0 + kIdxStep - 1) / kIdxStep) : 0;
+    const int nsteps = s0 < s_end ? (int)((s_end - s0 + WS - 1) / WS) : 0;
     int i = 0;
-    for (; i + 2 < nsteps; i += 2, s0 += 2 * kIdxStep) {
-        load_step<DI>(y, krows, s0 + kIdxStep, j, nt);
+    for (; i + 2 < nsteps; i += 2, s0 += 2 * WS) {
+        load_step<DI, U>(y, krows, s0 + WS, j, nt);
         __builtin_amdgcn_sched_barrier(0);
         score_step(x, s0);
-        load_step<DI>(x, krows, s0 + 2 * kIdxStep, j, nt);
+        load_step<DI, U>(x, krows, s0 + 2 * WS, j, nt);
         __builtin_amdgcn_sched_barrier(0);
-        score_step(y, s0 + kIdxStep);
+        score_step(y, s0 + WS);
     }
     if (nsteps - i == 2) {
-        load_step<DI>(y, krows, s0 + kIdxStep, j, nt);
+        load_step<DI, U>(y, krows, s0 + WS, j, nt);
         __builtin_amdgcn_sched_barrier(0);
         score_step(x, s0);
-        score_step(y, s0 + kIdxStep);
+        score_step(y, s0 + WS);
     } else if (nsteps - i == 1) {
         score_step(x, s0);
     }
@@ -247,12 +247,20 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
     if (nchunks == 0 || T == 0)
         return hipSuccess;
     dim3 grid((unsigned)nchunks, (unsigned)T);
+    // A workgroup that holds a single step of two groups per wave (the whole
+    // grid in one round) takes it as two pipelined one-group steps instead:
+    // each wave scores its first 32 tokens while the next 32 arrive, which
+    // shortens the tail after the last bytes land. Longer chunks keep
+    // two-group steps.
+    const bool one = chunk == kIdxStep;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx, base, n, H_I, scores, ld, chunk,
+                           hist0);
+    };
     if (H_I <= 32)
-        hipLaunchKernelGGL((indexer_decode_kernel<DI, 1>), grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx,
-                           base, n, H_I, scores, ld, chunk, hist0);
+        one ? go(indexer_decode_kernel<DI, 1, 1>) : go(indexer_decode_kernel<DI, 1, 2>);
     else
-        hipLaunchKernelGGL((indexer_decode_kernel<DI, 2>), grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx,
-                           base, n, H_I, scores, ld, chunk, hist0);
+        one ? go(indexer_decode_kernel<DI, 2, 1>) : go(indexer_decode_kernel<DI, 2, 2>);
     return hipGetLastError();
 }
 
