@@ -24,8 +24,8 @@
 // the second product without any data movement. Softmax runs online in fp32
 // in log2 units.
 // When one query's list is split over several workgroups, each writes its
-// unnormalised partial (m, l, o) and a combine kernel merges them and adds the
-// sink once.
+// partial (m, l, and o normalised by l, in fp16) with streaming stores, and a
+// combine kernel merges them and adds the sink once.
 #include "kernels.h"
 #include "select.h"
 
