@@ -1,6 +1,14 @@
 """Checks shared by the CPU and GPU tests (no method arithmetic)."""
 import numpy as np
 
+# (case, achieved error) of every tolerance check in the run, printed in the
+# terminal summary (outside pytest's output capture) by conftest.py
+ERRORS = []
+
+
+def report(what, err):
+    ERRORS.append((what, float(err)))
+
 
 def check_topk_invariants(scores, n, k, idx):
     """Full-size invariant: |S| = min(k, n), distinct, in range, ascending, and

@@ -34,3 +34,11 @@ def gpu():
         raise RuntimeError("GPU tests need a HIP device (run them with -m gpu on an MI355X)")
     from cross_layer_index_amd import ic
     return ic
+
+
+def pytest_terminal_summary(terminalreporter):
+    from checks import ERRORS
+    if ERRORS:
+        terminalreporter.section("achieved errors (max-abs unless noted; bar 5e-3)")
+        for what, err in ERRORS:
+            terminalreporter.write_line(f"[max-abs] {what}: {err:.3e}")

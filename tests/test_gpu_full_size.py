@@ -4,37 +4,39 @@ queries (and sampled layers of the 78-layer stack) one by one; every query's
 index row is also checked against the top-k invariants where its scores are
 known. Inputs of the large workloads are drawn on the device by the seeded
 generator and copied back for the oracle."""
+import sys
+
 import numpy as np
 import pytest
 import torch
 
-from checks import check_topk_invariants
+from checks import check_topk_invariants, report
 from cross_layer_index_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 ATOL = 5e-3
 
 
-def half_ulp_bf16(x):
-    x = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
-    return np.ldexp(1.0, np.floor(np.log2(x)).astype(np.int64) - 8)
-
-
 def assert_close(got, ref, what):
-    err = np.abs(got - ref)
-    tol = ATOL + half_ulp_bf16(ref)
-    assert (err <= tol).all(), f"{what}: max abs error {err.max()}"
-    return float(err.max())
+    """Flat max-abs 5e-3 against the fp64 oracle."""
+    err = float(np.abs(got - ref).max())
+    report(what, err)
+    assert err <= ATOL, f"{what}: max abs error {err:.3e} > {ATOL}"
+    return err
 
 
-def build_stack(ic, wl, rmap, device_gen):
+def bf16_rne(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def build_stack(ic, wl, rmap, device_gen, out_f32=False):
     lays, host = [], []
     for l in range(wl.n_layers):
         full = rmap[l] == l
         li = W.layer_inputs(wl, l, device="cuda" if device_gen else "cpu", with_indexer=full)
         d = W.LayerInputs(*[None if x is None else x.cuda() for x in (li.q_idx, li.w, li.k_idx, li.q, li.kv,
                                                                        li.sink)])
-        out = torch.empty((wl.T, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((wl.T, wl.H, wl.D_v), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
         lays.append(dict(q_idx=d.q_idx, w=d.w, k_idx=d.k_idx, q=d.q, kv=d.kv, sink=d.sink, out=out))
         host.append(li)
     return lays, host
@@ -65,11 +67,14 @@ def oracle_query(orc, wl, qd, idx_src=None):
     return I, idx
 
 
-def run_case(gpu, orc, wl, sample_t, sample_layers=None, device_gen=True):
+def run_case(gpu, orc, wl, sample_t, sample_layers=None, device_gen=True, out_f32=False, pairs=None):
+    """The stack at full size; sampled (layer, query) outputs against the
+    oracle at the flat 5e-3. With out_f32 and a dict `pairs`, the fp32
+    outputs of every layer are also returned in it (for the bf16 pairing)."""
     rmap = gpu.reuse_map_last_full(wl.is_full())
-    lays, host = build_stack(gpu, wl, rmap, device_gen)
+    lays, host = build_stack(gpu, wl, rmap, device_gen, out_f32)
     qs = gpu.make_queries(wl.base(), wl.n_valid(), wl.rows(), wl.same_seq, group=wl.group)
-    d = gpu.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v)
+    d = gpu.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v, out_f32)
     st = gpu.LayerStack(lays, rmap, qs, d, wl.scale)
     passes = st()
     torch.cuda.synchronize()
@@ -94,7 +99,10 @@ def run_case(gpu, orc, wl, sample_t, sample_layers=None, device_gen=True):
             sink = host[l].sink.cpu()
             ref = orc.sparse_mla(qd["q"], qd["kv"], np.array([0], np.int64), ref_idx[key], sink, wl.scale, wl.D_v)
             got = lays[l]["out"][t:t + 1].float().cpu().numpy()
-            worst = max(worst, assert_close(got, ref, f"layer {l} query {t}"))
+            worst = max(worst, assert_close(got, ref, f"{wl.name} layer {l} query {t} "
+                                                      f"[{'fp32' if out_f32 else 'bf16'}]"))
+    if pairs is not None:
+        pairs.update({l: lays[l]["out"].float().cpu().numpy() for l in range(wl.n_layers)})
     return st, worst
 
 
@@ -111,8 +119,21 @@ def test_ragged_64_full(gpu, orc):
 
 
 def test_edge_lengths_full(gpu, orc):
+    """The edge set (n = 0, 1, 63, 64, 65, 2047, 2048, 2049, 4095). Its short
+    rows give outputs near 3 (one key: o = v * sigmoid(s - sink)), where bf16
+    spacing alone is 2^-6: the fp32 stack holds the flat 5e-3 on every query,
+    and the bf16 stack's outputs are the rounded fp32 outputs bit for bit."""
     wl = W.WORKLOADS["edge_lengths"]
-    run_case(gpu, orc, wl, list(range(wl.T)), device_gen=False)
+    f32 = {}
+    run_case(gpu, orc, wl, list(range(wl.T)), device_gen=False, out_f32=True, pairs=f32)
+    rmap = gpu.reuse_map_last_full(wl.is_full())
+    lays, _ = build_stack(gpu, wl, rmap, False)
+    qs = gpu.make_queries(wl.base(), wl.n_valid(), wl.rows())
+    st = gpu.LayerStack(lays, rmap, qs, gpu.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v), wl.scale)
+    st()
+    torch.cuda.synchronize()
+    for l in range(wl.n_layers):
+        assert np.array_equal(lays[l]["out"].float().cpu().numpy(), bf16_rne(f32[l])), f"layer {l}"
 
 
 def test_mtp_verify_full(gpu, orc):
@@ -173,7 +194,7 @@ def test_prefill_1m_full(gpu, orc):
             ref = orc.sparse_mla(host[l].q[t:t + 1].cpu(), kv_host[l], np.array([0], np.int64), ref_idx,
                                  host[l].sink.cpu(), wl.scale, wl.D_v)
             got = lays[l]["out"][t:t + 1].float().cpu().numpy()
-            assert_close(got, ref, f"layer {l} query {t}")
+            assert_close(got, ref, f"prefill_1m layer {l} query {t} [bf16]")
     # every row: a valid index set of the right size
     assert (idx_all >= 0).all() and (np.diff(idx_all, axis=1) > 0).all()
     assert (idx_all < n[:, None]).all()
