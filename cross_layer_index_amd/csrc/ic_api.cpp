@@ -6,7 +6,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <vector>
 
 #include "kernels.h"
 
@@ -121,6 +120,9 @@ ic_status check_dims_mla(const ic_dims *d)
         return fail(IC_ERR_SHAPE, "k=%d outside [1, 2^20]", d->k);
     if (d->H < 1 || d->H > 4096)
         return fail(IC_ERR_SHAPE, "H=%d outside [1, 4096]", d->H);
+    if (d->k > ic::sparse_mla_max_k())
+        return fail(IC_ERR_UNSUPPORTED, "sparse MLA: k=%d exceeds the %d index entries one query is built for",
+                    d->k, ic::sparse_mla_max_k());
     if (!ic::sparse_mla_supported(d->D_qk, d->D_v))
         return fail(IC_ERR_UNSUPPORTED, "sparse MLA: (D_qk, D_v)=(%d, %d) not built; built: (576, 512), (80, 64)",
                     d->D_qk, d->D_v);
@@ -448,8 +450,14 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
     void *mla_ws = static_cast<char *>(ws) + L.mla_off;
     const ic::MlaPlan plan = ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    std::vector<int32_t> slot(n_layers, -1);
-    int32_t next_slot = 0;
+    // slot of a full layer = its rank among the full layers (counted where
+    // needed: the call allocates nothing, host memory included)
+    auto slot_of = [&](int32_t f) {
+        int32_t r = 0;
+        for (int32_t i = 0; i < f; ++i)
+            r += reuse_map[i] == i;
+        return r;
+    };
     const size_t slot_elems = (size_t)qs->T * d->k;
     // When the top-k takes its split path and the MLA grid fits on the chip at
     // once, a full layer's MLA workgroups finish the selection themselves
@@ -458,16 +466,22 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
     ic::TopkSplitView view{};
     const bool selecting = qs->max_n > 0 && ic::topk_split_view(topk_ws, qs->T, qs->max_n, &view) &&
                            ic::sparse_mla_selecting_supported(plan, qs->T, d->H, view);
+    // the per-query key stream also fills the top-k's first-digit histogram
+    // when the selection reads it; the workspace carries nothing from earlier
+    // calls, so the histograms are cleared once here (the row kernel leaves
+    // them clear for the next full layer)
+    const bool fused_hist = qs->max_n > 0 && n_full > 0 && !use_prefill_indexer(qs, d->H_I, d->D_I) &&
+                            ic::topk_reads_hist0(qs->T, qs->max_n);
+    if (fused_hist) {
+        hipError_t e = ic::launch_clear_hist0(topk_ws, qs->T, st);
+        if (e != hipSuccess)
+            return hip_status(e, "layer stack: histogram clear launch");
+    }
     for (int32_t l = 0; l < n_layers; ++l) {
         const ic_layer &y = layers[l];
         const bool full = reuse_map[l] == l;
         if (full) {
-            slot[l] = next_slot++;
-            int32_t *idx = index_cache + slot[l] * slot_elems;
-            // the per-query key stream also fills the top-k's first-digit
-            // histogram when the selection reads it
-            const bool fused_hist = qs->max_n > 0 && !use_prefill_indexer(qs, d->H_I, d->D_I) &&
-                                    ic::topk_reads_hist0(qs->T, qs->max_n);
+            int32_t *idx = index_cache + slot_of(l) * slot_elems;
             if (qs->max_n > 0) {
                 hipError_t e = launch_indexer(y.q_idx, y.w, y.k_idx, qs, d->H_I, d->D_I, scores, L.ld,
                                               fused_hist ? ic::topk_hist0(topk_ws) : nullptr, st);
@@ -481,7 +495,7 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
             if (e != hipSuccess)
                 return hip_status(e, "layer stack: top-k launch");
         }
-        int32_t *idx = index_cache + slot[reuse_map[l]] * slot_elems;
+        int32_t *idx = index_cache + slot_of(reuse_map[l]) * slot_elems;
         const int32_t f32 = d->out_dtype == IC_OUT_F32;
         hipError_t e = full && selecting
                            ? ic::launch_sparse_mla_selecting(y.q, y.kv, qs->base, qs->n_valid, qs->T, d->H, d->k,

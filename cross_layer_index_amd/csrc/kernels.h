@@ -29,12 +29,15 @@ bool indexer_prefill_supported(int32_t H_I, int32_t D_I);
 
 // ---- top-k ------------------------------------------------------------------
 // The workspace starts with the first-digit histograms [T][copies][2048]
-// (uint32, zero on entry and on return); topk_hist0() points at them.
+// (uint32) that a producer may fill; topk_hist0() points at them.
+// launch_clear_hist0 zeroes them (before the first producer of a call); the
+// row path returns them to zero after reading them.
 size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t k);
 uint32_t *topk_hist0(void *ws);
 // Whether the selection for this shape reads those histograms (a producer
 // need not fill them otherwise).
 bool topk_reads_hist0(int32_t T, int64_t max_n);
+hipError_t launch_clear_hist0(void *ws, int32_t T, hipStream_t stream);
 // hist_ready: the histograms were filled while the scores were produced.
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
                        int32_t k, int32_t *idx, void *ws, bool hist_ready, hipStream_t stream);
@@ -62,6 +65,9 @@ struct MlaPlan {
     bool direct_parts;       // partials few enough to store straight from the registers
 };
 bool sparse_mla_supported(int32_t D_qk, int32_t D_v);
+// Largest index list one query may carry: the combine merges at most
+// kMaxSplits splits of at most kMaxRowsPerSplit entries.
+int32_t sparse_mla_max_k();
 MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v);
 hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_t *base,
                              const int32_t *n_valid, const int32_t *idx, int32_t T, int32_t H, int32_t k, int32_t D_qk,

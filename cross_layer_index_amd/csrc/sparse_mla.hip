@@ -824,6 +824,8 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
 
 }  // namespace
 
+int32_t sparse_mla_max_k() { return kMaxSplits * kMaxRowsPerSplit; }
+
 bool sparse_mla_supported(int32_t D_qk, int32_t D_v)
 {
     return (D_qk == 576 && D_v == 512) || (D_qk == 80 && D_v == 64);

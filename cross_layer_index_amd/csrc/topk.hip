@@ -37,9 +37,13 @@
 //     those at or above the second-digit threshold.
 // Only ties spanning more than a list fall back to digit passes over the
 // full row.
-// The first-digit histogram is kept in kHistCopies copies per query (adders
-// pick a copy by workgroup index, which spreads atomic traffic); the workspace
-// holds them zeroed on entry and the finishing workgroup zeroes them again.
+// The first-digit histogram a producer fills is kept in kHistCopies copies per
+// query (adders pick a copy by workgroup index, which spreads atomic traffic);
+// the caller clears them before the producer runs (clear_hist0_kernel) and
+// the row kernel returns them to zero after reading them, so the next producer
+// in the same call finds them clear.
+#include <algorithm>
+
 #include "kernels.h"
 #include "radix_key.h"
 #include "select.h"
@@ -260,12 +264,11 @@ __global__ __launch_bounds__(kSplitThreads) void topk_collect_kernel(const float
 // list (slice order = position order), slices longer than C adding the rest.
 // If at least k keys reached the bound, the k-th largest key and all its ties
 // are among them and the three digits finish from the list; with fewer, or
-// more than the list holds, they finish from the whole row. Zeroes the
-// first-digit histograms when given. The kernel reads back none of its
-// global stores, so its barriers order LDS traffic only.
+// more than the list holds, they finish from the whole row. The kernel reads
+// back none of its global stores, so its barriers order LDS traffic only.
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ n, int32_t k,
-    int32_t *__restrict__ idx, uint32_t *__restrict__ hist0, const uint32_t *__restrict__ counts,
+    int32_t *__restrict__ idx, const uint32_t *__restrict__ counts,
     const uint64_t *__restrict__ regions, int32_t P, const uint32_t *__restrict__ bounds)
 {
     constexpr int NT = kFinishThreads;
@@ -277,10 +280,8 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     int32_t *out = idx + (int64_t)t * k;
-    uint32_t *h0 = hist0 ? hist0 + (int64_t)t * kHistCopies * kBins0 : nullptr;
     // loads first (slice counts, slice prefixes: inside the workspace whatever
-    // the row's length, which they do not wait for), then the stores that
-    // clear the histograms
+    // the row's length, which they do not wait for)
     static_assert(kMaxSplit <= NT, "one scan over the slices");
     static_assert((NT * kSpec) / kMaxSplit >= 1 && kSplitChunk <= 8192 && NT * kSpec <= 8192,
                   "C >= 1; slice and entry fit 13 bits each");
@@ -299,13 +300,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(
     }
     const int64_t nt = n[t];
     if (nt <= k) {
-        if (h0)
-            zero_hist0<NT>(h0);
         write_all<NT>(out, nt, k);
         return;
     }
-    if (h0)
-        zero_hist0<NT>(h0);
     // slice offsets (P <= NT: one scan)
     if (tid == 0)
         long_slice = 0;
@@ -536,6 +533,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
         finish_select<kRowThreads>(src, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
 }
 
+// grid-stride fill of the first-digit histograms with zeros (a kernel, not a
+// memset: calls are captured into HIP graphs)
+__global__ __launch_bounds__(256) void clear_hist0_kernel(uint4 *__restrict__ h, int64_t n4)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+        h[i] = make_uint4(0, 0, 0, 0);
+}
+
 struct TopkLayout {
     bool split;
     int64_t P;
@@ -574,6 +579,17 @@ size_t topk_workspace_bytes(int32_t T, int64_t max_n, int32_t) { return topk_lay
 uint32_t *topk_hist0(void *ws) { return reinterpret_cast<uint32_t *>(ws); }
 
 bool topk_reads_hist0(int32_t T, int64_t max_n) { return !topk_layout(T, max_n).split; }
+
+hipError_t launch_clear_hist0(void *ws, int32_t T, hipStream_t stream)
+{
+    const int64_t n4 = (int64_t)T * kHistCopies * kBins0 / 4;
+    if (n4 == 0)
+        return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 1024);
+    hipLaunchKernelGGL(clear_hist0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<uint4 *>(ws), n4);
+    return hipGetLastError();
+}
 
 bool topk_split_view(void *ws, int32_t T, int64_t max_n, TopkSplitView *v)
 {
@@ -622,9 +638,9 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        // histograms filled by the producer are not needed here; they are cleared
+        // (the split path builds no first-digit histogram: a producer fills none)
         hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kFinishThreads), 0, stream, scores, ld, n,
-                           k, idx, hist_ready ? hist0 : nullptr, counts, regions, (int32_t)L.P, bounds);
+                           k, idx, counts, regions, (int32_t)L.P, bounds);
     } else {
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
                            hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));

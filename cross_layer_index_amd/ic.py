@@ -187,8 +187,8 @@ def indexer_score(q_idx, w, k_idx, qs: Queries, scores: Optional[torch.Tensor] =
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (the library's counters expect zeros at first use)."""
-    return torch.zeros(max(256, (int(nbytes) + 255) // 256 * 256), dtype=torch.uint8, device=device)
+    """Scratch device memory for a call (its contents on entry do not matter)."""
+    return torch.empty(max(256, (int(nbytes) + 255) // 256 * 256), dtype=torch.uint8, device=device)
 
 
 def topk(scores, qs: Queries, k: int, idx: Optional[torch.Tensor] = None, ws=None, stream=None):
@@ -322,7 +322,7 @@ class LayerStack:
                  ws: Optional[torch.Tensor] = None, index_cache: Optional[torch.Tensor] = None):
         """``ws`` and ``index_cache`` may be shared between stacks whose calls
         never overlap (one decode loop reuses them every step); otherwise they
-        are allocated here (the workspace zero-filled, as the library asks)."""
+        are allocated here."""
         self.n = len(layers)
         self.layers = layers
         self.qs = qs

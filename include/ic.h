@@ -21,14 +21,11 @@
  *    slot); cache offsets are int64.
  *  - Every device buffer, workspace included, is allocated by the caller. The
  *    library never allocates or frees device memory.
- *  - Workspaces: zero-fill a workspace before its first use. Every call that
- *    returns IC_OK leaves the workspace's counters zero again, so one
- *    workspace serves any number of calls of the same entry point with the
- *    same sizes (T, max_n, k, dims) on one stream -- a decode loop, a layer
- *    stack. Before a call of another entry point or other sizes, zero-fill it
- *    again: the layout depends on the sizes, and the data one layout leaves
- *    in its scratch areas may lie where another keeps its counters. Calls
- *    that overlap in time must use distinct workspaces.
+ *  - Workspaces hold no state between calls: their contents on entry are
+ *    ignored (any bytes will do), and a call leaves nothing in them that a
+ *    later call reads. One workspace therefore serves any sequence of calls
+ *    whose sizes it covers. Calls that overlap in time must use distinct
+ *    workspaces.
  *  - Every call enqueues kernels on `stream` (a hipStream_t; NULL = default
  *    stream) and returns without synchronising; no call issues memsets or
  *    host<->device copies, so calls may be captured into a HIP graph.

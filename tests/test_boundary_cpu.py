@@ -112,6 +112,26 @@ def test_mla_validation(ic):
         == ic.IC_ERR_WORKSPACE
 
 
+def test_mla_rejects_lists_beyond_the_combine(ic):
+    """The split combine merges at most 256 splits of 2048 entries: an index
+    list of 524,289 entries is rejected before any launch (it would need 257
+    splits), 524,288 passes validation up to the workspace check."""
+    qs = Q(ic, max_n=1 << 20, rows=1 << 20)
+    f = ic._lib.ic_sparse_mla
+    over = ic.dims(64, 128, 524289, 128, 576, 512)
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, ctypes.byref(over), FAKE, FAKE, 1 << 40, None) \
+        == ic.IC_ERR_UNSUPPORTED
+    assert b"524289" in ic._lib.ic_last_error()
+    edge = ic.dims(64, 128, 524288, 128, 576, 512)
+    assert f(FAKE, FAKE, ctypes.byref(qs), FAKE, FAKE, 0.1, ctypes.byref(edge), FAKE, None, 0, None) \
+        == ic.IC_ERR_WORKSPACE
+    stack = ic._lib.ic_layer_stack
+    lay = (ic.ic_layer * 1)(ic.ic_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    rmap = (ctypes.c_int32 * 1)(0)
+    assert stack(1, lay, rmap, ctypes.byref(qs), ctypes.byref(over), 0.1, FAKE, None, FAKE, 1 << 40, None) \
+        == ic.IC_ERR_UNSUPPORTED
+
+
 def test_reuse_map_matches_oracle_rule(ic):
     import oracle
     for pattern in (W.WORKLOADS["stack_78"].is_full(), [True] * 78, [True] + [False] * 77,
