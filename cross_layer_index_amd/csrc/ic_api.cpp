@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -14,6 +15,16 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+
+// Scratch memory of ic_layer_stack_static: a file-scope device array, one copy
+// per GPU, resident while the library is loaded. Host code never uses the
+// array's name as an address: the device address of each GPU's copy is taken
+// once per device with hipGetSymbolAddress and kept in g_scratch_dev.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
 
 ic_status fail(ic_status s, const char *fmt, ...)
 {
@@ -35,6 +46,27 @@ ic_status hip_status(hipError_t e, const char *what)
     if (e != hipSuccess)
         return fail(IC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+// Device address of the current GPU's scratch copy (resolved on first use).
+ic_status scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(IC_ERR_HIP, "static layer stack: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(IC_ERR_UNSUPPORTED, "static layer stack: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(IC_ERR_HIP, "static layer stack: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return IC_OK;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -507,4 +539,27 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
             return hip_status(e, "layer stack: sparse MLA launch");
     }
     return ok();
+}
+
+IC_EXPORT ic_status ic_layer_stack_static(int32_t n_layers, const ic_layer *layers, const int32_t *reuse_map,
+                                          const ic_queries *qs, const ic_dims *d, float scale,
+                                          int32_t *index_cache, int32_t *indexer_passes, void *stream)
+{
+    if (ic_status s = check_reuse_map(n_layers, reuse_map))
+        return s;
+    if (ic_status s = check_queries(qs))
+        return s;
+    if (ic_status s = check_dims_mla(d))
+        return s;
+    const size_t need = qs->T > 0 ? stack_layout(qs, d).total : 0;
+    if (need > kScratchBytes)
+        return fail(IC_ERR_WORKSPACE,
+                    "static layer stack: these sizes need %zu bytes of scratch, beyond the library's %zu; "
+                    "use ic_layer_stack with a workspace", need, kScratchBytes);
+    void *ws = nullptr;
+    if (qs->T > 0)
+        if (ic_status s = scratch_address(&ws))
+            return s;
+    return ic_layer_stack(n_layers, layers, reuse_map, qs, d, scale, index_cache, indexer_passes, ws,
+                          qs->T > 0 ? kScratchBytes : 0, stream);
 }

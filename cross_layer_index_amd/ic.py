@@ -60,6 +60,8 @@ _SIGS = {
     "ic_layer_stack_workspace_size": ([_QP, _DP], _sz),
     "ic_layer_stack": ([_i32, ctypes.POINTER(ic_layer), _P, _QP, _DP, _f32, _P, ctypes.POINTER(_i32), _P, _sz,
                         _P], _i32),
+    "ic_layer_stack_static": ([_i32, ctypes.POINTER(ic_layer), _P, _QP, _DP, _f32, _P, ctypes.POINTER(_i32), _P],
+                              _i32),
     "ic_status_str": ([_i32], ctypes.c_char_p),
     "ic_last_error": ([], ctypes.c_char_p),
 }
@@ -361,6 +363,14 @@ class LayerStack:
         _check(_lib.ic_layer_stack(self.n, self.arr, self.rmap, ctypes.byref(self.qc), ctypes.byref(self.d),
                                    self.scale, _ptr(self.index_cache), ctypes.byref(self.passes), _ptr(self.ws),
                                    self.ws.numel(), _stream(stream)))
+        return self.passes.value
+
+    def call_static(self, stream=None) -> int:
+        """The same stack through ic_layer_stack_static: the library's own
+        scratch instead of this object's workspace (no allocation in the call)."""
+        _check(_lib.ic_layer_stack_static(self.n, self.arr, self.rmap, ctypes.byref(self.qc), ctypes.byref(self.d),
+                                          self.scale, _ptr(self.index_cache), ctypes.byref(self.passes),
+                                          _stream(stream)))
         return self.passes.value
 
 

@@ -236,6 +236,23 @@ ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, const int32_t
                          int32_t *index_cache, int32_t *indexer_passes,
                          void *ws, size_t ws_bytes, void *stream);
 
+/* ic_layer_stack for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, but the workspace is the library's own scratch -- a
+ * device array of 32 MiB per GPU, resident while the library is loaded --
+ * instead of a caller buffer. The call allocates nothing (device or host);
+ * the first call on a device looks up that device's copy of the array once.
+ * The caller still provides every input and output, the index cache included.
+ * Sizes whose workspace (ic_layer_stack_workspace_size) exceeds 32 MiB return
+ * IC_ERR_WORKSPACE before any launch (batch 1 fits up to about 700K cached
+ * tokens; batch 8 at 32K fits). All calls on one GPU share its scratch: calls
+ * that overlap in time on one GPU (two streams, two threads) race and must be
+ * serialised by the caller. Nothing needs clearing between calls: the scratch
+ * holds no state a later call reads. */
+ic_status ic_layer_stack_static(int32_t n_layers, const ic_layer *layers, const int32_t *reuse_map,
+                                const ic_queries *qs, const ic_dims *d, float scale,
+                                int32_t *index_cache, int32_t *indexer_passes, void *stream);
+
 /* Human-readable name of a status, and the detail of the last failure on the
  * calling thread (empty string if none). Both return static storage. */
 const char *ic_status_str(ic_status s);

@@ -28,7 +28,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(ic):
     names = declared_entry_points()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(ic._lib, n), n
     assert sorted(ic.EXPORTED) == names
@@ -130,6 +130,23 @@ def test_mla_rejects_lists_beyond_the_combine(ic):
     rmap = (ctypes.c_int32 * 1)(0)
     assert stack(1, lay, rmap, ctypes.byref(qs), ctypes.byref(over), 0.1, FAKE, None, FAKE, 1 << 40, None) \
         == ic.IC_ERR_UNSUPPORTED
+
+
+def test_static_stack_rejects_oversized_workspace(ic):
+    """ic_layer_stack_static serves sizes whose workspace fits its 32 MiB
+    scratch; larger ones (64 queries over 64K tokens) fail with
+    IC_ERR_WORKSPACE before anything is launched or looked up."""
+    qs = Q(ic, T=64, max_n=65536, rows=64 * 65536)
+    d = ic.dims(64, 128, 2048, 128, 576, 512)
+    assert ic._lib.ic_layer_stack_workspace_size(ctypes.byref(qs), ctypes.byref(d)) > (32 << 20)
+    lay = (ic.ic_layer * 1)(ic.ic_layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    rmap = (ctypes.c_int32 * 1)(0)
+    st = ic._lib.ic_layer_stack_static(1, lay, rmap, ctypes.byref(qs), ctypes.byref(d), 0.1, FAKE, None, None)
+    assert st == ic.IC_ERR_WORKSPACE
+    assert b"32" in ic._lib.ic_last_error() or b"33554432" in ic._lib.ic_last_error()
+    bad = (ctypes.c_int32 * 2)(1, 1)
+    assert ic._lib.ic_layer_stack_static(2, lay, bad, ctypes.byref(qs), ctypes.byref(d), 0.1, FAKE, None, None) \
+        == ic.IC_ERR_REUSE_MAP
 
 
 def test_reuse_map_matches_oracle_rule(ic):
