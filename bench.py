@@ -75,19 +75,92 @@ def indexer_flops(n: int, H_I: int, D_I: int) -> int:
     return 2 * H_I * D_I * n
 
 
+# source files whose text a kernel's counters were taken on
+KERNEL_SOURCES = {
+    "indexer_decode_kernel": ["indexer.hip", "radix_key.h"],
+    "indexer_prefill_kernel": ["indexer.hip"],
+    "sparse_mla_kernel": ["sparse_mla.hip", "select.h"],
+    "sparse_mla_kernel<selecting>": ["sparse_mla.hip", "select.h"],
+    "mla_combine_kernel": ["sparse_mla.hip"],
+    "topk_collect_kernel": ["topk.hip", "select.h", "radix_key.h"],
+    "topk_finish_kernel": ["topk.hip", "select.h", "radix_key.h"],
+    "topk_row_kernel": ["topk.hip", "select.h", "radix_key.h"],
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        h.update(open(os.path.join(ROOT, "cross_layer_index_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source (else None)."""
+    summaries (FETCH_SIZE and WRITE_SIZE, calibrated), if they were taken on
+    the kernel's current source (else None)."""
     import glob
-    import hashlib
     import re
-    src = os.path.join(ROOT, "cross_layer_index_amd", "csrc", "indexer.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = source_digest(kernel)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for m in re.finditer(r"<!-- traffic: (.*?) -->", open(path).read()):
             f = dict(kv.split("=", 1) for kv in m.group(1).split())
             if f.get("kernel") == kernel and f.get("workload") == workload and f.get("source_sha256") == digest:
                 return float(f["bytes_per_launch"])
+    return None
+
+
+def kernel_work(name: str, wl, nn, full: bool, splits_combined: bool):
+    """Algorithmic bytes and flops of one launch of kernel `name` in one layer
+    of the workload (the per-query-layer bytes of the method, split among the
+    kernels that move them: score round trips, split partials and survivor
+    lists are overhead and count nowhere). Returns (bytes, flops, flops_dtype)."""
+    kp = [min(wl.k, x) for x in nn]
+    if name in ("indexer_decode_kernel", "indexer_prefill_kernel"):
+        fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
+        return indexer_launch_bytes(wl, nn), fl, "fp8"
+    if name in ("topk_finish_kernel", "topk_row_kernel"):
+        return 4 * sum(kp), 0, None                              # the index list written
+    if name in ("topk_collect_kernel", "clear_hist0_kernel"):
+        return 0, 0, None
+    if name.startswith("sparse_mla_kernel"):
+        by = sum(4 * x + 2 * wl.D_qk * x for x in kp) + wl.T * wl.H * (2 * wl.D_qk + 4)
+        if name.endswith("<selecting>"):
+            by += 4 * sum(kp)                                    # it writes the layer's index list too
+        if not splits_combined:
+            by += wl.T * wl.H * 2 * wl.D_v                       # the output, when no combine follows
+        fl = sum(wl.H * x * (2 * wl.D_qk + 2 * wl.D_v) for x in kp)
+        return by, fl, "bf16"
+    if name == "mla_combine_kernel":
+        return wl.T * wl.H * 2 * wl.D_v, 0, None
+    return 0, 0, None
+
+
+def gpu_clocks():
+    """Current and peak shader/memory clocks as reported by amd-smi (or
+    rocm-smi), best effort; None when neither tool answers."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except Exception:
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                return {"tool": cmd[0], "clocks": json.loads(r.stdout)}
+            except ValueError:
+                return {"tool": cmd[0], "raw": r.stdout.strip()[:2000]}
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
     return None
 
 
@@ -132,14 +205,64 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode_128k",
                     choices=["decode_128k", "ragged_64", "stack_78", "prefill_1m", "mtp_verify", "tiny_2layer"])
-    ap.add_argument("--sets", type=int, default=None, help="rotating input sets (default 8 for decode_128k)")
+    ap.add_argument("--sets", type=int, default=None, help="rotating input sets (default: enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--kernel-steps", type=int, default=400, help="launches timed for the dominant kernel")
-    ap.add_argument("--only", choices=["all", "step", "indexer", "copy"], default="all",
-                    help="profiling aid: run only the stack steps, only the dominant-kernel launches, or "
-                         "only a plain 256 MiB device copy (the calibration for HBM traffic counters)")
+    ap.add_argument("--trace-steps", type=int, default=None, help="steps traced per kernel (per-kernel table)")
+    ap.add_argument("--no-prefill-indexer", action="store_true",
+                    help="leave out the one-launch prefill indexer figure of the default line")
+    ap.add_argument("--only", choices=["all", "step", "copy", "floor"], default="all",
+                    help="profiling aids: only the timed steps; only a plain 256 MiB device copy (the "
+                         "calibration of the HBM traffic counters); only single-launch 16 MiB reads "
+                         "(the floor of a launch that streams the indexer's key bytes)")
     return ap.parse_args()
+
+
+def only_copy(torch, dev, n):
+    src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(1, n)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": "copy", "bytes_read_per_copy": src.numel() * 4, "copies": n}))
+
+
+def only_floor(torch, dev, steps):
+    """Launches that each read 16 MiB and write 16 KiB (a row-wise max of a
+    [4096, 1024] fp32 tensor: one kernel, no cross-workgroup reduction), over
+    64 rotating buffers (1 GiB, four times the last-level cache), replayed as
+    one HIP graph: the time per launch is the floor of a single launch that
+    streams the decode indexer's 16 MiB of keys."""
+    bufs = [torch.randn((4096, 1024), device=dev) for _ in range(64)]
+    out = torch.empty(4096, device=dev)
+    fns = [lambda b=b: torch.amax(b, dim=1, out=out) for b in bufs]
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s_)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    reps = max(1, steps // len(fns))
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
+    print(json.dumps({"only": "floor", "bytes_read_per_launch": 1 << 24, "launches": reps * len(fns),
+                      "us_per_launch": us, "GB/s": (1 << 24) / us / 1e3,
+                      "hbm_frac": (1 << 24) / us / 1e3 / HBM_PEAK_GBS}))
 
 
 def main():
@@ -157,13 +280,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.only == "copy":
-        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(max(1, args.kernel_steps)):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"only": "copy", "bytes_read_per_copy": src.numel() * 4, "copies": args.kernel_steps}))
-        return
+        return only_copy(torch, dev, max(1, args.steps))
+    if args.only == "floor":
+        return only_floor(torch, dev, args.steps)
     wl = W.WORKLOADS[args.workload]
     n = wl.n_valid()
     nn = [int(x) for x in n.tolist()]
@@ -245,88 +364,151 @@ def main():
                 tails[r].replay()
         return run
 
-    def timed(run, K, W_):
+    def timed(run, K, W_, blocks=1):
+        """Time exactly K steps after W_ warmup steps, as `blocks` runs of
+        consecutive steps between events (one bracketed region in all):
+        returns the wall time, the event time and the per-step ms of each block."""
         run(W_)
-        run(K, prepare=True)           # any graph the timed steps need is built here
+        sizes = [K // blocks + (1 if b < K % blocks else 0) for b in range(blocks)]
+        for sz in set(sizes):
+            run(sz, prepare=True)          # any graph the timed steps need is built here
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
         t0 = time.perf_counter()
-        e0.record()
-        run(K)
-        e1.record()
+        ev[0].record()
+        for b, sz in enumerate(sizes):
+            run(sz)
+            ev[b + 1].record()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+        wall = time.perf_counter() - t0
+        per = [ev[b].elapsed_time(ev[b + 1]) / sizes[b] for b in range(blocks) if sizes[b]]
+        return wall, ev[0].elapsed_time(ev[-1]) * 1e-3, per
+
+    def step_launches(f):
+        """The kernels one step launches, in order (the library's trace)."""
+        tr = ic.Trace(4 * wl.n_layers + 8)
+        with tr:
+            f()
+        torch.cuda.synchronize()
+        return [name for name, _ in tr.read()]
+
+    def kernel_costs(fns, names, full_step_s, K, W_):
+        """Each kernel's cost in the step, measured as the timed step (HIP
+        events around graph replays of the rotating sets) minus the same step
+        with that kernel left out (ic_trace_skip), per launch."""
+        out = {}
+        for name in sorted(set(names)):
+            def skipping(f, name=name):
+                def g():
+                    with ic.SkipKernel(name):
+                        f()
+                return g
+            _, ev, _ = timed(runner([skipping(f) for f in fns]), K, W_)
+            out[name] = (full_step_s - ev / K) / names.count(name)
+        return out
 
     big = wl.name in ("stack_78", "prefill_1m")
     steps = min(args.steps, 20) if big else args.steps
     warm = min(args.warmup, 2) if big else args.warmup
     result = {}
-    if args.only in ("all", "step"):
-        run = runner(sets)
-        el, _ = timed(run, steps, warm)
-        result.update(value=wl.T * wl.n_layers * steps / el, ms_per_step=el * 1e3 / steps)
-        if wl.name == "stack_78":
-            ident = list(range(wl.n_layers))
-            allfull = shared_stacks(ic, sets, ident, qs, d, wl.scale, dev)
-            el2, _ = timed(runner(allfull), steps, warm)
-            result["all_full"] = {"value": wl.T * wl.n_layers * steps / el2, "ms_per_step": el2 * 1e3 / steps,
-                                  "indexer_passes": wl.n_layers}
-            result["indexcache_speedup"] = el2 / el
-            del allfull
-            # reuse-pattern variants: the same stack and inputs under other full-layer sets
-            pats = {}
-            for name, fl in W.REUSE_PATTERNS.items():
-                m = ic.reuse_map_last_full([l in set(fl) for l in range(wl.n_layers)])
-                st = shared_stacks(ic, sets, m, qs, d, wl.scale, dev)
-                elp, _ = timed(runner(st), steps, warm)
-                pats[name] = {"indexer_passes": len(fl), "ms_per_step": elp * 1e3 / steps,
-                              "value": wl.T * wl.n_layers * steps / elp, "speedup_vs_all_full": el2 / elp}
-                del st
-            result["reuse_patterns"] = pats
-            result["reuse_overlap"] = reuse_overlap(ic, W, wl, sets[0], rmap, qs, d, dev)
-
-    # ---- dominant kernel: the indexer, timed alone with events on its stream,
-    # rotating over the key caches of every full layer of every set
-    k_ms = None
-    if args.only in ("all", "indexer"):
-        fulls = [l for l in range(wl.n_layers) if rmap[l] == l]
-        scores = torch.empty((wl.T, ic.score_ld(qs.max_n)), dtype=torch.float32, device=dev)
-
-        def idx_fn(i, l):
-            y = sets[i].layers[l]
-            return lambda: ic.indexer_score(y["q_idx"], y["w"], y["k_idx"], qs, scores)
-
-        fns = [idx_fn(i, l) for i in range(R) for l in fulls]
-        run = runner(fns)
-        _, one = timed(run, 1, 1)
-        ksteps = int(max(10, min(args.kernel_steps, 0.2 / max(one, 1e-6))))
-        ksteps = -(-ksteps // len(fns)) * len(fns)           # whole rotations
-        _, ev = timed(run, ksteps, min(len(fns), ksteps))
-        k_ms = ev * 1e3 / ksteps
-
-    if args.only != "all":
-        print(json.dumps({"only": args.only, "workload": wl.name, **result, "indexer_ms": k_ms}))
+    run = runner(sets)
+    el, ev_s, per = timed(run, steps, warm, blocks=5 if steps >= 5 else 1)
+    result.update(value=wl.T * wl.n_layers * steps / el, ms_per_step=el * 1e3 / steps)
+    per_sorted = sorted(per)
+    result["repeats"] = {"blocks": len(per), "ms_per_step_mean": sum(per) / len(per),
+                         "ms_per_step_median": per_sorted[len(per) // 2], "ms_per_step_min": per_sorted[0],
+                         "ms_per_step_max": per_sorted[-1], "event_ms_per_step": ev_s * 1e3 / steps}
+    if args.only == "step":
+        print(json.dumps({"only": "step", "workload": wl.name, **result}))
         return
+    if wl.name == "stack_78":
+        ident = list(range(wl.n_layers))
+        allfull = shared_stacks(ic, sets, ident, qs, d, wl.scale, dev)
+        el2, _, _ = timed(runner(allfull), steps, warm)
+        result["all_full"] = {"value": wl.T * wl.n_layers * steps / el2, "ms_per_step": el2 * 1e3 / steps,
+                              "indexer_passes": wl.n_layers}
+        result["indexcache_speedup"] = el2 / el
+        del allfull
+        # reuse-pattern variants: the same stack and inputs under other full-layer sets
+        pats = {}
+        for name, fl in W.REUSE_PATTERNS.items():
+            m = ic.reuse_map_last_full([l in set(fl) for l in range(wl.n_layers)])
+            st = shared_stacks(ic, sets, m, qs, d, wl.scale, dev)
+            elp, _, _ = timed(runner(st), steps, warm)
+            pats[name] = {"indexer_passes": len(fl), "ms_per_step": elp * 1e3 / steps,
+                          "value": wl.T * wl.n_layers * steps / elp, "speedup_vs_all_full": el2 / elp}
+            del st
+        result["reuse_patterns"] = pats
+        result["reuse_overlap"] = reuse_overlap(ic, W, wl, sets[0], rmap, qs, d, dev)
 
+    # ---- every kernel of the step: its cost in the graph-replayed step, the
+    # step's time (HIP events) less the time of the same step without it
+    names = step_launches(sets[0])
+    full_step_s = ev_s / steps
+    costs = kernel_costs(sets, names, full_step_s, steps, warm)
     n_full = sum(1 for l in range(wl.n_layers) if rmap[l] == l)
-    if wl.same_seq:
-        fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
-        achieved = fl / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None, "kernel": "indexer_prefill_kernel",
-                "kernel_ms": k_ms, "algorithmic_flops_per_launch": fl}
+    combined = "mla_combine_kernel" in costs
+    table = []
+    for name, sec in costs.items():
+        per_step = names.count(name)
+        us = sec * 1e6
+        by, fl, fdt = kernel_work(name, wl, nn, True, combined)
+        row = {"kernel": name, "launches_per_step": per_step, "us_per_launch": us,
+               "us_per_step": us * per_step, "algorithmic_bytes_per_launch": by}
+        if by and us > 0:
+            row["GB/s"] = by / (us * 1e-6) / 1e9
+            row["hbm_frac"] = row["GB/s"] / HBM_PEAK_GBS
+        if fl and us > 0:
+            peak = FP8_PEAK_TFLOPS if fdt == "fp8" else BF16_PEAK_TFLOPS
+            row["algorithmic_flops_per_launch"] = fl
+            row["TFLOP/s"] = fl / (us * 1e-6) / 1e12
+            row[f"{fdt}_mfma_frac"] = row["TFLOP/s"] / peak
+        table.append(row)
+    table.sort(key=lambda r: -r["us_per_step"])
+    dom = table[0]
+    by, fl, fdt = kernel_work(dom["kernel"], wl, nn, True, combined)
+    mfma_bound = fl and (fl / (FP8_PEAK_TFLOPS if fdt == "fp8" else BF16_PEAK_TFLOPS) / 1e12 >
+                         by / HBM_PEAK_GBS / 1e9)
+    if mfma_bound:
+        peak = FP8_PEAK_TFLOPS if fdt == "fp8" else BF16_PEAK_TFLOPS
+        achieved = fl / (dom["us_per_launch"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": measured_traffic(dom["kernel"], wl.name), "kernel": dom["kernel"],
+                "kernel_ms": dom["us_per_launch"] * 1e-3, "algorithmic_flops_per_launch": fl,
+                "flops_dtype": fdt}
     else:
-        by = indexer_launch_bytes(wl, nn)
-        achieved = by / (k_ms * 1e-3) / 1e9
-        kname = "indexer_prefill_kernel" if wl.group > 1 else "indexer_decode_kernel"
+        achieved = by / (dom["us_per_launch"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kname, wl.name),
-                "kernel": kname, "kernel_ms": k_ms, "algorithmic_bytes_per_launch": by}
-        if wl.group > 1:
-            # a group of m queries does m x 128 flop per key byte: report the
-            # matrix-core side too
-            fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
-            roof["mfma_frac"] = fl / (k_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom["kernel"], wl.name),
+                "kernel": dom["kernel"], "kernel_ms": dom["us_per_launch"] * 1e-3,
+                "algorithmic_bytes_per_launch": by}
+    roof["share_of_step"] = dom["us_per_step"] * 1e-3 / result["ms_per_step"]
+
+    # ---- the chunked-prefill indexer (1M-token cache, 4096 causal queries),
+    # one launch as the prefill workload runs it, timed on the default line
+    pf = None
+    if args.only == "all" and wl.name == "decode_128k" and not args.no_prefill_indexer:
+        pw = W.WORKLOADS["prefill_1m"]
+        pn = pw.n_valid()
+        pqs = ic.make_queries(pw.base(), pn, pw.rows(), True, device=dev)
+        pli = W.layer_inputs(W.scaled(pw, D_qk=8, D_v=8, H=1), 0, device=dev)   # indexer tensors only matter
+        psc = torch.empty((pw.T, ic.score_ld(pqs.max_n)), dtype=torch.float32, device=dev)
+        fn = lambda: ic.indexer_score(pli.q_idx, pli.w, pli.k_idx, pqs, psc)
+        fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        for i in range(3):
+            fn()
+            e[i + 1].record()
+        torch.cuda.synchronize()
+        ms = [e[i].elapsed_time(e[i + 1]) for i in range(3)]
+        pfl = sum(indexer_flops(int(x), pw.H_I, pw.D_I) for x in pn.tolist())
+        pf = {"workload": "prefill_1m indexer (4096 causal queries over 1,048,576 tokens, 64x128 fp8)",
+              "launches": 3, "ms_per_launch": sum(ms) / 3, "ms_min": min(ms),
+              "algorithmic_flops_per_launch": pfl, "TFLOP/s": pfl / (sum(ms) / 3 * 1e-3) / 1e12,
+              "fp8_mfma_frac": pfl / (sum(ms) / 3 * 1e-3) / 1e12 / FP8_PEAK_TFLOPS}
+        del psc, pli
 
     # ---- the step after the path: gated head output (wv_b, sigmoid gate) for
     # this workload's queries, timed alone over rotating inputs
@@ -338,7 +520,7 @@ def main():
         gfns = [lambda x=x: ic.gated_output(x.o, x.wv_b, x.gate, out=gouts) for x in gsets]
         grun = runner(gfns)
         gk = 8 * NG
-        _, gev = timed(grun, gk, NG)
+        _, gev, _ = timed(grun, gk, NG)
         g_s = gev / gk
         gbytes = 2 * (wl.H * D_o * wl.D_v + wl.T * wl.H * (wl.D_v + 2 * D_o))
         gflops = 2 * wl.T * wl.H * D_o * wl.D_v
@@ -355,24 +537,24 @@ def main():
     if args.only == "all" and wl.D_v == 512 and wl.name in ("decode_128k", "mtp_verify", "ragged_64", "prefill_1m"):
         NW = 8
         D_rope = W.d_rope(wl)
-        table = W.rope_table(max(1, max(nn)), D_rope).to(dev)
+        table_r = W.rope_table(max(1, max(nn)), D_rope).to(dev)
         kc = torch.empty((wl.T, wl.D_I), dtype=torch.uint8, device=dev)
         kvc = torch.empty((wl.T, wl.D_qk), dtype=torch.bfloat16, device=dev)
         dst = torch.arange(wl.T, dtype=torch.int64, device=dev)
         wfns = []
         for i in range(NW):
-            x = W.write_inputs(wl, i, device=dev, rope=table)
-            tk = ic.Tokens(dst, x.pos, wl.T, table)
+            x = W.write_inputs(wl, i, device=dev, rope=table_r)
+            tk = ic.Tokens(dst, x.pos, wl.T, table_r)
             wfns.append(lambda x=x, tk=tk: ic.write_cache(tk, x.k_pre, x.ln_w, x.ln_b, x.eps, kc, x.kv_pre, kvc))
         wk = 8 * NW
-        _, wev = timed(runner(wfns), wk, NW)
+        _, wev, _ = timed(runner(wfns), wk, NW)
         w_s = wev / wk
         per_tok = 3 * wl.D_I + 4 * wl.D_qk + 4 * D_rope + 12
         wbytes = wl.T * per_tok + 8 * wl.D_I
         wpath = {"T": wl.T, "D_I": wl.D_I, "D_qk": wl.D_qk, "D_rope": D_rope, "us": w_s * 1e6,
                  "bytes_per_token": per_tok, "GB/s": wbytes / w_s / 1e9,
                  "hbm_frac": wbytes / w_s / 1e9 / HBM_PEAK_GBS}
-        del wfns, table
+        del wfns, table_r
 
     # ---- CPU baseline: the oracle on this host, on a bounded sample
     cpu = None
@@ -382,6 +564,7 @@ def main():
         if host0 is not None:
             x, base, nv, layers_used, qn = host0, wl.base().numpy(), n.numpy(), wl.n_layers, wl.T
             sample = f"full passes of input set 0 ({wl.n_layers} layer(s) x {wl.T} queries)"
+            rm = rmap
         else:
             # one query through a full and a shared layer, copied back from the device
             import numpy as np
@@ -402,21 +585,20 @@ def main():
                 o.k_idx = y["k_idx"][rows].cpu() if j == 0 else None
                 o.q, o.kv, o.sink = y["q"][t:t + 1].cpu(), y["kv"][rows].cpu(), y["sink"].cpu()
                 x.append(o)
-            rmap_s = [0] + ([0] if l_sh is not None else [])
+            rm = [0] + ([0] if l_sh is not None else [])
             base, nv, layers_used, qn = np.array([0], np.int64), np.array([nn[t]], np.int32), len(used), 1
-            rmap_cpu = rmap_s
             sample = (f"query 0 through a full{' and a shared' if l_sh is not None else ''} layer "
                       f"(L={nn[t]}), repeated")
-        rm = rmap if host0 is not None else rmap_cpu
-        reps, t0 = 0, time.perf_counter()
+        reps_c, t0 = 0, time.perf_counter()
         while True:
             oracle.layer_stack(x, rm, base, nv, wl.k, wl.scale, wl.D_v)
-            reps += 1
+            reps_c += 1
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
-        el = time.perf_counter() - t0
-        cpu = {"value": reps * qn * layers_used / el, "unit": "query-layers/s", "cores": threads, "kind": "oracle",
-               "sample": f"{reps} x {sample} through the C oracle (fp64, OpenMP, {threads} threads)"}
+        el_c = time.perf_counter() - t0
+        cpu = {"value": reps_c * qn * layers_used / el_c, "unit": "query-layers/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{reps_c} x {sample} through the C oracle (fp64, OpenMP, {threads} threads)"}
 
     line = {
         "metric": METRIC if wl.name == "decode_128k" else f"{wl.name} query-layers/s (index+topk+sparse MLA)",
@@ -436,6 +618,13 @@ def main():
                    "D_qk": wl.D_qk, "D_v": wl.D_v, "rotating_sets": R},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "repeats": result["repeats"],
+        "kernels": table,
+        "kernel_costs": {"launches_per_step": len(names), "step_us_events": full_step_s * 1e6,
+                         "sum_of_kernel_us": sum(r["us_per_step"] for r in table),
+                         "method": "per kernel: (timed step - the same step with that kernel left out, "
+                                   "ic_trace_skip) / launches, both timed with HIP events around graph "
+                                   "replays of the rotating input sets"},
     }
     if not wl.same_seq:
         # per-query byte counts hold only where queries read caches of their own;
@@ -445,13 +634,18 @@ def main():
         # a draft/verify group streams its sequence's keys once
         step_bytes -= n_full * (sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn) - indexer_launch_bytes(wl, nn))
         line["step_hbm_frac"] = step_bytes / (result["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        line["step_algorithmic_bytes"] = step_bytes
     for k2 in ("all_full", "indexcache_speedup", "reuse_patterns", "reuse_overlap"):
         if k2 in result:
             line[k2] = result[k2]
+    if pf is not None:
+        line["prefill_indexer"] = pf
     if gate is not None:
         line["gated_output"] = gate
     if wpath is not None:
         line["write_path"] = wpath
+    line["host"] = {"cpu_model": cpu_model(), "threads": len(os.sched_getaffinity(0))}
+    line["gpu"] = {"name": torch.cuda.get_device_name(dev), "clocks": gpu_clocks()}
     print(json.dumps(line))
 
 

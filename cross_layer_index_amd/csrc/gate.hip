@@ -197,18 +197,21 @@ hipError_t launch_gated_output(const uint16_t *o, const uint16_t *wv_b, const ui
 #define IC_GATE_LAUNCH(DVV, NTT)                                                                                  \
     hipLaunchKernelGGL((gated_output_kernel<DVV, NTT>), grid, dim3(NTT), 0, stream, o, wv_b, gate, T, H, D_o,     \
                        blocks, out)
-    if (D_v == 512) {
-        if (narrow)
-            IC_GATE_LAUNCH(512, 256);
-        else
-            IC_GATE_LAUNCH(512, 512);
-    } else {
-        if (narrow)
-            IC_GATE_LAUNCH(64, 256);
-        else
-            IC_GATE_LAUNCH(64, 512);
+    if (!trace_skip("gated_output_kernel")) {
+        if (D_v == 512) {
+            if (narrow)
+                IC_GATE_LAUNCH(512, 256);
+            else
+                IC_GATE_LAUNCH(512, 512);
+        } else {
+            if (narrow)
+                IC_GATE_LAUNCH(64, 256);
+            else
+                IC_GATE_LAUNCH(64, 512);
+        }
     }
 #undef IC_GATE_LAUNCH
+    trace_launch(stream, "gated_output_kernel");
     return hipGetLastError();
 }
 

@@ -6,7 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <array>
 #include <mutex>
+#include <new>
+#include <vector>
 
 #include "kernels.h"
 
@@ -15,6 +18,16 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+
+// Tracing state of the calling thread (ic_trace_start / ic_trace_stop).
+constexpr int kTraceNameLen = IC_TRACE_NAME_LEN;
+struct Trace {
+    ic_trace *tr = nullptr;          // armed trace; null = disarmed
+    int32_t count = 0;               // launches seen since ic_trace_start
+    hipError_t error = hipSuccess;
+};
+thread_local Trace g_trace;
+thread_local char g_trace_skip[IC_TRACE_NAME_LEN] = "";   // kernel left out ("" = none)
 
 // Scratch memory of ic_layer_stack_static: a file-scope device array, one copy
 // per GPU, resident while the library is loaded. Host code never uses the
@@ -258,6 +271,131 @@ hipError_t launch_indexer(const uint8_t *q_idx, const float *w, const uint8_t *k
 }
 
 }  // namespace
+
+// A trace: its events (the start mark, then one per launch) and the names.
+struct ic_trace {
+    std::vector<hipEvent_t> events;
+    std::vector<std::array<char, kTraceNameLen>> names;
+    int32_t recorded = 0;            // launches of the last armed period with an event
+};
+
+namespace {
+// An event record that stays a timestamp under stream capture (an external
+// event node in the graph), a plain record otherwise.
+hipError_t trace_record(hipEvent_t ev, hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess)
+        return e;
+    return cs == hipStreamCaptureStatusActive ? hipEventRecordWithFlags(ev, stream, hipEventRecordExternal)
+                                              : hipEventRecord(ev, stream);
+}
+}  // namespace
+
+void ic::trace_launch(hipStream_t stream, const char *kernel)
+{
+    Trace &st = g_trace;
+    if (!st.tr)
+        return;
+    ic_trace &tr = *st.tr;
+    if ((size_t)st.count + 1 < tr.events.size()) {
+        const hipError_t e = trace_record(tr.events[st.count + 1], stream);
+        if (e != hipSuccess && st.error == hipSuccess)
+            st.error = e;
+        snprintf(tr.names[st.count].data(), kTraceNameLen, "%s", kernel);
+        tr.recorded = st.count + 1;
+    }
+    ++st.count;
+}
+
+bool ic::trace_skip(const char *kernel)
+{
+    return g_trace_skip[0] != '\0' && strcmp(g_trace_skip, kernel) == 0;
+}
+
+IC_EXPORT ic_status ic_trace_skip(const char *kernel)
+{
+    if (kernel && strlen(kernel) >= sizeof g_trace_skip)
+        return fail(IC_ERR_SHAPE, "trace: kernel name longer than %d", IC_TRACE_NAME_LEN - 1);
+    snprintf(g_trace_skip, sizeof g_trace_skip, "%s", kernel ? kernel : "");
+    return ok();
+}
+
+IC_EXPORT ic_status ic_trace_create(int32_t capacity, ic_trace **out)
+{
+    if (!out || capacity < 1 || capacity > (1 << 20))
+        return fail(IC_ERR_SHAPE, "trace: capacity=%d outside [1, 2^20] or no output pointer", capacity);
+    *out = nullptr;
+    ic_trace *tr = new (std::nothrow) ic_trace;
+    if (!tr)
+        return fail(IC_ERR_HIP, "trace: out of host memory");
+    tr->names.resize(capacity);
+    for (int32_t i = 0; i <= capacity; ++i) {
+        hipEvent_t ev = nullptr;
+        const hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+            ic_trace_destroy(tr);
+            return fail(IC_ERR_HIP, "trace: hipEventCreate: %s", hipGetErrorString(e));
+        }
+        tr->events.push_back(ev);
+    }
+    *out = tr;
+    return ok();
+}
+
+IC_EXPORT void ic_trace_destroy(ic_trace *tr)
+{
+    if (!tr)
+        return;
+    if (g_trace.tr == tr)
+        g_trace = Trace{};
+    for (hipEvent_t ev : tr->events)
+        (void)hipEventDestroy(ev);
+    delete tr;
+}
+
+IC_EXPORT ic_status ic_trace_start(ic_trace *tr, void *stream)
+{
+    if (!tr)
+        return fail(IC_ERR_NULL, "trace: no trace");
+    const hipError_t e = trace_record(tr->events[0], reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(IC_ERR_HIP, "trace: start mark: %s", hipGetErrorString(e));
+    tr->recorded = 0;
+    g_trace = Trace{tr, 0, hipSuccess};
+    return ok();
+}
+
+IC_EXPORT int32_t ic_trace_stop(void)
+{
+    const int32_t n = g_trace.count;
+    const hipError_t e = g_trace.error;
+    g_trace = Trace{};
+    if (e != hipSuccess) {
+        fail(IC_ERR_HIP, "trace: hipEventRecord: %s", hipGetErrorString(e));
+        return -1;
+    }
+    return n;
+}
+
+IC_EXPORT ic_status ic_trace_read(const ic_trace *tr, float *us, char *names, int32_t n)
+{
+    if (!tr || !us)
+        return fail(IC_ERR_NULL, "trace: trace and us are required");
+    if (n < 0 || n > tr->recorded)
+        return fail(IC_ERR_SHAPE, "trace: %d launches asked, %d recorded", n, tr->recorded);
+    for (int32_t i = 0; i < n; ++i) {
+        float ms = 0.0f;
+        const hipError_t e = hipEventElapsedTime(&ms, tr->events[i], tr->events[i + 1]);
+        if (e != hipSuccess)
+            return fail(IC_ERR_HIP, "trace: launch %d: hipEventElapsedTime: %s", i, hipGetErrorString(e));
+        us[i] = ms * 1000.0f;
+        if (names)
+            memcpy(names + (size_t)i * kTraceNameLen, tr->names[i].data(), kTraceNameLen);
+    }
+    return ok();
+}
 
 IC_EXPORT const char *ic_status_str(ic_status s)
 {

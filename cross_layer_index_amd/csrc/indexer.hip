@@ -254,13 +254,15 @@ hipError_t launch_decode_di(const uint8_t *q_idx, const float *w, const uint8_t 
     // two-group steps.
     const bool one = chunk == kIdxStep;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx, base, n, H_I, scores, ld, chunk,
+        if (!trace_skip("indexer_decode_kernel"))
+            hipLaunchKernelGGL(kern, grid, dim3(kIdxThreads), 0, stream, q_idx, w, k_idx, base, n, H_I, scores, ld, chunk,
                            hist0);
     };
     if (H_I <= 32)
         one ? go(indexer_decode_kernel<DI, 1, 1>) : go(indexer_decode_kernel<DI, 1, 2>);
     else
         one ? go(indexer_decode_kernel<DI, 2, 1>) : go(indexer_decode_kernel<DI, 2, 2>);
+    trace_launch(stream, "indexer_decode_kernel");
     return hipGetLastError();
 }
 
@@ -493,7 +495,9 @@ hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const ui
     if (groups > 65535)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)nchunks, (unsigned)groups);
-    if (P == 1)
+    if (trace_skip("indexer_prefill_kernel"))
+        ;
+    else if (P == 1)
         hipLaunchKernelGGL(indexer_prefill_kernel<1>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
                            T, G, scores, ld, chunk);
     else if (P == 2)
@@ -505,6 +509,7 @@ hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const ui
     else
         hipLaunchKernelGGL(indexer_prefill_kernel<8>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
                            T, G, scores, ld, chunk);
+    trace_launch(stream, "indexer_prefill_kernel");
     return hipGetLastError();
 }
 

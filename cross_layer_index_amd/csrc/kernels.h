@@ -8,6 +8,14 @@
 
 namespace ic {
 
+// Tracing hook (a profiling aid): after a kernel launch, records the next of
+// the caller's trace events on `stream` when tracing is armed on the calling
+// thread (ic_trace_start in ic.h), and keeps the kernel's name.
+void trace_launch(hipStream_t stream, const char *kernel);
+// Whether launches of `kernel` are left out on the calling thread
+// (ic_trace_skip; a profiling aid: the step's time without that kernel).
+bool trace_skip(const char *kernel);
+
 // ---- indexer --------------------------------------------------------------
 // Decode form: each query streams its own key rows (no reuse across queries).
 // With `hist0` non-null, also adds each score's first radix digit (bits 31..21

@@ -807,18 +807,23 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
         part_o = reinterpret_cast<uint16_t *>(ws);
         part_ml = reinterpret_cast<float *>(part_o + (size_t)T * plan.splits * H * DV);
     }
-    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
+    if (!trace_skip(SEL ? "sparse_mla_kernel<selecting>" : "sparse_mla_kernel"))
+        hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
                        q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
                        out_f32, part_o, part_ml, (int32_t)plan.direct_parts, sa);
+    trace_launch(stream, SEL ? "sparse_mla_kernel<selecting>" : "sparse_mla_kernel");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
         return e;
-    if (plan.splits > kCombineBatchMax / 2)
+    if (trace_skip("mla_combine_kernel"))
+        ;
+    else if (plan.splits > kCombineBatchMax / 2)
         hipLaunchKernelGGL((mla_combine_kernel<DV, kCombineBatchMax>), dim3(H, T), dim3(DV / 4), 0, stream, part_o,
                            part_ml, sink, H, plan.splits, out, out_f32);
     else
         hipLaunchKernelGGL((mla_combine_kernel<DV, kCombineBatchMax / 2>), dim3(H, T), dim3(DV / 4), 0, stream, part_o,
                            part_ml, sink, H, plan.splits, out, out_f32);
+    trace_launch(stream, "mla_combine_kernel");
     return hipGetLastError();
 }
 

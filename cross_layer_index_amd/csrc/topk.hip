@@ -586,8 +586,10 @@ hipError_t launch_clear_hist0(void *ws, int32_t T, hipStream_t stream)
     if (n4 == 0)
         return hipSuccess;
     const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 1024);
-    hipLaunchKernelGGL(clear_hist0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+    if (!trace_skip("clear_hist0_kernel"))
+        hipLaunchKernelGGL(clear_hist0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<uint4 *>(ws), n4);
+    trace_launch(stream, "clear_hist0_kernel");
     return hipGetLastError();
 }
 
@@ -614,10 +616,13 @@ hipError_t launch_topk_collect(const float *scores, int64_t ld, const int32_t *n
     if (!L.split)
         return hipErrorInvalidValue;
     char *base = static_cast<char *>(ws);
-    hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream, scores,
+    if (!trace_skip("topk_collect_kernel"))
+        if (!trace_skip("topk_collect_kernel"))
+            hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream, scores,
                        ld, n, max_n, k, reinterpret_cast<uint32_t *>(base + L.counts_off),
                        reinterpret_cast<uint64_t *>(base + L.regions_off),
                        reinterpret_cast<uint32_t *>(base + L.bounds_off));
+    trace_launch(stream, "topk_collect_kernel");
     return hipGetLastError();
 }
 
@@ -633,17 +638,23 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
         uint32_t *counts = reinterpret_cast<uint32_t *>(base + L.counts_off);
         uint64_t *regions = reinterpret_cast<uint64_t *>(base + L.regions_off);
         uint32_t *bounds = reinterpret_cast<uint32_t *>(base + L.bounds_off);
-        hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream,
+        if (!trace_skip("topk_collect_kernel"))
+            hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream,
                            scores, ld, n, max_n, k, counts, regions, bounds);
+        trace_launch(stream, "topk_collect_kernel");
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
         // (the split path builds no first-digit histogram: a producer fills none)
-        hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kFinishThreads), 0, stream, scores, ld, n,
+        if (!trace_skip("topk_finish_kernel"))
+            hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)T), dim3(kFinishThreads), 0, stream, scores, ld, n,
                            k, idx, counts, regions, (int32_t)L.P, bounds);
+        trace_launch(stream, "topk_finish_kernel");
     } else {
-        hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
+        if (!trace_skip("topk_row_kernel"))
+            hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
                            hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));
+        trace_launch(stream, "topk_row_kernel");
     }
     return hipGetLastError();
 }

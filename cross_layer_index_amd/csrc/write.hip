@@ -145,8 +145,10 @@ hipError_t launch_write_cache(const int64_t *row, const int32_t *pos, int32_t T,
     if (T <= 0)
         return hipSuccess;
     const dim3 grid((unsigned)((T + kWriteTokens - 1) / kWriteTokens));
-    hipLaunchKernelGGL(write_cache_kernel, grid, dim3(kWriteThreads), 0, stream, row, pos, T, rows, rope, n_pos,
+    if (!trace_skip("write_cache_kernel"))
+        hipLaunchKernelGGL(write_cache_kernel, grid, dim3(kWriteThreads), 0, stream, row, pos, T, rows, rope, n_pos,
                        D_rope, key_rope, k_pre, ln_w, ln_b, eps, D_I, k_idx, kv_pre, D_qk, kv);
+    trace_launch(stream, "write_cache_kernel");
     return hipGetLastError();
 }
 

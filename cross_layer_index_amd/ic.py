@@ -62,6 +62,12 @@ _SIGS = {
                         _P], _i32),
     "ic_layer_stack_static": ([_i32, ctypes.POINTER(ic_layer), _P, _QP, _DP, _f32, _P, ctypes.POINTER(_i32), _P],
                               _i32),
+    "ic_trace_create": ([_i32, ctypes.POINTER(_P)], _i32),
+    "ic_trace_destroy": ([_P], None),
+    "ic_trace_start": ([_P, _P], _i32),
+    "ic_trace_stop": ([], _i32),
+    "ic_trace_read": ([_P, ctypes.POINTER(ctypes.c_float), ctypes.c_char_p, _i32], _i32),
+    "ic_trace_skip": ([ctypes.c_char_p], _i32),
     "ic_status_str": ([_i32], ctypes.c_char_p),
     "ic_last_error": ([], ctypes.c_char_p),
 }
@@ -372,6 +378,67 @@ class LayerStack:
                                           self.scale, _ptr(self.index_cache), ctypes.byref(self.passes),
                                           _stream(stream)))
         return self.passes.value
+
+
+class Trace:
+    """Times every kernel the library launches on this thread while active
+    (ic_trace_start / ic_trace_stop): ``with tr: ...`` records the start mark
+    on the current stream and one event after each launch; after the stream
+    has run them, ``tr.read()`` gives [(kernel name, microseconds)] per launch.
+    Inside HIP-graph capture the events become timestamp nodes of the graph
+    where the HIP runtime supports external event records."""
+
+    NAME_LEN = 48
+
+    def __init__(self, capacity: int):
+        h = _P()
+        _check(_lib.ic_trace_create(int(capacity), ctypes.byref(h)))
+        self._h = h
+        self.capacity = int(capacity)
+        self.count = 0
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _lib.ic_trace_destroy(self._h)
+            self._h = None
+
+    def __enter__(self):
+        _check(_lib.ic_trace_start(self._h, _stream(None)))
+        return self
+
+    def __exit__(self, *exc):
+        n = _lib.ic_trace_stop()
+        if n < 0:
+            raise ICError(IC_ERR_HIP, _lib.ic_last_error().decode())
+        self.count = n
+        return False
+
+    def read(self):
+        n = min(self.count, self.capacity)
+        us = (ctypes.c_float * max(n, 1))()
+        names = ctypes.create_string_buffer(self.NAME_LEN * max(n, 1))
+        _check(_lib.ic_trace_read(self._h, us, names, n))
+        raw = names.raw
+        return [(raw[i * self.NAME_LEN:(i + 1) * self.NAME_LEN].split(b"\0", 1)[0].decode(), float(us[i]))
+                for i in range(n)]
+
+
+class SkipKernel:
+    """``with SkipKernel(name): ...`` leaves out every launch of kernel
+    `name` on this thread (ic_trace_skip): a profiling aid that gives a
+    kernel's cost in a step as the step's time without it. Results computed
+    inside are wrong by design."""
+
+    def __init__(self, kernel: str):
+        self.kernel = kernel
+
+    def __enter__(self):
+        _check(_lib.ic_trace_skip(self.kernel.encode()))
+        return self
+
+    def __exit__(self, *exc):
+        _check(_lib.ic_trace_skip(None))
+        return False
 
 
 def layer_stack(layers, reuse_map, qs: Queries, d: ic_dims, scale: float):

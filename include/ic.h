@@ -253,6 +253,35 @@ ic_status ic_layer_stack_static(int32_t n_layers, const ic_layer *layers, const 
                                 const ic_queries *qs, const ic_dims *d, float scale,
                                 int32_t *index_cache, int32_t *indexer_passes, void *stream);
 
+/* Tracing, a profiling aid outside the computation. A trace owns timing
+ * HIP events: ic_trace_create makes one with room for `capacity` launches
+ * (host memory and capacity + 1 events; not under stream capture).
+ * ic_trace_start records the start mark on `stream` and arms the calling
+ * thread: from then on, right after the i-th kernel the library launches (in
+ * any call on this thread, i counting from 0, while i < capacity) it records
+ * the trace's event i + 1 on that launch's stream and keeps the kernel's name.
+ * Under HIP graph capture the records are made as external event nodes of
+ * the graph (each replay timestamps them) where the HIP runtime in use
+ * supports that; otherwise ic_trace_start returns IC_ERR_HIP. ic_trace_stop disarms and returns
+ * the number of launches seen (which may exceed capacity), or -1 if an event
+ * record failed (ic_last_error() says why). Once the stream has reached the
+ * last event, ic_trace_read gives the time of launches 0..n-1 in
+ * microseconds (event i to event i + 1: the kernel's time on its stream) and,
+ * if `names` is not NULL, their kernel names in names + 48 * i
+ * (NUL-terminated). Tracing never changes what a call computes. */
+#define IC_TRACE_NAME_LEN 48
+typedef struct ic_trace ic_trace;
+ic_status ic_trace_create(int32_t capacity, ic_trace **trace);
+void ic_trace_destroy(ic_trace *trace);
+ic_status ic_trace_start(ic_trace *trace, void *stream);
+int32_t ic_trace_stop(void);
+ic_status ic_trace_read(const ic_trace *trace, float *us, char *names, int32_t n);
+/* Leave out every launch of the named kernel (one of the names the trace
+ * reports) on the calling thread until called again (NULL: launch all). A
+ * profiling aid only: the calls then compute wrong results; timing a step
+ * with and without a kernel gives that kernel's cost in the step. */
+ic_status ic_trace_skip(const char *kernel);
+
 /* Human-readable name of a status, and the detail of the last failure on the
  * calling thread (empty string if none). Both return static storage. */
 const char *ic_status_str(ic_status s);

@@ -28,7 +28,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(ic):
     names = declared_entry_points()
-    assert len(names) == 13
+    assert len(names) == 19
     for n in names:
         assert hasattr(ic._lib, n), n
     assert sorted(ic.EXPORTED) == names

@@ -496,3 +496,43 @@ def test_gated_output_prefill_sampled(gpu, orc):
     for t in (0, 15, 16, 2047, 4095):
         ref = orc.gated_output(gi.o[t:t + 1].cpu(), gi.wv_b.cpu(), gi.gate[t:t + 1].cpu())
         assert_gated(got[t:t + 1], ref, f"gated output prefill query {t}")
+
+
+def test_trace_records_every_launch(gpu):
+    """Tracing (ic_trace_start) names and times every kernel of a layer stack
+    and leaves its results unchanged; leaving a kernel out (ic_trace_skip,
+    the per-kernel cost measurement) still reports its launches, and the
+    stack computes the reference again once the switch is cleared."""
+    wl = W.scaled(W.WORKLOADS["decode_128k"], lengths=[20000], n_layers=3, full_layers=[0, 2])
+    rmap = gpu.reuse_map_last_full(wl.is_full())
+    lays = []
+    for l in range(wl.n_layers):
+        y = dev(W.layer_inputs(wl, l, with_indexer=rmap[l] == l))
+        lays.append(dict(q_idx=y.q_idx, w=y.w, k_idx=y.k_idx, q=y.q, kv=y.kv, sink=y.sink,
+                         out=torch.empty((wl.T, wl.H, wl.D_v), dtype=torch.bfloat16, device="cuda")))
+    st = gpu.LayerStack(lays, rmap, qs_of(gpu, wl), gpu.dims(wl.H_I, wl.D_I, wl.k, wl.H, wl.D_qk, wl.D_v),
+                        wl.scale)
+    st()
+    torch.cuda.synchronize()
+    ref = [y["out"].clone() for y in lays]
+    tr = gpu.Trace(32)
+    with tr:
+        st()
+    torch.cuda.synchronize()
+    ks = tr.read()
+    names = [k[0] for k in ks]
+    assert tr.count == len(names) >= wl.n_layers
+    assert names.count("indexer_decode_kernel") == 2
+    assert sum(n.startswith("sparse_mla_kernel") for n in names) == 3
+    assert all(k[1] > 0 for k in ks)
+    for l, y in enumerate(lays):
+        assert torch.equal(y["out"], ref[l])
+    tr2 = gpu.Trace(32)
+    with gpu.SkipKernel("mla_combine_kernel"), tr2:
+        st()
+    torch.cuda.synchronize()
+    assert [k[0] for k in tr2.read()] == names
+    st()
+    torch.cuda.synchronize()
+    for l, y in enumerate(lays):
+        assert torch.equal(y["out"], ref[l]), f"layer {l} after the skip switch was cleared"
