@@ -228,14 +228,15 @@ def only_copy(torch, dev, n):
 
 
 def only_floor(torch, dev, steps):
-    """Launches that each read 16 MiB and write 16 KiB (a row-wise max of a
-    [4096, 1024] fp32 tensor: one kernel, no cross-workgroup reduction), over
-    64 rotating buffers (1 GiB, four times the last-level cache), replayed as
-    one HIP graph: the time per launch is the floor of a single launch that
-    streams the decode indexer's 16 MiB of keys."""
-    bufs = [torch.randn((4096, 1024), device=dev) for _ in range(64)]
-    out = torch.empty(4096, device=dev)
-    fns = [lambda b=b: torch.amax(b, dim=1, out=out) for b in bufs]
+    """Single launches that each read 16 MiB once in plain coalesced loads and
+    do nothing else (ic_stream_read), over 64 rotating buffers (1 GiB, four
+    times the last-level cache), replayed as one HIP graph: the time per
+    launch is the floor of a single launch streaming the decode indexer's
+    16 MiB of keys."""
+    from cross_layer_index_amd import ic
+    bufs = [torch.randint(0, 255, (1 << 24,), dtype=torch.uint8, device=dev) for _ in range(64)]
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    fns = [lambda b=b: ic.stream_read(b, sink) for b in bufs]
     for f in fns:
         f()
     torch.cuda.synchronize()
@@ -260,8 +261,8 @@ def only_floor(torch, dev, steps):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
-    print(json.dumps({"only": "floor", "bytes_read_per_launch": 1 << 24, "launches": reps * len(fns),
-                      "us_per_launch": us, "GB/s": (1 << 24) / us / 1e3,
+    print(json.dumps({"only": "floor", "kernel": "stream_read_kernel", "bytes_read_per_launch": 1 << 24,
+                      "launches": reps * len(fns), "us_per_launch": us, "GB/s": (1 << 24) / us / 1e3,
                       "hbm_frac": (1 << 24) / us / 1e3 / HBM_PEAK_GBS}))
 
 

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libic.so")
 
-SOURCES = ["ic_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "gate.hip", "write.hip"]
+SOURCES = ["ic_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "gate.hip", "write.hip", "calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

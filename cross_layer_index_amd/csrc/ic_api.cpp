@@ -314,6 +314,20 @@ bool ic::trace_skip(const char *kernel)
     return g_trace_skip[0] != '\0' && strcmp(g_trace_skip, kernel) == 0;
 }
 
+IC_EXPORT ic_status ic_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes < 0 || bytes % 16)
+        return fail(IC_ERR_SHAPE, "stream read: bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+    if (bytes == 0)
+        return ok();
+    if (!src || !sink)
+        return fail(IC_ERR_NULL, "stream read: src and sink are required");
+    if (!aligned16(src) || !aligned16(sink))
+        return fail(IC_ERR_ALIGN, "stream read: pointers must be 16-byte aligned");
+    return hip_status(ic::launch_stream_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream)),
+                      "stream read launch");
+}
+
 IC_EXPORT ic_status ic_trace_skip(const char *kernel)
 {
     if (kernel && strlen(kernel) >= sizeof g_trace_skip)

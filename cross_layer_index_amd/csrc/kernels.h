@@ -107,4 +107,8 @@ hipError_t launch_write_cache(const int64_t *row, const int32_t *pos, int32_t T,
                               const float *ln_w, const float *ln_b, float eps, int32_t D_I, uint8_t *k_idx,
                               const uint16_t *kv_pre, int32_t D_qk, uint16_t *kv, hipStream_t stream);
 
+// Calibration: one pass of plain coalesced 16-byte reads over `bytes` of src
+// (sink: 64 words that are never written for real data).
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+
 }  // namespace ic

@@ -68,6 +68,7 @@ _SIGS = {
     "ic_trace_stop": ([], _i32),
     "ic_trace_read": ([_P, ctypes.POINTER(ctypes.c_float), ctypes.c_char_p, _i32], _i32),
     "ic_trace_skip": ([ctypes.c_char_p], _i32),
+    "ic_stream_read": ([_P, _i64, _P, _P], _i32),
     "ic_status_str": ([_i32], ctypes.c_char_p),
     "ic_last_error": ([], ctypes.c_char_p),
 }
@@ -421,6 +422,15 @@ class Trace:
         raw = names.raw
         return [(raw[i * self.NAME_LEN:(i + 1) * self.NAME_LEN].split(b"\0", 1)[0].decode(), float(us[i]))
                 for i in range(n)]
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """One launch reading all of ``src`` once (calibration: the floor of a
+    launch streaming that many bytes); ``sink`` is 64 int32 on the device."""
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _dev(sink, torch.int32, "sink")
+    _check(_lib.ic_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)))
 
 
 class SkipKernel:

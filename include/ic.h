@@ -282,6 +282,13 @@ ic_status ic_trace_read(const ic_trace *trace, float *us, char *names, int32_t n
  * with and without a kernel gives that kernel's cost in the step. */
 ic_status ic_trace_skip(const char *kernel);
 
+/* Calibration, a measurement aid outside the computation: one launch that
+ * reads `bytes` (a multiple of 16) of device memory at src once, in plain
+ * coalesced 16-byte loads, and does nothing else (sink: 64 device words, 16-byte
+ * aligned, never written for real data). Its time is the floor of a single
+ * launch that streams that many bytes, e.g. the decode indexer's keys. */
+ic_status ic_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
 /* Human-readable name of a status, and the detail of the last failure on the
  * calling thread (empty string if none). Both return static storage. */
 const char *ic_status_str(ic_status s);

@@ -28,7 +28,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(ic):
     names = declared_entry_points()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(ic._lib, n), n
     assert sorted(ic.EXPORTED) == names
@@ -147,6 +147,17 @@ def test_static_stack_rejects_oversized_workspace(ic):
     bad = (ctypes.c_int32 * 2)(1, 1)
     assert ic._lib.ic_layer_stack_static(2, lay, bad, ctypes.byref(qs), ctypes.byref(d), 0.1, FAKE, None, None) \
         == ic.IC_ERR_REUSE_MAP
+
+
+def test_stream_read_validation(ic):
+    """The calibration read rejects sizes that are not whole 16-byte vectors
+    and null or misaligned pointers before any launch; zero bytes is a no-op."""
+    f = ic._lib.ic_stream_read
+    assert f(FAKE, 24, FAKE, None) == ic.IC_ERR_SHAPE
+    assert f(FAKE, -16, FAKE, None) == ic.IC_ERR_SHAPE
+    assert f(None, 32, FAKE, None) == ic.IC_ERR_NULL
+    assert f(FAKE + 8, 32, FAKE, None) == ic.IC_ERR_ALIGN
+    assert f(None, 0, None, None) == ic.IC_OK
 
 
 def test_reuse_map_matches_oracle_rule(ic):
