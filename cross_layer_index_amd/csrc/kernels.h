@@ -67,6 +67,7 @@ hipError_t launch_topk_collect(const float *scores, int64_t ld, const int32_t *n
 
 // ---- sparse MLA -----------------------------------------------------------
 struct MlaPlan {
+    int32_t heads_per_wg;    // heads per workgroup: 128 (wide form) or 64
     int32_t splits;          // k-splits per (query, head group)
     int32_t rows_per_split;  // multiple of the row tile
     size_t ws_bytes;         // partial results when splits > 1

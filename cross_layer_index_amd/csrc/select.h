@@ -407,7 +407,9 @@ struct SplitSel {
     uint32_t key[E], pos[E];
     uint32_t C;
 
-    __device__ void load(const uint64_t *reg_t, int64_t stride, int32_t P)
+    // (both members inline into the caller: called, they would keep the
+    // arrays in memory behind `this`)
+    __device__ __forceinline__ void load(const uint64_t *reg_t, int64_t stride, int32_t P)
     {
         C = min((uint32_t)(NT * E) / (uint32_t)P, (uint32_t)stride) & ~3u;
 #pragma unroll
@@ -428,7 +430,7 @@ struct SplitSel {
     // Only slots in [s0, s1) are emitted (a group whose slots lie outside
     // skips the per-key work).
     template <class Emit>
-    __device__ void select(const RowSrc &row, int32_t k, uint32_t c0, uint32_t bound, int32_t P, Shared &sh,
+    __device__ __forceinline__ void select(const RowSrc &row, int32_t k, uint32_t c0, uint32_t bound, int32_t P, Shared &sh,
                            uint32_t *cnt, uint32_t s0, uint32_t s1, Emit emit)
     {
         constexpr bool LB = true;

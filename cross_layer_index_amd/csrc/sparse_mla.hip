@@ -26,6 +26,9 @@
 // When one query's list is split over several workgroups, each writes its
 // partial (m, l, and o normalised by l, in fp16) with streaming stores, and a
 // combine kernel merges them and adds the sink once.
+#include <cstdlib>
+#include <cstring>
+
 #include "kernels.h"
 #include "select.h"
 
@@ -110,6 +113,15 @@ __device__ __forceinline__ float rows_sum(float x)
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf16x2));
+}
+
+// Sum of the two bf16 values of a packed pair. The softmax denominators add
+// the probabilities as rounded for the value product, so that the weights
+// the product applies are normalised exactly (a single dominant row then
+// passes its value through unchanged, whatever its probability's rounding).
+__device__ __forceinline__ float bf16x2_sum(uint32_t w)
+{
+    return __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
 }
 
 // LDS tile: kTile gathered rows, row-major, each row padded to ROWCH 16-byte
@@ -440,16 +452,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
                 al[r] = __shfl(alpha, 4 * g + r);   // O rows are heads 4*g + r
         }
         float p[8];
-        float ps = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8; ++i)
             p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
-            ps += p[i];
-        }
-        ps = rows_sum(ps);
-        l_run += ps;
         const uint4 pw = make_uint4(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                                     cvt_pk_bf16(p[6], p[7]));
+        float ps = (bf16x2_sum(pw.x) + bf16x2_sum(pw.y)) + (bf16x2_sum(pw.z) + bf16x2_sum(pw.w));
+        ps = rows_sum(ps);
+        l_run += ps;
         const bf16x8 pa = as_bf16x8(pw);
         if (__builtin_amdgcn_readfirstlane(rescale)) {   // rare: a branch, not selects
 #pragma unroll
@@ -655,6 +665,481 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     }
 }
 
+// ---- wide form -------------------------------------------------------------
+// 128 heads per workgroup: 4 waves of 32 heads, each over the whole 576-wide
+// row (no split of the dims, so no partial scores cross waves and the tile
+// loop writes no LDS), on v_mfma_f32_32x32x16_bf16:
+//   S^T[j,h] = sum_d K[j,d] Q[h,d]   (A = 32 gathered rows x 16 dims from LDS,
+//                                     B = q of the wave's 32 heads in registers)
+//   O[h,v]  += sum_j P[h,j] V[j,v]    (A = P straight from the S^T accumulator,
+//                                     B = V by transposing LDS reads)
+// The S^T accumulator holds (row 8*(r/4) + 4*(l/32) + r%4, head l%32) in lane
+// l, element r. Read as P's K slots (slot e of K-step s <-> row
+// 16s + 4*(l/32) + e for e < 4, 16s + 8 + 4*(l/32) + (e-4) after), it feeds the
+// second product as is: the transposing V reads deliver those rows in the same
+// slots. Every selected row is gathered once for all 128 heads, into a ring of
+// four tiles: three gathers stay in flight while one tile is used, and one
+// barrier per tile orders it all.
+constexpr int kWThreads = 256;
+constexpr int kWWaves = kWThreads / 64;
+constexpr int kWHeadsPerWave = 32;
+constexpr int kWHeadsPerWG = kWWaves * kWHeadsPerWave;     // 128
+constexpr int kWQkBatch = 4;                               // QK^T K-steps whose fragments are read together
+constexpr int kWPvBatch = 2;                               // PV value tiles whose fragments are read together
+constexpr float kHeadroom = 32.0f;                         // log2 of the largest probability before a second pass
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// One 64-lane LDS fill (global_load_lds, 16 bytes a lane): lane l's bytes
+// base + voff land at LDS byte address lds + 16 l. Written as inline asm so
+// that the compiler does not track it: with four buffers in flight its own
+// alias bookkeeping for such fills falls back to waiting for all of them
+// before a read of any buffer. The fill has no register result; the waits
+// for it are the explicit ones in the tile loop (and any wait the compiler
+// places for its own loads only waits longer). M0 is written in the same
+// block, one wait state before its use.
+__device__ __forceinline__ void lds_fill16(const void *base, uint32_t voff, uint32_t lds)
+{
+    // base and lds are the same in every lane (a wave's fill has one source
+    // base and one LDS span); say so to the compiler, which keeps them in
+    // scalar registers, M0 for the LDS address
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t bs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+    asm volatile("s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(bs), "{m0}"(__builtin_amdgcn_readfirstlane((int)lds))
+                 : "memory");
+}
+
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8 &a, const bf16x8 &b, const v16f &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Max / sum of a value over the two half-waves (lanes l and l ^ 32): the
+// swap of a value with itself leaves one copy of each half in each result.
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int DQK, int DV>
+struct WideGeom {
+    static constexpr int KS = DQK / 16;                     // 32x32x16 K-steps of QK^T
+    static constexpr int NT = DV / 32;                      // 32-column value tiles
+    static constexpr int KROW = DQK + 8;                    // LDS row stride (bf16): rows 4 banks apart
+    static constexpr int ROWCH = KROW * 2 / 16;             // 16-byte chunks per LDS row
+    static constexpr int NCH = DQK / 8;                     // of which hold data
+    static constexpr int INSTR = (kTile * ROWCH + 63) / 64; // fill instructions per tile
+    static constexpr int ELEMS = INSTR * 64 * 8;            // bf16 slots per buffer
+    static constexpr int FPW = (INSTR + kWWaves - 1) / kWWaves;   // fill instructions per wave, most
+    static constexpr int FPW_MIN = INSTR / kWWaves;               // and fewest
+    static constexpr int SROW = DV + 8;                     // partial staging row stride (fp16)
+    static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK, "shape");
+    static_assert((KROW / 2) % 32 == 4, "consecutive LDS rows 4 banks apart");
+    static_assert(kWHeadsPerWave * SROW <= ELEMS, "a wave's partial fits one tile buffer");
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const int64_t *__restrict__ base,
+    const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
+    const float *__restrict__ sink, float scale_log2,
+    int32_t rows_per_split, int32_t splits, void *__restrict__ out, int32_t out_f32,
+    uint16_t *__restrict__ part_o, float *__restrict__ part_ml, int32_t n_units)
+{
+    using G = WideGeom<DQK, DV>;
+    // the ring's buffers are separate LDS objects: a read of one is known not
+    // to alias the fills in flight into the others
+    __shared__ __attribute__((aligned(16))) uint16_t tile0[G::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t tile1[G::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t tile2[G::ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t tile3[G::ELEMS];
+    __shared__ __attribute__((aligned(16))) int32_t rowid[kMaxRowsPerSplit + kTile];
+
+    // Workgroups go round-robin over the 8 XCDs (linear id mod 8). Work unit
+    // u = (query, split, head group), in that order of significance from
+    // the left, is taken by slot u mod per of XCD u / per: each XCD takes a
+    // contiguous block of units, so the splits of a query share its q
+    // fragments (and the head groups its rows) through one L2. The grid is
+    // 8 * per; ids past the last unit return at once.
+    const int nhg = H / kWHeadsPerWG;
+    int split, hg, t;
+    {
+        const int per = (int)(gridDim.x >> 3);
+        const int u = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+        if (u >= n_units)
+            return;
+        hg = u % nhg;
+        split = (u / nhg) % splits;
+        t = u / (nhg * splits);
+    }
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane & 31;
+    const int g = lane >> 5;
+    const int h0 = hg * kWHeadsPerWG + wave * kWHeadsPerWave;
+    const int hc = h0 + c;                        // this lane's S^T column (and P row)
+    const char *kvq = reinterpret_cast<const char *>(kv + base[t] * DQK);
+    const int j_begin = split * rows_per_split;
+    const int j_end = min(k, j_begin + rows_per_split);
+    const int nrows = j_end - j_begin;
+    const int padded = (nrows + kTile - 1) / kTile * kTile;
+    const int32_t nt = n_valid[t];
+    int any_valid = 0;
+    for (int i = tid; i < padded; i += kWThreads) {
+        int r = i < nrows ? idx[(int64_t)t * k + j_begin + i] : -1;
+        r = (r >= 0 && r < nt) ? r : -1;
+        rowid[i] = r;
+        any_valid |= r >= 0;
+    }
+    const bool has_rows = __syncthreads_or(any_valid);
+
+    bf16x8 qf[G::KS];                             // loaded with the first fills, below
+
+    // fill instruction m places 64 lanes x 16 bytes contiguously: lane's chunk
+    // m * 64 + lane is chunk ch of tile row r (the spare chunk of each row, and
+    // rows past the tile, read row 0: finite data the math never uses). The
+    // lane index passes through an empty asm so that the per-fill offsets are
+    // recomputed here (a few VALU ops) instead of being hoisted out of the
+    // tile loop into registers it does not have; the row ids are read all
+    // at once, without branches, before the fills go out.
+    // LDS byte addresses of the four buffers (constants once LDS is laid out)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)tile0, lds1 = (uint32_t)(uintptr_t)(lds_void *)tile1;
+    const uint32_t lds2 = (uint32_t)(uintptr_t)(lds_void *)tile2, lds3 = (uint32_t)(uintptr_t)(lds_void *)tile3;
+    auto issue = [&](uint32_t lds_tile, int j0) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        int rid[G::FPW];
+        uint32_t coff[G::FPW];
+#pragma unroll
+        for (int i = 0; i < G::FPW; ++i) {
+            const int chunk = (wave + kWWaves * i) * 64 + ln;
+            const int r = chunk / G::ROWCH;
+            const int ch = chunk - r * G::ROWCH;
+            const int id = rowid[j0 + min(r, kTile - 1)];
+            rid[i] = r < kTile ? max(id, 0) : 0;
+            coff[i] = ch < G::NCH ? 16u * ch : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < G::FPW; ++i) {
+            const int m = wave + kWWaves * i;
+            if (m < G::INSTR)
+                lds_fill16(kvq, (uint32_t)rid[i] * (uint32_t)(2 * DQK) + coff[i], lds_tile + m * 1024);
+        }
+    };
+
+    // Softmax state of head hc (log2 units), the same in both half-waves.
+    // O is never rescaled inside the tile loop (that would take the
+    // accumulators through the VALU): each head's reference m_run moves
+    // freely only while its O is still empty, and afterwards stays put while
+    // the logits stay within kHeadroom above it, probabilities of up to
+    // 2^kHeadroom being exact in bf16 and far from overflow in the fp32
+    // sums. A logit beyond that marks the pass void; a second pass then runs
+    // with every head's reference at its largest logit, found by the first.
+    const float sink_l2 = splits == 1 ? sink[hc] * kLog2e : -INFINITY;   // the sink, a value-less logit
+    float m_run, l_run, m_top;
+    bool o_nz;                                    // head hc has terms in O
+    int overflow = 0;
+    auto reset = [&](float m0) __attribute__((always_inline)) {
+        m_run = m0;
+        l_run = splits == 1 ? __builtin_amdgcn_exp2f(sink_l2 - m0) : 0.0f;
+        m_top = m0;
+        o_nz = false;
+    };
+    reset(splits == 1 ? sink_l2 : kMInit);
+    v16f o[G::NT];
+#pragma unroll
+    for (int i = 0; i < G::NT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o[i][r] = 0.0f;
+
+    // Matrix row m of the tile is tile row perm(m) = 8(m/8) + 2(m%4) + (m/4)%2:
+    // the K reads (8 lanes on 8 rows, 16 bytes each) and the transposing V
+    // reads (16 lanes on 4 rows x 4 column quads) then spread over all banks
+    auto perm = [](int m) { return 8 * (m >> 3) + 2 * (m & 3) + ((m >> 2) & 1); };
+    const int kb = perm(c) * G::KROW + 8 * g;                       // K: matrix row c, dims 8g..
+    const int p16 = lane & 15;
+    const int vb = perm(4 * g + (p16 >> 2)) * G::KROW + 16 * ((lane >> 4) & 1) + 4 * (p16 & 3);
+
+    auto compute = [&](const uint16_t *K, int j0) __attribute__((always_inline)) {
+        // S^T over the 36 K-steps (one accumulation chain: a dependent
+        // matrix op takes its predecessor's result by forwarding)
+        v16f acc[1];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[0][r] = 0.0f;
+#pragma unroll
+        for (int i0 = 0; i0 < G::KS; i0 += kWQkBatch) {
+            uint4 fa[kWQkBatch];
+#pragma unroll
+            for (int i = 0; i < kWQkBatch; ++i)
+                if (i0 + i < G::KS)
+                    fa[i] = *reinterpret_cast<const uint4 *>(K + kb + 16 * (i0 + i));
+#pragma unroll
+            for (int i = 0; i < kWQkBatch; ++i)
+                if (i0 + i < G::KS)
+                    acc[0] = mfma_bf16_32x32x16(as_bf16x8(fa[i]), qf[i0 + i], acc[0]);
+        }
+        // validity of this lane's 16 rows: matrix row 8a + 4g + b is index
+        // entry j0 + perm(.) = j0 + 8a + 2b + g
+        float s[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int4 x0 = *reinterpret_cast<const int4 *>(&rowid[j0 + 8 * a]);
+            const int4 x1 = *reinterpret_cast<const int4 *>(&rowid[j0 + 8 * a + 4]);
+            const int v[4] = {g ? x0.y : x0.x, g ? x0.w : x0.z, g ? x1.y : x1.x, g ? x1.w : x1.z};
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int r = 4 * a + b;
+                const float sum = acc[0][r];
+                s[r] = v[b] >= 0 ? sum * scale_log2 : -INFINITY;
+                mt = fmaxf(mt, s[r]);
+            }
+        }
+        mt = halves_max(mt);                      // all 32 rows of head hc
+        m_top = fmaxf(m_top, mt);
+        if (!o_nz) {
+            if (mt > m_run) {                     // only the sink's term to carry over
+                l_run *= __builtin_amdgcn_exp2f(m_run - mt);
+                m_run = mt;
+            }
+        } else if (mt > m_run + kHeadroom) {
+            overflow = 1;
+        }
+        o_nz = o_nz || mt > -INFINITY;
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            p[r] = __builtin_amdgcn_exp2f(fminf(s[r] - m_run, kHeadroom));
+        bf16x8 pa[2];
+        float ps = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 pw = make_uint4(cvt_pk_bf16(p[8 * h + 0], p[8 * h + 1]), cvt_pk_bf16(p[8 * h + 2], p[8 * h + 3]),
+                                        cvt_pk_bf16(p[8 * h + 4], p[8 * h + 5]), cvt_pk_bf16(p[8 * h + 6], p[8 * h + 7]));
+            ps += (bf16x2_sum(pw.x) + bf16x2_sum(pw.y)) + (bf16x2_sum(pw.z) + bf16x2_sum(pw.w));
+            pa[h] = as_bf16x8(pw);
+        }
+        l_run += halves_sum(ps);
+        // V operand of value tile i, K-step h: rows 16h + 4g + 0..3 and
+        // 16h + 8 + 4g + 0..3 of column 32 i + (lane % 32)
+        auto vfrag = [&](int i, int h) -> bf16x8 {
+            const uint16_t *pv = K + vb + 16 * h * G::KROW + 32 * i;
+            const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)pv);
+            const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(pv + 8 * G::KROW));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+#pragma unroll
+        for (int i0 = 0; i0 < G::NT; i0 += kWPvBatch) {
+            bf16x8 vf[kWPvBatch][2];
+#pragma unroll
+            for (int i = 0; i < kWPvBatch; ++i) {
+                vf[i][0] = vfrag(i0 + i, 0);
+                vf[i][1] = vfrag(i0 + i, 1);
+            }
+#pragma unroll
+            for (int i = 0; i < kWPvBatch; ++i) {
+                o[i0 + i] = mfma_bf16_32x32x16(pa[0], vf[i][0], o[i0 + i]);
+                o[i0 + i] = mfma_bf16_32x32x16(pa[1], vf[i][1], o[i0 + i]);
+            }
+        }
+    };
+
+    // Ring of four tiles, tile i in buffer i % 4: step i waits for its own
+    // fills of tile i (those of tiles i+1 and i+2 stay in flight), and after
+    // the barrier -- tile i complete for every wave, tile i-1's buffer free --
+    // issues tile i+3 into that buffer, then uses tile i. The loop writes no
+    // LDS, so no fill in flight is waited for before its time. The first
+    // three tiles and the q fragments go out together and are waited for
+    // before the loop (the compiler then has no load of its own pending in
+    // it). Unrolled by four so that every access names its buffer.
+    const int ntiles = has_rows ? padded / kTile : 0;
+    auto step = [&](int i, const uint16_t *cur, uint32_t ahead) __attribute__((always_inline)) {
+        // fills issued after tile i's: those of tiles i+1 and i+2 that exist
+        // (each wave issues at least FPW_MIN per tile)
+        if (i + 2 < ntiles)
+            wait_vmcnt<2 * G::FPW_MIN>();
+        else if (i + 1 < ntiles)
+            wait_vmcnt<G::FPW_MIN>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();
+        if (i + 3 < ntiles)
+            issue(ahead, (i + 3) * kTile);
+        compute(cur, i * kTile);
+    };
+    auto issue3 = [&]() __attribute__((always_inline)) {
+        issue(lds0, 0);
+        if (ntiles > 1)
+            issue(lds1, kTile);
+        if (ntiles > 2)
+            issue(lds2, 2 * kTile);
+    };
+    if (ntiles > 0)
+        issue3();
+    // q fragments: K-step i, lane (head c, half g) holds d = 16 i + 8 g .. + 8
+#pragma unroll
+    for (int i = 0; i < G::KS; ++i)
+        qf[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(q + ((int64_t)t * H + hc) * DQK + 16 * i + 8 * g));
+    for (int pass = 0; ntiles > 0; ++pass) {
+        if (pass > 0)
+            issue3();
+        wait_vmcnt<0>();
+        for (int i = 0; i < ntiles; i += 4) {
+            step(i, tile0, lds3);
+            if (i + 1 < ntiles)
+                step(i + 1, tile1, lds0);
+            if (i + 2 < ntiles)
+                step(i + 2, tile2, lds1);
+            if (i + 3 < ntiles)
+                step(i + 3, tile3, lds2);
+        }
+        wait_vmcnt<0>();                          // the fills past the last tile
+        // (the barrier also frees every buffer for a second pass)
+        if (pass > 0 || !__syncthreads_or(overflow))
+            break;
+        reset(m_top);
+        o_nz = true;                              // the reference is final
+#pragma unroll
+        for (int i = 0; i < G::NT; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[i][r] = 0.0f;
+    }
+
+    // Element r of lane l is head 8(r/4) + 4g + r%4 of the wave, column
+    // 32 i + c of value tile i. Each wave stages its 32 x DV block in one
+    // tile buffer (all free once every wave has left the loop) and stores
+    // whole rows, 16 bytes a lane. A scheduling barrier after each value
+    // tile keeps the accumulator reads from crowding the registers.
+    auto head_of = [&](int r) { return 8 * (r >> 2) + 4 * g + (r & 3); };
+    lds_barrier();
+    uint16_t *stg = wave == 0 ? tile0 : (wave == 1 ? tile1 : (wave == 2 ? tile2 : tile3));
+    // rows of the staged block to global memory: row j of `bytes` bytes at
+    // stg + j * stride bytes goes to dst(j)
+    auto store_rows = [&](auto bytes_c, int stride, auto dst) {
+        constexpr int chunks = decltype(bytes_c)::value / 16;
+        static_assert(kWHeadsPerWave * chunks % 64 == 0, "whole rounds of the wave");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own staging writes
+#pragma unroll 8
+        for (int it = 0; it < kWHeadsPerWave * chunks / 64; ++it) {
+            const int q = lane + 64 * it;
+            const int j = q / chunks, ch = q - j * chunks;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(stg) + j * stride + 16 * ch);
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst(j)) + ch);
+        }
+    };
+    using RowBytes = std::integral_constant<int, DV * 2>;       // a bf16 or fp16 row; an fp32 half row
+    float inv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float l = __shfl(l_run, head_of(r));
+        inv[r] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+    if (splits == 1) {
+        const int64_t orow = (int64_t)t * H + h0;
+        if (out_f32) {
+            // fp32 rows in two halves of 256 columns (33 KB of staging each)
+            constexpr int SW = DV / 2 + 4;
+            float *st = reinterpret_cast<float *>(stg);
+            static_assert(kWHeadsPerWave * SW * 4 <= G::ELEMS * 2, "a half fits a tile buffer");
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int i = hf * G::NT / 2; i < (hf + 1) * G::NT / 2; ++i) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        st[head_of(r) * SW + 32 * (i - hf * G::NT / 2) + c] = o[i][r] * inv[r];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                store_rows(RowBytes{}, SW * 4, [&](int j) {
+                    return reinterpret_cast<float *>(out) + (orow + j) * DV + hf * (DV / 2);
+                });
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::NT; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    stg[head_of(r) * G::SROW + 32 * i + c] = (uint16_t)f32_to_bf16_rne(o[i][r] * inv[r]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            store_rows(RowBytes{}, G::SROW * 2, [&](int j) {
+                return reinterpret_cast<uint16_t *>(out) + (orow + j) * DV;
+            });
+        }
+    } else {
+        // The split's partial, normalised by its own denominator and stored
+        // as fp16 scaled by 2^-e per (head, half of the value columns), e > 0
+        // only when that half reaches 2^14; (m, l, e0, e1) go beside it.
+        const int64_t prow = ((int64_t)t * splits + split) * H;
+        // optimistic pass at the plain scale (e = 0), tracking magnitudes
+        float mxa = 0.0f;
+#pragma unroll
+        for (int i = 0; i < G::NT; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float v = o[i][r] * inv[r];
+                mxa = fmaxf(mxa, fabsf(v));
+                stg[head_of(r) * G::SROW + 32 * i + c] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (__builtin_amdgcn_readfirstlane(__any(!(mxa < 16384.0f)))) {
+            // rare: a half reaches 2^14 somewhere in the wave; exponents per
+            // (head, half) over the half-wave's 32 lanes, staged again
+            float mx[16][2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx[r][0] = mx[r][1] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < G::NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx[r][i >= G::NT / 2] = fmaxf(mx[r][i >= G::NT / 2], fabsf(o[i][r] * inv[r]));
+            float scl[16][2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    float m = mx[r][hf];
+#pragma unroll
+                    for (int off = 16; off > 0; off >>= 1)
+                        m = fmaxf(m, __shfl_xor(m, off));
+                    const int e = m >= 16384.0f ? ilogbf(m) - 13 : 0;
+                    scl[r][hf] = ldexpf(inv[r], -e);
+                    if (c == 0)
+                        part_ml[(prow + h0 + head_of(r)) * 4 + 2 + hf] = (float)e;
+                }
+#pragma unroll
+            for (int i = 0; i < G::NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    stg[head_of(r) * G::SROW + 32 * i + c] =
+                        __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl[r][i >= G::NT / 2]));
+            if (g == 0) {
+                part_ml[(prow + hc) * 4 + 0] = m_run;
+                part_ml[(prow + hc) * 4 + 1] = l_run;
+            }
+        } else if (g == 0) {
+            *reinterpret_cast<float4 *>(part_ml + (prow + hc) * 4) = make_float4(m_run, l_run, 0.0f, 0.0f);
+        }
+        store_rows(RowBytes{}, G::SROW * 2, [&](int j) { return part_o + (prow + h0 + j) * DV; });
+    }
+}
+
 // grid: (H, T); block: DV/4 threads, four value columns each. Merges the
 // per-split partials (fp16, normalised by the split's own denominator and
 // scaled by 2^-e) and adds the sink:
@@ -800,17 +1285,27 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
                         int32_t T, int32_t H, int32_t k, const float *sink, float scale, void *out,
                         int32_t out_f32, const MlaPlan &plan, void *ws, const SelArgs &sa, hipStream_t stream)
 {
-    const int hg = (H + kHeadsPerWG - 1) / kHeadsPerWG;
+    const int hg = (H + plan.heads_per_wg - 1) / plan.heads_per_wg;
     uint16_t *part_o = nullptr;
     float *part_ml = nullptr;
     if (plan.splits > 1) {
         part_o = reinterpret_cast<uint16_t *>(ws);
         part_ml = reinterpret_cast<float *>(part_o + (size_t)T * plan.splits * H * DV);
     }
-    if (!trace_skip(SEL ? "sparse_mla_kernel<selecting>" : "sparse_mla_kernel"))
+    if (trace_skip(SEL ? "sparse_mla_kernel<selecting>" : "sparse_mla_kernel")) {
+    } else if (plan.heads_per_wg == kWHeadsPerWG) {
+        // the wide form: 576/512 rows from a finished list only
+        if (SEL || DQK != 576 || DV != 512)
+            return hipErrorInvalidValue;
+        const int32_t n_units = plan.splits * hg * T;   // eight slots of ceil(n_units / 8) each
+        hipLaunchKernelGGL((sparse_mla_wide_kernel<576, 512>), dim3((n_units + 7) / 8 * 8), dim3(kWThreads), 0,
+                           stream, q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split,
+                           plan.splits, out, out_f32, part_o, part_ml, n_units);
+    } else {
         hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
-                       q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out,
-                       out_f32, part_o, part_ml, (int32_t)plan.direct_parts, sa);
+                           q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits,
+                           out, out_f32, part_o, part_ml, (int32_t)plan.direct_parts, sa);
+    }
     trace_launch(stream, SEL ? "sparse_mla_kernel<selecting>" : "sparse_mla_kernel");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1)
@@ -839,7 +1334,24 @@ bool sparse_mla_supported(int32_t D_qk, int32_t D_v)
 MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
 {
     MlaPlan p;
-    const int64_t hg = (H + kHeadsPerWG - 1) / kHeadsPerWG;
+    // The wide form (128 heads per workgroup: each row gathered once, four
+    // tiles in flight) serves the 576/512 rows when the heads come in whole
+    // groups of 128 and the batch holds at least 16 tiles of rows per CU;
+    // smaller batches are latency-bound, where the narrow form's eight
+    // waves per workgroup finish each unit of work sooner.
+    // IC_MLA_FORM=wide or =narrow overrides the choice where both apply
+    // (so that tests reach either form at any size).
+    const int64_t wide_tiles = (int64_t)T * (H / kWHeadsPerWG) * ((k + kTile - 1) / kTile);
+    const bool wide_ok = D_v == 512 && H % kWHeadsPerWG == 0;
+    bool wide = wide_ok && wide_tiles >= 16 * kResidentWGs;
+    if (const char *f = getenv("IC_MLA_FORM")) {
+        if (!strcmp(f, "wide"))
+            wide = wide_ok;
+        else if (!strcmp(f, "narrow"))
+            wide = false;
+    }
+    p.heads_per_wg = wide ? kWHeadsPerWG : kHeadsPerWG;
+    const int64_t hg = (H + p.heads_per_wg - 1) / p.heads_per_wg;
     const int64_t base_wgs = (int64_t)T * hg;
     int64_t max_splits = (k + 4 * kTile - 1) / (4 * kTile);   // >= 4 tiles per split
     if (max_splits > kMaxSplits)
@@ -896,7 +1408,13 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int64_
 
 bool sparse_mla_selecting_supported(const MlaPlan &plan, int32_t T, int32_t H, const TopkSplitView &v)
 {
-    const int64_t wgs = (int64_t)plan.splits * ((H + kHeadsPerWG - 1) / kHeadsPerWG) * T;
+    const int64_t wgs = (int64_t)plan.splits * ((H + plan.heads_per_wg - 1) / plan.heads_per_wg) * T;
+    // The wide form's four waves would select 8192 keys at 32 a thread,
+    // slower than the separate finishing pass it saves: it takes its rows
+    // from a finished list. (The narrow form keeps one slice count per
+    // thread: at most 512 slices.)
+    if (plan.heads_per_wg == kWHeadsPerWG)
+        return false;
     return wgs <= kResidentWGs && v.P >= 1 && v.P <= kMlaThreads;
 }
 

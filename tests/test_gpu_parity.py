@@ -254,6 +254,19 @@ def test_topk_exact(gpu, orc, name):
 
 
 # ---------------------------------------------------------------- sparse MLA --
+@pytest.fixture(params=["narrow", "wide"])
+def mla_form(request, monkeypatch):
+    """Both forms of the sparse MLA kernel, whatever the library would pick
+    for the size (the wide one takes the heads 128 to a workgroup)."""
+    monkeypatch.setenv("IC_MLA_FORM", request.param)
+    return request.param
+
+
+def needs_form(form, H):
+    if form == "wide" and H % 128:
+        pytest.skip("the wide form takes whole groups of 128 heads")
+
+
 def mla_case(name):
     """(workload, idx [T, k] int32 with sequence-local positions)."""
     rng = np.random.default_rng(7)
@@ -279,14 +292,25 @@ def mla_case(name):
         idx[0, :1500] = rng.permutation(1500)
         rng.shuffle(idx[0])
         return wl, idx
+    if name == "many_queries":
+        # enough queries that every (query, head group) takes one workgroup
+        # and no split: the sink enters inside the kernel
+        lengths = [int(x) for x in rng.integers(1, 200, 512)]
+        wl = W.scaled(W.WORKLOADS["decode_128k"], T=512, k=64, lengths=lengths)
+        idx = np.full((512, 64), -1, np.int32)
+        for t, nt in enumerate(lengths):
+            sel = rng.choice(nt, min(nt, 64), replace=False)
+            idx[t, :sel.size] = sel
+        return wl, idx
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_split", "batch_k64", "padded_split"])
-def test_sparse_mla_close(gpu, orc, name):
+@pytest.mark.parametrize("name", ["tiny", "decode_split", "batch_k64", "padded_split", "many_queries"])
+def test_sparse_mla_close(gpu, orc, name, mla_form):
     """fp32 output within 5e-3 of the fp64 oracle; the bf16 output of the same
     launch is its rounded image (and within 5e-3 where bf16 can be)."""
     wl, idx = mla_case(name)
+    needs_form(mla_form, wl.H)
     li = W.layer_inputs(wl, 0, with_indexer=False)
     d = dev(li)
     qs = qs_of(gpu, wl)
@@ -294,13 +318,13 @@ def test_sparse_mla_close(gpu, orc, name):
     ref = orc.sparse_mla(li.q, li.kv, wl.base(), idx, li.sink, wl.scale, wl.D_v)
     f32 = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v, out_f32=True).cpu().numpy()
     b16 = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v).float().cpu().numpy()
-    assert_close(f32, ref, f"sparse MLA {name} [fp32]")
-    assert_bf16_output(b16, f32, ref, f"sparse MLA {name}")
+    assert_close(f32, ref, f"sparse MLA {name} {mla_form} [fp32]")
+    assert_bf16_output(b16, f32, ref, f"sparse MLA {name} {mla_form}")
     for got in (f32, b16):
         assert np.all(got[idx.max(1) < 0] == 0)                                  # empty rows are zero
 
 
-def test_sparse_mla_large_values(gpu, orc):
+def test_sparse_mla_large_values(gpu, orc, mla_form):
     """Latent rows scaled by 1e5 (and q by 1e-5, so the scores stay as they
     were): the split partials, stored in fp16 with a per-(head, half)
     power-of-two scale, must stay in range; the fp32 output holds the bar
@@ -318,12 +342,37 @@ def test_sparse_mla_large_values(gpu, orc):
     assert np.isfinite(f32).all()
     assert np.abs(ref).max() > 16384.0                                          # the scaled range is in use
     err = max_abs(f32, ref)
-    report("sparse MLA large values [fp32, bar 5e-3 x 1e5]", err)
+    report(f"sparse MLA large values {mla_form} [fp32, bar 5e-3 x 1e5]", err)
     assert err <= ATOL * big, f"max abs error {err} (scaled bar {ATOL * big})"
     assert np.array_equal(b16, bf16_rne(f32))
 
 
-def test_sparse_mla_deterministic(gpu):
+@pytest.mark.parametrize("name", ["decode_split", "many_queries"])
+def test_sparse_mla_logit_range(gpu, orc, name, mla_form):
+    """q scaled by a power of two until the logits of a head spread over
+    hundreds of units: later rows then beat the first rows' maximum by far
+    (the narrow form rescales its sums; the wide form, whose probabilities
+    may grow only so far above its first reference, takes a second pass over
+    the rows with every reference at its final maximum). The output must
+    still match the oracle's softmax to the bar."""
+    wl, idx = mla_case(name)
+    li = W.layer_inputs(wl, 0, with_indexer=False)
+    t0 = int(np.argmax((idx >= 0).sum(1)))
+    rows = idx[t0][idx[t0] >= 0] + int(wl.base()[t0])
+    logits = wl.scale * (li.q[t0].double().numpy() @ li.kv[rows].double().numpy().T)
+    f = 2.0 ** math.ceil(math.log2(300.0 / logits.std(axis=1).mean()))
+    q = (li.q.float() * f).to(torch.bfloat16)
+    assert torch.equal(q.float() / f, li.q.float())                             # exact scaling
+    qs = qs_of(gpu, wl)
+    i = torch.from_numpy(idx).cuda()
+    ref = orc.sparse_mla(q, li.kv, wl.base(), idx, li.sink, wl.scale, wl.D_v)
+    f32 = gpu.sparse_mla(q.cuda(), li.kv.cuda(), qs, i, li.sink.cuda(), wl.scale, wl.D_v,
+                         out_f32=True).cpu().numpy()
+    assert np.isfinite(f32).all()
+    assert_close(f32, ref, f"sparse MLA {name} {mla_form} logits x{f:g} [fp32]")
+
+
+def test_sparse_mla_deterministic(gpu, mla_form):
     wl, idx = mla_case("decode_split")
     d = dev(W.layer_inputs(wl, 0, with_indexer=False))
     qs = qs_of(gpu, wl)
@@ -335,7 +384,7 @@ def test_sparse_mla_deterministic(gpu):
 
 # --------------------------------------------------------------- layer stack --
 @pytest.mark.parametrize("case", ["decode_3layer", "ragged_2layer"])
-def test_layer_stack_graph_replay(gpu, case):
+def test_layer_stack_graph_replay(gpu, case, mla_form):
     """The stack captured in a HIP graph and replayed several times, with eager
     work and synchronisations between the replays, gives the eager result bit
     for bit every time: the calls enqueue no memsets or copies, and the
@@ -393,7 +442,7 @@ def run_stack(ic, wl, layers_dev, rmap, out_f32=False):
 
 @pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer", "ties_3layer",
                                   "clustered_2layer"])
-def test_layer_stack_small(gpu, orc, case):
+def test_layer_stack_small(gpu, orc, case, mla_form):
     if case == "tiny":
         wl = W.WORKLOADS["tiny_2layer"]
     elif case == "clustered_2layer":
@@ -416,6 +465,7 @@ def test_layer_stack_small(gpu, orc, case):
                       lengths=[700, 65], H=8)
     else:
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=4, full_layers=[0], T=2, k=64, lengths=[300, 50], H=8)
+    needs_form(mla_form, wl.H)
     host = [W.layer_inputs(wl, l) for l in range(wl.n_layers)]
     if case == "ties_3layer":
         for x in host:
@@ -433,10 +483,10 @@ def test_layer_stack_small(gpu, orc, case):
     for l in range(wl.n_layers):
         got_idx = cache[slots[rmap[l]]].cpu().numpy()
         assert np.array_equal(got_idx, r_index[l])
-        assert_close(outs[l].cpu().numpy(), r_outs[l], f"layer stack {case} layer {l} [fp32]")
+        assert_close(outs[l].cpu().numpy(), r_outs[l], f"layer stack {case} {mla_form} layer {l} [fp32]")
 
 
-def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc):
+def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc, mla_form):
     """Index entries outside [0, n_valid[t]) (a list that breaks the contract)
     are treated as empty on the device: the output equals the oracle's on the
     same list with those entries replaced by -1, and no latent row outside the
@@ -456,7 +506,7 @@ def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc):
     got = gpu.sparse_mla(d.q, d.kv, qs, torch.from_numpy(idx).cuda(), d.sink, wl.scale, wl.D_v,
                          out_f32=True).float().cpu().numpy()
     ref = orc.sparse_mla(li.q, li.kv, wl.base(), clean, li.sink, wl.scale, wl.D_v)
-    assert_close(got, ref, "sparse MLA out-of-range entries [fp32]")
+    assert_close(got, ref, f"sparse MLA out-of-range entries {mla_form} [fp32]")
 
 
 # ------------------------------------------------------------ gated output --
