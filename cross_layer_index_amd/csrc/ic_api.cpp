@@ -338,8 +338,10 @@ IC_EXPORT ic_status ic_trace_skip(const char *kernel)
 
 IC_EXPORT ic_status ic_trace_create(int32_t capacity, ic_trace **out)
 {
-    if (!out || capacity < 1 || capacity > (1 << 20))
-        return fail(IC_ERR_SHAPE, "trace: capacity=%d outside [1, 2^20] or no output pointer", capacity);
+    if (!out)
+        return fail(IC_ERR_NULL, "trace: no output pointer");
+    if (capacity < 1 || capacity > (1 << 20))
+        return fail(IC_ERR_SHAPE, "trace: capacity=%d outside [1, 2^20]", capacity);
     *out = nullptr;
     ic_trace *tr = new (std::nothrow) ic_trace;
     if (!tr)

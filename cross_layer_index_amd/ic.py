@@ -134,6 +134,54 @@ class Queries:
                           int(self.rows), int(self.group), 0)
 
 
+def debug_enabled() -> bool:
+    """IC_DEBUG=1 in the environment: every call first reads back the
+    device-resident values the library cannot check (n_valid, base, index
+    lists) and rejects a contract violation before anything is enqueued.
+    The read-back synchronises the device; it is a debugging aid only."""
+    return os.environ.get("IC_DEBUG") == "1"
+
+
+def check_contract(qs: Queries, idx: Optional[torch.Tensor] = None) -> None:
+    """The device-resident contract of include/ic.h, checked on the host:
+    0 <= n_valid[t] <= max_n, base[t] >= 0, base[t] + n_valid[t] <= rows,
+    equal bases within a shared sequence (same_seq, or each group of a
+    draft/verify batch), and every idx entry -1 or in [0, n_valid[t]).
+    Raises ICError(IC_ERR_SHAPE) naming the first violation."""
+    base = qs.base.detach().to("cpu", torch.int64)
+    n = qs.n_valid.detach().to("cpu", torch.int64)
+    if base.shape != n.shape or base.dim() != 1:
+        raise ICError(IC_ERR_SHAPE, "base and n_valid must be 1-D of one length")
+
+    def bad(what, t):
+        raise ICError(IC_ERR_SHAPE, f"contract violated at query {int(t)}: {what} "
+                                    f"(base={int(base[t])}, n_valid={int(n[t])}, max_n={qs.max_n}, rows={qs.rows})")
+
+    for cond, what in ((n < 0, "n_valid < 0"), (n > qs.max_n, "n_valid > max_n"), (base < 0, "base < 0"),
+                       (base + n > qs.rows, "base + n_valid > rows")):
+        if bool(cond.any()):
+            bad(what, torch.nonzero(cond)[0, 0])
+    if qs.same_seq and base.numel() and bool((base != base[0]).any()):
+        bad("same_seq with unequal bases", torch.nonzero(base != base[0])[0, 0])
+    if qs.group > 1 and base.numel():
+        if base.numel() % qs.group:
+            raise ICError(IC_ERR_SHAPE, f"T={base.numel()} is not a multiple of group={qs.group}")
+        g = base.view(-1, qs.group)
+        off = g != g[:, :1]
+        if bool(off.any()):
+            r, c = (int(x) for x in torch.nonzero(off)[0])
+            bad("unequal bases within a group", r * qs.group + c)
+    if idx is not None:
+        i = idx.detach().to("cpu", torch.int64)
+        if i.dim() != 2 or i.shape[0] != n.numel():
+            raise ICError(IC_ERR_SHAPE, f"idx must be [T, k], got {tuple(i.shape)}")
+        wrong = (i != -1) & ((i < 0) | (i >= n[:, None]))
+        if bool(wrong.any()):
+            t, j = (int(x) for x in torch.nonzero(wrong)[0])
+            raise ICError(IC_ERR_SHAPE, f"contract violated at query {t}: idx[{t}, {j}] = {int(i[t, j])} "
+                                        f"is neither -1 nor in [0, n_valid) = [0, {int(n[t])})")
+
+
 def make_queries(base: torch.Tensor, n_valid: torch.Tensor, rows: int, same_seq=False, device="cuda",
                  group: int = 1) -> Queries:
     nv = n_valid.to(torch.int32)
@@ -179,6 +227,8 @@ def _cache_rows(qs: "Queries"):
 # ---------------------------------------------------------------- entries --
 def indexer_score(q_idx, w, k_idx, qs: Queries, scores: Optional[torch.Tensor] = None, stream=None):
     """Indexer scores [T, ld] fp32 (ld = max_n rounded up to 4)."""
+    if debug_enabled():
+        check_contract(qs)
     q_idx, k_idx = _u8(q_idx, "q_idx"), _u8(k_idx, "k_idx")
     _dev(w, torch.float32, "w")
     T, H_I, D_I = q_idx.shape
@@ -201,6 +251,8 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 def topk(scores, qs: Queries, k: int, idx: Optional[torch.Tensor] = None, ws=None, stream=None):
+    if debug_enabled():
+        check_contract(qs)
     _dev(scores, torch.float32, "scores")
     _shape(scores, (qs.T, (">=", qs.max_n)), "scores")
     qc = qs.c()
@@ -218,6 +270,8 @@ def topk(scores, qs: Queries, k: int, idx: Optional[torch.Tensor] = None, ws=Non
 
 def sparse_mla(q, kv, qs: Queries, idx, sink, scale: float, D_v: int, out=None, out_f32=False, ws=None,
                stream=None):
+    if debug_enabled():
+        check_contract(qs, idx)
     _bf16(q, "q")
     _bf16(kv, "kv")
     _dev(idx, torch.int32, "idx")
@@ -367,6 +421,8 @@ class LayerStack:
         self.passes = _i32(-1)
 
     def __call__(self, stream=None) -> int:
+        if debug_enabled():
+            check_contract(self.qs)
         _check(_lib.ic_layer_stack(self.n, self.arr, self.rmap, ctypes.byref(self.qc), ctypes.byref(self.d),
                                    self.scale, _ptr(self.index_cache), ctypes.byref(self.passes), _ptr(self.ws),
                                    self.ws.numel(), _stream(stream)))
@@ -375,6 +431,8 @@ class LayerStack:
     def call_static(self, stream=None) -> int:
         """The same stack through ic_layer_stack_static: the library's own
         scratch instead of this object's workspace (no allocation in the call)."""
+        if debug_enabled():
+            check_contract(self.qs)
         _check(_lib.ic_layer_stack_static(self.n, self.arr, self.rmap, ctypes.byref(self.qc), ctypes.byref(self.d),
                                           self.scale, _ptr(self.index_cache), ctypes.byref(self.passes),
                                           _stream(stream)))
