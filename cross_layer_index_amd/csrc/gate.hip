@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NT) void gated_output_kernel(const uint16_t *__rest
     __shared__ __attribute__((aligned(16))) unsigned char ob1[kGateRows * GG::ROWB];
     const int groups = (D_o + wcols - 1) / wcols;
     const int h = blockIdx.x / groups;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
     const int lane = threadIdx.x & 63;
     const int e0 = (blockIdx.x % groups) * wcols + wave * 16;
     const bool active = e0 < D_o;                 // D_o is a multiple of 16: whole tiles

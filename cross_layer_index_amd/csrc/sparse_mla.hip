@@ -228,7 +228,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // the wave index through readfirstlane: the compiler then knows it is
+    // wave-uniform, so conditions on it (the second half's shorter K-step
+    // count when the K-steps are odd) become scalar branches. Under an EXEC
+    // mask instead, a skipped matrix instruction would still run (they
+    // ignore EXEC) on operand registers that were never loaded.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hgrp = wave & 3;
     const int half = wave >> 2;
     const int c = lane & 15;
@@ -689,6 +694,7 @@ constexpr int kWPvBatch = 2;                               // PV value tiles who
 constexpr float kHeadroom = 32.0f;                         // log2 of the largest probability before a second pass
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // One 64-lane LDS fill (global_load_lds, 16 bytes a lane): lane l's bytes
 // base + voff land at LDS byte address lds + 16 l. Written as inline asm so
@@ -784,7 +790,7 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 31;
     const int g = lane >> 5;
     const int h0 = hg * kWHeadsPerWG + wave * kWHeadsPerWave;
@@ -1020,12 +1026,12 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
     }
 
     // Element r of lane l is head 8(r/4) + 4g + r%4 of the wave, column
-    // 32 i + c of value tile i. Each wave stages its 32 x DV block in one
-    // tile buffer (all free once every wave has left the loop) and stores
-    // whole rows, 16 bytes a lane. A scheduling barrier after each value
-    // tile keeps the accumulator reads from crowding the registers.
+    // 32 i + c of value tile i. The output (no split) is staged per wave in
+    // one tile buffer (all free once every wave has left the loop) and goes
+    // out as whole rows, 16 bytes a lane; a split's partial goes out from
+    // the registers (below). A scheduling barrier after each value tile
+    // keeps the accumulator reads from crowding the registers.
     auto head_of = [&](int r) { return 8 * (r >> 2) + 4 * g + (r & 3); };
-    lds_barrier();
     uint16_t *stg = wave == 0 ? tile0 : (wave == 1 ? tile1 : (wave == 2 ? tile2 : tile3));
     // rows of the staged block to global memory: row j of `bytes` bytes at
     // stg + j * stride bytes goes to dst(j)
@@ -1049,6 +1055,7 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
         inv[r] = l > 0.0f ? 1.0f / l : 0.0f;
     }
     if (splits == 1) {
+        lds_barrier();                            // every wave has left the tile loop
         const int64_t orow = (int64_t)t * H + h0;
         if (out_f32) {
             // fp32 rows in two halves of 256 columns (33 KB of staging each)
@@ -1081,40 +1088,56 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
             });
         }
     } else {
-        // The split's partial, normalised by its own denominator and stored
-        // as fp16 scaled by 2^-e per (head, half of the value columns), e > 0
-        // only when that half reaches 2^14; (m, l, e0, e1) go beside it.
+        // The split's partial, normalised by its own denominator, goes out
+        // straight from the accumulators in their own order (the wide combine
+        // reads that order): per (32-head block, value tile i) 64 lanes x 16
+        // fp16, elements 8 hh .. 8 hh + 7 of lane l at ((i * 2 + hh) * 64 + l)
+        // * 8, so each store instruction writes 1 KB contiguously. Values
+        // are scaled by 2^-e per (head, half of the value columns), e > 0
+        // only when that half reaches 2^14; (m, l, e0, e1) go beside them.
         const int64_t prow = ((int64_t)t * splits + split) * H;
-        // optimistic pass at the plain scale (e = 0), tracking magnitudes
-        float mxa = 0.0f;
+        u32x4 *pw = reinterpret_cast<u32x4 *>(part_o + (prow + h0) * DV) + lane;
+        auto store_tile = [&](int i, auto scale_of) __attribute__((always_inline)) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 8 * hh + 2 * e;
+                    w4[e] = __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(o[i][r] * scale_of(r)),
+                                                                static_cast<_Float16>(o[i][r + 1] * scale_of(r + 1))});
+                }
+                __builtin_nontemporal_store(u32x4{w4[0], w4[1], w4[2], w4[3]}, pw + (i * 2 + hh) * 64);
+            }
+        };
+        // optimistic pass at the plain scale (e = 0), tracking |o| per
+        // (element, half)
+        float mxr[16][2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mxr[r][0] = mxr[r][1] = 0.0f;
 #pragma unroll
         for (int i = 0; i < G::NT; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = o[i][r] * inv[r];
-                mxa = fmaxf(mxa, fabsf(v));
-                stg[head_of(r) * G::SROW + 32 * i + c] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-            }
+            for (int r = 0; r < 16; ++r)
+                mxr[r][i >= G::NT / 2] = fmaxf(mxr[r][i >= G::NT / 2], fabsf(o[i][r]));
+            store_tile(i, [&](int r) { return inv[r]; });
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (__builtin_amdgcn_readfirstlane(__any(!(mxa < 16384.0f)))) {
+        bool big = false;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            big |= !(mxr[r][0] * inv[r] < 16384.0f) || !(mxr[r][1] * inv[r] < 16384.0f);
+        if (__builtin_amdgcn_readfirstlane(__any(big))) {
             // rare: a half reaches 2^14 somewhere in the wave; exponents per
-            // (head, half) over the half-wave's 32 lanes, staged again
-            float mx[16][2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                mx[r][0] = mx[r][1] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < G::NT; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx[r][i >= G::NT / 2] = fmaxf(mx[r][i >= G::NT / 2], fabsf(o[i][r] * inv[r]));
+            // (head, half) over the half-wave's 32 lanes, stored again (a
+            // lane's later stores to the same address land last)
             float scl[16][2];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    float m = mx[r][hf];
+                    float m = mxr[r][hf] * inv[r];
 #pragma unroll
                     for (int off = 16; off > 0; off >>= 1)
                         m = fmaxf(m, __shfl_xor(m, off));
@@ -1125,10 +1148,7 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
                 }
 #pragma unroll
             for (int i = 0; i < G::NT; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stg[head_of(r) * G::SROW + 32 * i + c] =
-                        __builtin_bit_cast(uint16_t, static_cast<_Float16>(o[i][r] * scl[r][i >= G::NT / 2]));
+                store_tile(i, [&](int r) { return scl[r][i >= G::NT / 2]; });
             if (g == 0) {
                 part_ml[(prow + hc) * 4 + 0] = m_run;
                 part_ml[(prow + hc) * 4 + 1] = l_run;
@@ -1136,7 +1156,6 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
         } else if (g == 0) {
             *reinterpret_cast<float4 *>(part_ml + (prow + hc) * 4) = make_float4(m_run, l_run, 0.0f, 0.0f);
         }
-        store_rows(RowBytes{}, G::SROW * 2, [&](int j) { return part_o + (prow + h0 + j) * DV; });
     }
 }
 
@@ -1279,6 +1298,111 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
     }
 }
 
+// Merges the wide form's split partials (register order, see its epilogue)
+// and adds the sink:
+//   out = sum_s 2^(m_s - m) l_s 2^e_s p_s / (2^(sink - m) + sum_s 2^(m_s - m) l_s)
+// grid: (value tiles x 32-head blocks, T); block: 64 threads, thread l the
+// lane whose 16 values it merges: heads 8(r/4) + 4(l/32) + r%4 of the block,
+// column 32 i + l%32. Weights go through LDS; the merged block goes out as
+// rows through an LDS transpose.
+template <int DV>
+__global__ __launch_bounds__(64) void mla_combine_wide_kernel(const uint16_t *__restrict__ part_o,
+                                                              const float *__restrict__ part_ml,
+                                                              const float *__restrict__ sink, int32_t H,
+                                                              int32_t splits, void *__restrict__ out,
+                                                              int32_t out_f32)
+{
+    constexpr int NT = DV / 32;
+    extern __shared__ float wgt_dyn[];                       // [splits][33]: weight of (split, head)
+    auto wgt = [&](int s_, int h_) -> float & { return wgt_dyn[s_ * 33 + h_]; };
+    __shared__ float inv_den[32];
+    __shared__ float ot[32][33];
+    const int i = blockIdx.x % NT;
+    const int wb = blockIdx.x / NT;
+    const int t = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int hf = i >= NT / 2;
+    const int64_t pr0 = (int64_t)t * splits * H;             // row of split 0, head 0
+    if (lane < 32) {
+        // head 32 wb + lane: the maximum over the splits and the sink, then
+        // the weights and the denominator
+        const int h = 32 * wb + lane;
+        const float ms = sink[h] * kLog2e;
+        float m = ms;
+#pragma unroll 8
+        for (int s = 0; s < splits; ++s)
+            m = fmaxf(m, part_ml[(pr0 + (int64_t)s * H + h) * 4]);
+        float d = exp2f(ms - m);
+#pragma unroll 8
+        for (int s = 0; s < splits; ++s) {
+            const float4 ml = *reinterpret_cast<const float4 *>(part_ml + (pr0 + (int64_t)s * H + h) * 4);
+            const float wl = exp2f(ml.x - m) * ml.y;
+            wgt(s, lane) = ldexpf(wl, (int)(hf ? ml.w : ml.z));
+            d += wl;
+        }
+        inv_den[lane] = 1.0f / d;
+    }
+    __syncthreads();
+    const int g = lane >> 5;
+    auto head_of = [&](int r) { return 8 * (r >> 2) + 4 * g + (r & 3); };
+    const uint4 *p = reinterpret_cast<const uint4 *>(part_o + (pr0 + 32 * wb) * DV) + (i * 2) * 64 + lane;
+    const int64_t stride = (int64_t)H * DV / 8;               // uint4s between splits
+    auto h2f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        acc[r] = 0.0f;
+    constexpr int CB = 8;                                     // splits in flight
+    for (int s0 = 0; s0 < splits; s0 += CB) {
+        uint4 x[CB][2];
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+            if (s0 + u < splits) {
+                x[u][0] = p[(int64_t)(s0 + u) * stride];
+                x[u][1] = p[(int64_t)(s0 + u) * stride + 64];
+            }
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+            if (s0 + u < splits) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t wv[4] = {x[u][hh].x, x[u][hh].y, x[u][hh].z, x[u][hh].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 8 * hh + 2 * e;
+                        acc[r] = fmaf(h2f(wv[e] & 0xFFFFu), wgt(s0 + u, head_of(r)), acc[r]);
+                        acc[r + 1] = fmaf(h2f(wv[e] >> 16), wgt(s0 + u, head_of(r + 1)), acc[r + 1]);
+                    }
+                }
+            }
+    }
+    const int c = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        ot[head_of(r)][c] = acc[r] * inv_den[head_of(r)];
+    __syncthreads();
+    // rows out: head j of the block, columns 32 i .. 32 i + 31
+    const int64_t orow = (int64_t)t * H + 32 * wb;
+    if (out_f32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                        // 32 rows x 8 float4s
+            const int k = lane + 64 * q, j = k >> 3, ch = k & 7;
+            const float4 v = make_float4(ot[j][4 * ch], ot[j][4 * ch + 1], ot[j][4 * ch + 2], ot[j][4 * ch + 3]);
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (orow + j) * DV + 32 * i + 4 * ch) = v;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {                        // 32 rows x 4 chunks of 8 bf16
+            const int k = lane + 64 * q, j = k >> 2, ch = k & 3;
+            const uint4 v = make_uint4(pack_bf16x2(ot[j][8 * ch], ot[j][8 * ch + 1]),
+                                       pack_bf16x2(ot[j][8 * ch + 2], ot[j][8 * ch + 3]),
+                                       pack_bf16x2(ot[j][8 * ch + 4], ot[j][8 * ch + 5]),
+                                       pack_bf16x2(ot[j][8 * ch + 6], ot[j][8 * ch + 7]));
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + (orow + j) * DV + 32 * i + 8 * ch) = v;
+        }
+    }
+}
+
 template <int DQK, int DV, bool SEL>
 hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *base, const int32_t *n_valid,
                         const int32_t *idx,
@@ -1312,6 +1436,10 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
         return e;
     if (trace_skip("mla_combine_kernel"))
         ;
+    else if (plan.heads_per_wg == kWHeadsPerWG)
+        hipLaunchKernelGGL((mla_combine_wide_kernel<512>), dim3((512 / 32) * (H / 32), T), dim3(64),
+                           (size_t)plan.splits * 33 * sizeof(float), stream, part_o, part_ml, sink, H, plan.splits,
+                           out, out_f32);
     else if (plan.splits > kCombineBatchMax / 2)
         hipLaunchKernelGGL((mla_combine_kernel<DV, kCombineBatchMax>), dim3(H, T), dim3(DV / 4), 0, stream, part_o,
                            part_ml, sink, H, plan.splits, out, out_f32);

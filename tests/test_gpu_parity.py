@@ -486,6 +486,27 @@ def test_layer_stack_small(gpu, orc, case, mla_form):
         assert_close(outs[l].cpu().numpy(), r_outs[l], f"layer stack {case} {mla_form} layer {l} [fp32]")
 
 
+def test_sparse_mla_odd_k_steps_after_graph_replays(gpu, orc, monkeypatch):
+    """80-wide rows make an odd count of 32-wide K-steps, so the two halves of
+    a head group run different numbers of matrix steps. The vector registers
+    a kernel's waves start with hold whatever earlier work left there; after
+    the ragged graph-replay test below, a matrix step that ran on never-loaded
+    operands (matrix instructions ignore EXEC masks) made every output NaN.
+    Several launches after that same work, each checked against the oracle."""
+    monkeypatch.setenv("IC_MLA_FORM", "narrow")
+    test_layer_stack_graph_replay(gpu, "ragged_2layer", "narrow")
+    wl, idx = mla_case("tiny")
+    li = W.layer_inputs(wl, 0, with_indexer=False)
+    d = dev(li)
+    qs = qs_of(gpu, wl)
+    i = torch.from_numpy(idx).cuda()
+    ref = orc.sparse_mla(li.q, li.kv, wl.base(), idx, li.sink, wl.scale, wl.D_v)
+    for rep in range(4):
+        got = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v, out_f32=True).cpu().numpy()
+        assert np.isfinite(got).all(), f"launch {rep}: non-finite output"
+        assert_close(got, ref, f"sparse MLA tiny after graph replays, launch {rep} [fp32]")
+
+
 def test_sparse_mla_out_of_range_entries_are_empty(gpu, orc, mla_form):
     """Index entries outside [0, n_valid[t]) (a list that breaks the contract)
     are treated as empty on the device: the output equals the oracle's on the
