@@ -228,12 +228,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // the wave index through readfirstlane: the compiler then knows it is
-    // wave-uniform, so conditions on it (the second half's shorter K-step
-    // count when the K-steps are odd) become scalar branches. Under an EXEC
-    // mask instead, a skipped matrix instruction would still run (they
-    // ignore EXEC) on operand registers that were never loaded.
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = tid >> 6;
     const int hgrp = wave & 3;
     const int half = wave >> 2;
     const int c = lane & 15;
@@ -385,7 +380,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     auto qk = [&](const uint16_t *K, f4 &st0, f4 &st1) {
         // both halves have KSH steps when KS is even (the 576-wide rows); an
         // odd KS leaves the second half one step short
-        const int nks = (G::KS % 2 == 0) ? KSH : min(KSH, G::KS - ks0);
+        // (through readfirstlane: the compiler then knows the count is the
+        // same in every lane, so the steps past it are skipped by a scalar
+        // branch. Under an EXEC mask instead, a skipped matrix instruction
+        // would still run -- they ignore EXEC -- on operand registers that
+        // were never loaded.)
+        const int nks = __builtin_amdgcn_readfirstlane((G::KS % 2 == 0) ? KSH : min(KSH, G::KS - ks0));
         // even and odd K-steps accumulate separately: four independent
         // matrix-instruction chains instead of two dependent ones
         f4 acc[2][2];
