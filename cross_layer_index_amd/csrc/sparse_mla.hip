@@ -344,8 +344,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         for (int i = 0; i < kFillPerWave; ++i) {
             const int m = wave + kWaves * i;
             if (m < TG::INSTR) {
-                const int r = fill_row[i];
-                const int rid = r < kTile ? rowid[j0 + r] : -1;
+                const int rid = rowid[j0 + min(fill_row[i], kTile - 1)];
                 const uint32_t off = (uint32_t)max(rid, 0) * (uint32_t)(2 * DQK) + (uint32_t)fill_boff[i];
                 __builtin_amdgcn_global_load_lds(kvq + off, (lds_void *)(tile + m * 64 * 8), 16, 0, 0);
             }
@@ -692,8 +691,8 @@ constexpr int kWThreads = 256;
 constexpr int kWWaves = kWThreads / 64;
 constexpr int kWHeadsPerWave = 32;
 constexpr int kWHeadsPerWG = kWWaves * kWHeadsPerWave;     // 128
-constexpr int kWQkBatch = 4;                               // QK^T K-steps whose fragments are read together
-constexpr int kWPvBatch = 2;                               // PV value tiles whose fragments are read together
+constexpr int kWQkDepth = 4;                               // QK^T fragment reads in flight
+constexpr int kWPvDepth = 4;                               // PV fragment reads in flight
 constexpr float kHeadroom = 32.0f;                         // log2 of the largest probability before a second pass
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -817,8 +816,10 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
     bf16x8 qf[G::KS];                             // loaded with the first fills, below
 
     // fill instruction m places 64 lanes x 16 bytes contiguously: lane's chunk
-    // m * 64 + lane is chunk ch of tile row r (the spare chunks of each row, and
-    // rows past the tile, read row 0: finite data the math never uses). The
+    // m * 64 + lane is chunk ch of tile row r (the spare chunks of each row
+    // read chunk 0, and slots past the tile's rows repeat its last row: finite
+    // data the math never uses; the row id loads stay unconditional, so they
+    // go out together rather than each behind its own branch and wait). The
     // lane index passes through an empty asm so that the per-fill offsets are
     // recomputed here (a few VALU ops) instead of being hoisted out of the
     // tile loop into registers it does not have; the row ids are read all
@@ -836,8 +837,7 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
             const int chunk = (wave + kWWaves * i) * 64 + ln;
             const int r = chunk / G::ROWCH;
             const int ch = chunk - r * G::ROWCH;
-            const int id = rowid[j0 + min(r, kTile - 1)];
-            rid[i] = r < kTile ? max(id, 0) : 0;
+            rid[i] = max(rowid[j0 + min(r, kTile - 1)], 0);
             coff[i] = ch < G::NCH ? 16u * (uint32_t)(ch ^ ((r >> 3) & 1)) : 0u;
         }
 #pragma unroll
@@ -895,17 +895,17 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             acc[0][r] = 0.0f;
+        // fragments read kWQkDepth K-steps ahead: each step's read goes into
+        // the slot the step kWQkDepth before it has just consumed
+        uint4 fa[kWQkDepth];
 #pragma unroll
-        for (int i0 = 0; i0 < G::KS; i0 += kWQkBatch) {
-            uint4 fa[kWQkBatch];
+        for (int i = 0; i < kWQkDepth; ++i)
+            fa[i] = *reinterpret_cast<const uint4 *>(K + kb + 16 * i);
 #pragma unroll
-            for (int i = 0; i < kWQkBatch; ++i)
-                if (i0 + i < G::KS)
-                    fa[i] = *reinterpret_cast<const uint4 *>(K + kb + 16 * (i0 + i));
-#pragma unroll
-            for (int i = 0; i < kWQkBatch; ++i)
-                if (i0 + i < G::KS)
-                    acc[0] = mfma_bf16_32x32x16(as_bf16x8(fa[i]), qf[i0 + i], acc[0]);
+        for (int s = 0; s < G::KS; ++s) {
+            acc[0] = mfma_bf16_32x32x16(as_bf16x8(fa[s % kWQkDepth]), qf[s], acc[0]);
+            if (s + kWQkDepth < G::KS)
+                fa[s % kWQkDepth] = *reinterpret_cast<const uint4 *>(K + kb + 16 * (s + kWQkDepth));
         }
         // validity of this lane's 16 rows: matrix row 8a + 4g + b is index
         // entry j0 + perm(.) = j0 + 8a + 2b + g
@@ -956,19 +956,19 @@ __global__ __launch_bounds__(kWThreads, 1) void sparse_mla_wide_kernel(
             const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(K + vb8 + 16 * h * G::KROW + 32 * i));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         };
+        // product s: value tile 2(s/4) + s%2, K-half (s/2)%2 (a tile's two
+        // products one apart, not back to back), its fragment read
+        // kWPvDepth products ahead into the slot just consumed
+        constexpr int NS = 2 * G::NT;
+        bf16x8 vf[kWPvDepth];
 #pragma unroll
-        for (int i0 = 0; i0 < G::NT; i0 += kWPvBatch) {
-            bf16x8 vf[kWPvBatch][2];
+        for (int s = 0; s < kWPvDepth; ++s)
+            vf[s] = vfrag(2 * (s / 4) + (s % 2), (s / 2) % 2);
 #pragma unroll
-            for (int i = 0; i < kWPvBatch; ++i) {
-                vf[i][0] = vfrag(i0 + i, 0);
-                vf[i][1] = vfrag(i0 + i, 1);
-            }
-#pragma unroll
-            for (int i = 0; i < kWPvBatch; ++i) {
-                o[i0 + i] = mfma_bf16_32x32x16(pa[0], vf[i][0], o[i0 + i]);
-                o[i0 + i] = mfma_bf16_32x32x16(pa[1], vf[i][1], o[i0 + i]);
-            }
+        for (int s = 0; s < NS; ++s) {
+            o[2 * (s / 4) + (s % 2)] = mfma_bf16_32x32x16(pa[(s / 2) % 2], vf[s % kWPvDepth], o[2 * (s / 4) + (s % 2)]);
+            if (s + kWPvDepth < NS)
+                vf[s % kWPvDepth] = vfrag(2 * ((s + kWPvDepth) / 4) + ((s + kWPvDepth) % 2), ((s + kWPvDepth) / 2) % 2);
         }
     };
 
