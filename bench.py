@@ -58,7 +58,9 @@ def default_sets(wl, nn) -> int:
 def indexer_launch_bytes(wl, nn) -> int:
     """Algorithmic bytes of one indexer launch: every query's q and w, and the
     key rows of every sequence once (queries of a draft/verify group share
-    their sequence's key stream)."""
+    their sequence's key stream, and causal prefill queries all read one)."""
+    if wl.same_seq:
+        return max(nn, default=0) * wl.D_I + len(nn) * wl.H_I * (wl.D_I + 4)
     g = max(1, wl.group)
     if g == 1:
         return sum(indexer_bytes(x, wl.H_I, wl.D_I) for x in nn)
