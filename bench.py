@@ -87,6 +87,10 @@ KERNEL_SOURCES = {
     "topk_collect_kernel": ["topk.hip", "select.h", "radix_key.h"],
     "topk_finish_kernel": ["topk.hip", "select.h", "radix_key.h"],
     "topk_row_kernel": ["topk.hip", "select.h", "radix_key.h"],
+    "indexer_prefill_sample": ["indexer.hip"],
+    "indexer_prefill_collect": ["indexer.hip", "radix_key.h"],
+    "prefill_bound_kernel": ["topk.hip", "select.h", "radix_key.h"],
+    "prefill_select_kernel": ["topk.hip", "select.h", "radix_key.h"],
 }
 
 
@@ -113,16 +117,23 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
-def kernel_work(name: str, wl, nn, full: bool, splits_combined: bool):
+def kernel_work(name: str, wl, nn, full: bool, splits_combined: bool, collecting: bool = False):
     """Algorithmic bytes and flops of one launch of kernel `name` in one layer
     of the workload (the per-query-layer bytes of the method, split among the
     kernels that move them: score round trips, split partials and survivor
     lists are overhead and count nowhere). Returns (bytes, flops, flops_dtype)."""
     kp = [min(wl.k, x) for x in nn]
-    if name in ("indexer_decode_kernel", "indexer_prefill_kernel"):
+    if name in ("indexer_decode_kernel", "indexer_prefill_kernel", "indexer_prefill_collect"):
+        if name == "indexer_prefill_kernel" and collecting:
+            return 0, 0, None                                    # serves only queries the collection missed
         fl = sum(indexer_flops(x, wl.H_I, wl.D_I) for x in nn)
         return indexer_launch_bytes(wl, nn), fl, "fp8"
-    if name in ("topk_finish_kernel", "topk_row_kernel"):
+    if name == "indexer_prefill_sample":                         # one key in 64
+        fl = sum(indexer_flops(-(-x // 64), wl.H_I, wl.D_I) for x in nn)
+        return indexer_launch_bytes(wl, [-(-x // 64) for x in nn]), fl, "fp8"
+    if name in ("topk_finish_kernel", "topk_row_kernel", "prefill_select_kernel"):
+        if name == "topk_row_kernel" and collecting:
+            return 0, 0, None
         return 4 * sum(kp), 0, None                              # the index list written
     if name in ("topk_collect_kernel", "clear_hist0_kernel"):
         return 0, 0, None
@@ -451,11 +462,12 @@ def main():
     costs = kernel_costs(sets, names, full_step_s, steps, warm)
     n_full = sum(1 for l in range(wl.n_layers) if rmap[l] == l)
     combined = "mla_combine_kernel" in costs
+    collecting = "indexer_prefill_collect" in costs
     table = []
     for name, sec in costs.items():
         per_step = names.count(name)
         us = sec * 1e6
-        by, fl, fdt = kernel_work(name, wl, nn, True, combined)
+        by, fl, fdt = kernel_work(name, wl, nn, True, combined, collecting)
         row = {"kernel": name, "launches_per_step": per_step, "us_per_launch": us,
                "us_per_step": us * per_step, "algorithmic_bytes_per_launch": by}
         if by and us > 0:
@@ -469,7 +481,7 @@ def main():
         table.append(row)
     table.sort(key=lambda r: -r["us_per_step"])
     dom = table[0]
-    by, fl, fdt = kernel_work(dom["kernel"], wl, nn, True, combined)
+    by, fl, fdt = kernel_work(dom["kernel"], wl, nn, True, combined, collecting)
     mfma_bound = fl and (fl / (FP8_PEAK_TFLOPS if fdt == "fp8" else BF16_PEAK_TFLOPS) / 1e12 >
                          by / HBM_PEAK_GBS / 1e9)
     if mfma_bound:

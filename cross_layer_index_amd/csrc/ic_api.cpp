@@ -5,7 +5,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <array>
 #include <mutex>
 #include <new>
@@ -225,9 +227,22 @@ ic_status check_reuse_map(int32_t n_layers, const int32_t *m)
 int64_t score_ld(const ic_queries *qs) { return (int64_t)round_up((size_t)(qs->max_n > 0 ? qs->max_n : 1), 4); }
 
 // layer-stack workspace: [scores][top-k][sparse MLA], each 256-byte aligned
+// Causal prefill over long rows selects from a bounded collection of the
+// scores instead of whole score rows (see topk.hip); the score rows stay in
+// the layout for the queries the collection cannot serve.
+struct Collect {
+    bool on;
+    int64_t sample_ld, chunk, nchunks;
+    int32_t cap;
+    size_t sample_off, bound_off, slices_off, counts_off, need_off;
+};
+
+int prefill_collect_mode(const ic_queries *qs, const ic_dims *d);
+
 struct StackLayout {
     size_t scores_off, topk_off, mla_off, total;
     int64_t ld;
+    Collect col;
 };
 
 StackLayout stack_layout(const ic_queries *qs, const ic_dims *d)
@@ -237,7 +252,27 @@ StackLayout stack_layout(const ic_queries *qs, const ic_dims *d)
     L.scores_off = 0;
     L.topk_off = round_up((size_t)qs->T * L.ld * sizeof(float), 256);
     L.mla_off = L.topk_off + round_up(ic::topk_workspace_bytes(qs->T, qs->max_n, d->k), 256);
-    L.total = L.mla_off + round_up(ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v).ws_bytes, 256);
+    size_t end = L.mla_off + round_up(ic::plan_sparse_mla(qs->T, d->H, d->k, d->D_v).ws_bytes, 256);
+    Collect &c = L.col;
+    c = Collect{};
+    c.on = prefill_collect_mode(qs, d) > 0;
+    if (c.on) {
+        const int64_t T = qs->T, n = qs->max_n;
+        c.sample_ld = ((n + ic::kPfSampleStride - 1) / ic::kPfSampleStride + 3) / 4 * 4;
+        c.chunk = ic::indexer_prefill_chunk(qs->T, 16, n);
+        c.nchunks = (n + c.chunk - 1) / c.chunk;
+        // twice a chunk's expected share of the survivors (about 2k + 16 x the
+        // sample stride per query), plus 64
+        const int64_t expect = (2 * (int64_t)d->k + 16 * ic::kPfSampleStride) * c.chunk / n;
+        c.cap = (int32_t)std::min<int64_t>(c.chunk, (2 * expect + 64 + 63) / 64 * 64);
+        c.sample_off = end;
+        c.bound_off = c.sample_off + round_up((size_t)T * c.sample_ld * sizeof(float), 256);
+        c.slices_off = c.bound_off + round_up((size_t)T * 4, 256);
+        c.counts_off = c.slices_off + round_up((size_t)T * c.nchunks * c.cap * 8, 256);
+        c.need_off = c.counts_off + round_up((size_t)T * c.nchunks * 4, 256);
+        end = c.need_off + round_up((size_t)T * 4, 256);
+    }
+    L.total = end;
     return L;
 }
 
@@ -258,6 +293,25 @@ int32_t shared_key_group(const ic_queries *qs, int32_t H_I, int32_t D_I)
 bool use_prefill_indexer(const ic_queries *qs, int32_t H_I, int32_t D_I)
 {
     return shared_key_group(qs, H_I, D_I) > 0;
+}
+
+// 0: score rows; 1: bounded collection; 2: bounded collection with nothing
+// collected, so that every query takes the score rows (a test of that path).
+// Causal prefill of at least 256 queries over rows of at least 65,536 tokens
+// collects; IC_PREFILL_TOPK=scores|collect|fallback overrides the length rule.
+int prefill_collect_mode(const ic_queries *qs, const ic_dims *d)
+{
+    if (!qs->same_seq || qs->T < 256 || shared_key_group(qs, d->H_I, d->D_I) != 16 || qs->max_n < 1)
+        return 0;
+    if (const char *f = getenv("IC_PREFILL_TOPK")) {
+        if (!strcmp(f, "scores"))
+            return 0;
+        if (!strcmp(f, "collect"))
+            return 1;
+        if (!strcmp(f, "fallback"))
+            return 2;
+    }
+    return qs->max_n >= 65536 ? 1 : 0;
 }
 
 hipError_t launch_indexer(const uint8_t *q_idx, const float *w, const uint8_t *k_idx, const ic_queries *qs,
@@ -666,7 +720,37 @@ IC_EXPORT ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, con
     for (int32_t l = 0; l < n_layers; ++l) {
         const ic_layer &y = layers[l];
         const bool full = reuse_map[l] == l;
-        if (full) {
+        if (full && L.col.on) {
+            // bounded collection: sample scores, bounds, collection, selection;
+            // then the score rows and the row top-k for the queries marked
+            int32_t *idx = index_cache + slot_of(l) * slot_elems;
+            char *w8 = static_cast<char *>(ws);
+            const Collect &c = L.col;
+            float *sample = reinterpret_cast<float *>(w8 + c.sample_off);
+            uint32_t *bound = reinterpret_cast<uint32_t *>(w8 + c.bound_off);
+            uint64_t *slices = reinterpret_cast<uint64_t *>(w8 + c.slices_off);
+            uint32_t *counts = reinterpret_cast<uint32_t *>(w8 + c.counts_off);
+            uint32_t *need = reinterpret_cast<uint32_t *>(w8 + c.need_off);
+            hipError_t e = ic::launch_indexer_prefill_sample(y.q_idx, y.w, y.k_idx, qs->base, qs->n_valid, qs->T,
+                                                             qs->max_n, sample, c.sample_ld, st);
+            if (e == hipSuccess)
+                e = ic::launch_prefill_bound(sample, c.sample_ld, qs->n_valid, qs->T, d->k, bound,
+                                             prefill_collect_mode(qs, d) == 2, st);
+            if (e == hipSuccess)
+                e = ic::launch_indexer_prefill_collect(y.q_idx, y.w, y.k_idx, qs->base, qs->n_valid, qs->T,
+                                                       qs->max_n, bound, slices, counts, c.cap, st);
+            if (e == hipSuccess)
+                e = ic::launch_prefill_select(slices, counts, (int32_t)c.nchunks, c.chunk, c.cap, qs->n_valid,
+                                              qs->T, d->k, idx, need, st);
+            if (e == hipSuccess)
+                e = ic::launch_indexer_prefill(y.q_idx, y.w, y.k_idx, qs->base, qs->n_valid, qs->T, qs->max_n,
+                                               d->H_I, d->D_I, 16, scores, L.ld, st, need);
+            if (e == hipSuccess)
+                e = ic::launch_topk(scores, L.ld, qs->n_valid, qs->T, qs->max_n, d->k, idx, topk_ws, false, st,
+                                    need);
+            if (e != hipSuccess)
+                return hip_status(e, "layer stack: prefill indexer and top-k launches");
+        } else if (full) {
             int32_t *idx = index_cache + slot_of(l) * slot_elems;
             if (qs->max_n > 0) {
                 hipError_t e = launch_indexer(y.q_idx, y.w, y.k_idx, qs, d->H_I, d->D_I, scores, L.ld,

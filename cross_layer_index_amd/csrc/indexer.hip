@@ -298,15 +298,38 @@ constexpr int kPfSlab = 1024;                             // bytes per fill inst
 constexpr int kPfGroupBytes = 32 * kPfDI;                 // 4 slabs
 static_assert(kPfGroups == kPfWaves, "wave w fills group w of each tile");
 
-template <int P>
+// What a launch of the shared-key kernel produces (causal prefill uses all
+// three, see the collecting top-k in topk.hip):
+//   kPfScores   the score rows;
+//   kPfSample   the score rows of a strided sample of the keys: sample row i
+//               is key row kPfSampleStride * i, and query t sees
+//               ceil(n_t / kPfSampleStride) of them;
+//   kPfCollect  no score rows: each score whose order key is at or above the
+//               query's bound goes, as (key << 32 | position), into the
+//               query's slice for this token chunk, in position order, and
+//               the slice's count is stored (beyond `cap` entries only counted).
+enum { kPfScores = 0, kPfSample = 1, kPfCollect = 2 };
+
+// The collecting mode's outputs. Slice (t, c) of query t and token chunk c
+// (blockIdx.x) holds `cap` entries from (t * gridDim.x + c) * cap.
+struct PfCollect {
+    const uint32_t *bound;       // [T] order-key bound per query
+    uint64_t *slices;
+    uint32_t *counts;            // [T, gridDim.x]
+    int32_t cap;
+};
+
+template <int P, int MODE>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     const uint8_t *__restrict__ q_idx, const float *__restrict__ w, const uint8_t *__restrict__ k_idx,
     const int64_t *__restrict__ base, const int32_t *__restrict__ n, int32_t T, int32_t grp,
-    float *__restrict__ scores, int64_t ld, int64_t chunk)
+    float *__restrict__ scores, int64_t ld, int64_t chunk, const uint32_t *__restrict__ need, PfCollect col)
 {
     static_assert(P == 1 || P == 2 || P == 4 || P == 8, "query pairs per workgroup");
     constexpr int S = kPfWaves / P;                       // token splits of a tile
     constexpr int kUnits = 2 * P;                         // (group, query) units per wave per tile
+    // collecting keeps each query's survivors in position order in one wave
+    static_assert(MODE != kPfCollect || S == 1, "one wave per query");
     using G = IdxGeom<kPfDI>;
     // three separate LDS objects (not one array): a read of one buffer is then
     // known not to alias the fills in flight into the others, and the
@@ -323,11 +346,25 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     const int qp = wave % P;                              // this wave's query pair
     const int ts = wave / P;                              // and token split
 
+    // visible rows of query t (sample rows in the sampling mode)
+    auto n_of = [&](int t) -> int64_t {
+        const int64_t v = n[t];
+        return MODE == kPfSample ? (v + kPfSampleStride - 1) / kPfSampleStride : v;
+    };
+    // a gated launch (need non-null) serves only groups with a query marked
+    if (need) {
+        bool any = false;
+        for (int i = 0; i < grp; ++i)
+            if (t_base + i < T)
+                any = any || need[t_base + i] != 0u;
+        if (!any)
+            return;
+    }
     // extent of the group: the largest n among its queries
     int64_t nmax = 0;
     for (int i = 0; i < grp; ++i)
         if (t_base + i < T)
-            nmax = max(nmax, (int64_t)n[t_base + i]);
+            nmax = max(nmax, n_of(t_base + i));
     const int64_t s_begin = (int64_t)blockIdx.x * chunk;
     if (s_begin >= nmax)
         return;
@@ -336,13 +373,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
 
     int tq[kPfQW];
     int64_t nq[kPfQW];
+    uint32_t bq[kPfQW];                                   // collecting: bound and running count
+    uint32_t run[kPfQW];
     v8i a[kPfQW][2][G::KS];
     float wr[kPfQW][2][16];
 #pragma unroll
     for (int i = 0; i < kPfQW; ++i) {
         tq[i] = t_base + qp * kPfQW + i;
         const bool ok = qp * kPfQW + i < grp && tq[i] < T;
-        nq[i] = ok ? n[tq[i]] : 0;
+        nq[i] = ok ? n_of(tq[i]) : 0;
+        bq[i] = MODE == kPfCollect && ok ? col.bound[tq[i]] : 0xFFFFFFFFu;
+        run[i] = 0;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int h = 32 * mt + j;
@@ -367,6 +408,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     auto issue = [&](uint8_t *buf, int64_t tile) {
         int64_t row = tile + frow;
         row = row < s_end ? row : s_end - 1;
+        if (MODE == kPfSample)
+            row *= kPfSampleStride;
         const uint8_t *src = krows + row * kPfDI + fcol;
         uint8_t *dst = buf + wave * kPfGroupBytes;
 #pragma unroll
@@ -425,8 +468,23 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
             }
             sum = half_sum(sum);
             const int64_t s = tile + 32 * gidx(kk) + j;
-            if (g == 0 && s < nq[i])
+            if (MODE == kPfCollect) {
+                // scores at or above the bound, in position order (lanes in
+                // order, units of a query in token order)
+                const uint32_t key = ord_key(sum);
+                const bool keep = g == 0 && s < nq[i] && key >= bq[i];
+                const uint64_t m = __ballot(keep);
+                if (m) {
+                    const uint32_t o = run[i] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (keep && o < (uint32_t)col.cap)
+                        col.slices[((int64_t)tq[i] * gridDim.x + blockIdx.x) * col.cap + o] =
+                            ((uint64_t)key << 32) | (uint32_t)s;
+                    run[i] += (uint32_t)__popcll(m);
+                }
+            } else if (g == 0 && s < nq[i]) {
                 scores[(int64_t)tq[i] * ld + s] = sum;
+            }
         }
     };
 
@@ -453,6 +511,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
         if (it + 2 < ntiles)
             step(it + 2, tile2, tile1);
     }
+    if (MODE == kPfCollect && lane == 0)
+#pragma unroll
+        for (int i = 0; i < kPfQW; ++i)
+            if (qp * kPfQW + i < grp && tq[i] < T)
+                col.counts[(int64_t)tq[i] * gridDim.x + blockIdx.x] = run[i];
 }
 
 }  // namespace
@@ -472,15 +535,8 @@ hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uin
 
 bool indexer_prefill_supported(int32_t H_I, int32_t D_I) { return H_I == 64 && D_I == kPfDI; }
 
-hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
-                                  const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
-                                  int32_t H_I, int32_t D_I, int32_t G, float *scores, int64_t ld,
-                                  hipStream_t stream)
+int64_t indexer_prefill_chunk(int32_t T, int32_t G, int64_t max_n)
 {
-    if (!indexer_prefill_supported(H_I, D_I) || G < 1 || G > kPfQ)
-        return hipErrorInvalidValue;
-    if (T == 0 || max_n == 0)
-        return hipSuccess;
     const int64_t groups = (T + G - 1) / G;
     const int P = G <= 2 ? 1 : (G <= 4 ? 2 : (G <= 8 ? 4 : 8));
     // token chunks: at least 64 units per wave per workgroup (32 / P tiles),
@@ -491,25 +547,90 @@ hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const ui
     int64_t chunk = (int64_t)kPfTile * (32 / P);
     while (chunk < max_n && groups * ((max_n + chunk - 1) / chunk) > 16384)
         chunk *= 2;
+    return chunk;
+}
+
+namespace {
+template <int MODE>
+void launch_pf(int P, dim3 grid, hipStream_t stream, const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+               const int64_t *base, const int32_t *n, int32_t T, int32_t G, float *scores, int64_t ld,
+               int64_t chunk, const uint32_t *need, const PfCollect &col)
+{
+    if constexpr (MODE != kPfScores)     // groups of 16 queries: eight pairs, one per wave
+        hipLaunchKernelGGL((indexer_prefill_kernel<8, MODE>), grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx,
+                           base, n, T, G, scores, ld, chunk, need, col);
+    else if (P == 1)
+        hipLaunchKernelGGL((indexer_prefill_kernel<1, MODE>), grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx,
+                           base, n, T, G, scores, ld, chunk, need, col);
+    else if (P == 2)
+        hipLaunchKernelGGL((indexer_prefill_kernel<2, MODE>), grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx,
+                           base, n, T, G, scores, ld, chunk, need, col);
+    else if (P == 4)
+        hipLaunchKernelGGL((indexer_prefill_kernel<4, MODE>), grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx,
+                           base, n, T, G, scores, ld, chunk, need, col);
+    else
+        hipLaunchKernelGGL((indexer_prefill_kernel<8, MODE>), grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx,
+                           base, n, T, G, scores, ld, chunk, need, col);
+}
+}  // namespace
+
+hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                  const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                  int32_t H_I, int32_t D_I, int32_t G, float *scores, int64_t ld,
+                                  hipStream_t stream, const uint32_t *need)
+{
+    if (!indexer_prefill_supported(H_I, D_I) || G < 1 || G > kPfQ)
+        return hipErrorInvalidValue;
+    if (T == 0 || max_n == 0)
+        return hipSuccess;
+    const int64_t groups = (T + G - 1) / G;
+    const int P = G <= 2 ? 1 : (G <= 4 ? 2 : (G <= 8 ? 4 : 8));
+    const int64_t chunk = indexer_prefill_chunk(T, G, max_n);
     const int64_t nchunks = (max_n + chunk - 1) / chunk;
     if (groups > 65535)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nchunks, (unsigned)groups);
-    if (trace_skip("indexer_prefill_kernel"))
-        ;
-    else if (P == 1)
-        hipLaunchKernelGGL(indexer_prefill_kernel<1>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
-                           T, G, scores, ld, chunk);
-    else if (P == 2)
-        hipLaunchKernelGGL(indexer_prefill_kernel<2>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
-                           T, G, scores, ld, chunk);
-    else if (P == 4)
-        hipLaunchKernelGGL(indexer_prefill_kernel<4>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
-                           T, G, scores, ld, chunk);
-    else
-        hipLaunchKernelGGL(indexer_prefill_kernel<8>, grid, dim3(kPfThreads), 0, stream, q_idx, w, k_idx, base, n,
-                           T, G, scores, ld, chunk);
+    if (!trace_skip("indexer_prefill_kernel"))
+        launch_pf<kPfScores>(P, dim3((unsigned)nchunks, (unsigned)groups), stream, q_idx, w, k_idx, base, n, T, G,
+                             scores, ld, chunk, need, PfCollect{});
     trace_launch(stream, "indexer_prefill_kernel");
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_prefill_sample(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                         const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                         float *scores, int64_t ld, hipStream_t stream)
+{
+    if (T == 0 || max_n == 0)
+        return hipSuccess;
+    const int64_t max_s = (max_n + kPfSampleStride - 1) / kPfSampleStride;
+    const int64_t groups = (T + kPfQ - 1) / kPfQ;
+    const int64_t chunk = indexer_prefill_chunk(T, kPfQ, max_s);
+    const int64_t nchunks = (max_s + chunk - 1) / chunk;
+    if (groups > 65535)
+        return hipErrorInvalidValue;
+    if (!trace_skip("indexer_prefill_sample"))
+        launch_pf<kPfSample>(8, dim3((unsigned)nchunks, (unsigned)groups), stream, q_idx, w, k_idx, base, n, T, kPfQ,
+                             scores, ld, chunk, nullptr, PfCollect{});
+    trace_launch(stream, "indexer_prefill_sample");
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_prefill_collect(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                          const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                          const uint32_t *bound, uint64_t *slices, uint32_t *counts, int32_t cap,
+                                          hipStream_t stream)
+{
+    if (T == 0 || max_n == 0)
+        return hipSuccess;
+    const int64_t groups = (T + kPfQ - 1) / kPfQ;
+    const int64_t chunk = indexer_prefill_chunk(T, kPfQ, max_n);
+    const int64_t nchunks = (max_n + chunk - 1) / chunk;
+    if (groups > 65535)
+        return hipErrorInvalidValue;
+    if (!trace_skip("indexer_prefill_collect"))
+        launch_pf<kPfCollect>(8, dim3((unsigned)nchunks, (unsigned)groups), stream, q_idx, w, k_idx, base, n, T, kPfQ,
+                              nullptr, 0, chunk, nullptr, PfCollect{bound, slices, counts, cap});
+    trace_launch(stream, "indexer_prefill_collect");
     return hipGetLastError();
 }
 

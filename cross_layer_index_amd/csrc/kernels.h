@@ -29,11 +29,28 @@ hipError_t launch_indexer_decode(const uint8_t *q_idx, const float *w, const uin
 // group of queries through LDS.
 // Shared-sequence indexer: groups of G (<= 16) consecutive queries, each
 // group reading one sequence (every base[t] equal within a group).
+// With `need` non-null only groups holding a query with need[t] != 0 run.
 hipError_t launch_indexer_prefill(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
                                   const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
                                   int32_t H_I, int32_t D_I, int32_t G, float *scores, int64_t ld,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const uint32_t *need = nullptr);
 bool indexer_prefill_supported(int32_t H_I, int32_t D_I);
+// Token chunk per workgroup of the shared-key launch for these sizes.
+int64_t indexer_prefill_chunk(int32_t T, int32_t G, int64_t max_n);
+// Causal prefill with the bounded collection (H_I = 64, D_I = 128, groups of
+// 16): scores of the sampled keys (sample row i = key row
+// kPfSampleStride * i; query t sees ceil(n_t / kPfSampleStride) of them) into
+// scores [T, ld]; and the collection of every score at or above bound[t]
+// (order keys) into the slices [T, nchunks, cap] with their counts [T, nchunks]
+// (nchunks from indexer_prefill_chunk(T, 16, max_n)).
+constexpr int64_t kPfSampleStride = 64;
+hipError_t launch_indexer_prefill_sample(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                         const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                         float *scores, int64_t ld, hipStream_t stream);
+hipError_t launch_indexer_prefill_collect(const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                                          const int64_t *base, const int32_t *n, int32_t T, int64_t max_n,
+                                          const uint32_t *bound, uint64_t *slices, uint32_t *counts, int32_t cap,
+                                          hipStream_t stream);
 
 // ---- top-k ------------------------------------------------------------------
 // The workspace starts with the first-digit histograms [T][copies][2048]
@@ -47,8 +64,19 @@ uint32_t *topk_hist0(void *ws);
 bool topk_reads_hist0(int32_t T, int64_t max_n);
 hipError_t launch_clear_hist0(void *ws, int32_t T, hipStream_t stream);
 // hist_ready: the histograms were filled while the scores were produced.
+// With `need` non-null (row path only) only queries with need[t] != 0 run.
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n,
-                       int32_t k, int32_t *idx, void *ws, bool hist_ready, hipStream_t stream);
+                       int32_t k, int32_t *idx, void *ws, bool hist_ready, hipStream_t stream,
+                       const uint32_t *need = nullptr);
+// Causal prefill with bounded collection: per-query key bounds from the
+// sample scores [T, ld]; then the selection from the collected slices
+// (writes idx row t and need[t] = 0, or only need[t] = 1 when the scores
+// path must serve query t).
+hipError_t launch_prefill_bound(const float *sample, int64_t ld, const int32_t *n, int32_t T, int32_t k,
+                                uint32_t *bound, bool none, hipStream_t stream);
+hipError_t launch_prefill_select(const uint64_t *slices, const uint32_t *counts, int32_t nchunks, int64_t chunk,
+                                 int32_t cap, const int32_t *n, int32_t T, int32_t k, int32_t *idx, uint32_t *need,
+                                 hipStream_t stream);
 
 // Split path in two launches around a consumer that selects itself: the
 // first phase (the collected keys at or above a sampled bound, per query, in

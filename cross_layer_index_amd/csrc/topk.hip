@@ -466,11 +466,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
                                                                const int32_t *__restrict__ n, int32_t k,
                                                                int32_t *__restrict__ idx,
                                                                uint32_t *__restrict__ hist0,
-                                                               uint64_t *__restrict__ surv)
+                                                               uint64_t *__restrict__ surv,
+                                                               const uint32_t *__restrict__ gate)
 {
     __shared__ Shared sh;
     __shared__ __align__(16) uint64_t list[kRowListCap];
     const int t = blockIdx.x;
+    if (gate && gate[t] == 0u)                    // a gated launch serves the marked queries only
+        return;
     const int tid = threadIdx.x;
     const int64_t nt = n[t];
     int32_t *out = idx + (int64_t)t * k;
@@ -531,6 +534,144 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float *__re
                                           out);
     else
         finish_select<kRowThreads>(src, sh, 1, d0 << 21, 0xFFE00000u, need, k, out);
+}
+
+// ---- causal prefill with bounded collection ---------------------------------
+// The prefill indexer first scores a strided sample of the keys (one in
+// kPfSampleStride). Per query, prefill_bound_kernel takes from the sample
+// scores a two-digit key bound at a sample rank of twice the k-th largest
+// key's expected rank plus 16; the collecting indexer then keeps every score
+// at or above the bound, per (query, token chunk) slice in position order,
+// and prefill_select_kernel finishes the selection from the slices. When at
+// least k scores reach the bound, the k-th largest key and all its ties are
+// among them, so the result is exact. A query with fewer than k, a slice
+// past its capacity, or more than fit the LDS list is marked in `need`;
+// the scores path (indexer and row top-k, gated by `need`) then serves it.
+constexpr int kPfSelMaxChunks = 1024;      // token chunks per query the selection reads
+
+// grid: T; block: kRowThreads. bound[t] = 0xFFFFFFFF when n_t <= k (nothing
+// to collect: every position is kept) or when `none` is set (nothing
+// collected: every longer query takes the score rows), 0 when the sample
+// cannot bound the k-th key (everything is collected).
+__global__ __launch_bounds__(kRowThreads) void prefill_bound_kernel(const float *__restrict__ sample, int64_t ld,
+                                                                    const int32_t *__restrict__ n, int32_t k,
+                                                                    uint32_t *__restrict__ bound, int32_t none)
+{
+    __shared__ Shared sh;
+    const int t = blockIdx.x;
+    const int64_t nt = n[t];
+    if (nt <= k || none) {
+        if (threadIdx.x == 0)
+            bound[t] = 0xFFFFFFFFu;
+        return;
+    }
+    const int64_t ns = (nt + kPfSampleStride - 1) / kPfSampleStride;
+    const uint64_t tgt = 2 * (((uint64_t)k * ns + nt - 1) / nt) + 16;
+    if (tgt > (uint64_t)ns) {
+        if (threadIdx.x == 0)
+            bound[t] = 0u;
+        return;
+    }
+    const RowSrc src{sample + (int64_t)t * ld, ns};
+    uint32_t b = 0, above = 0, d1 = 0, above1 = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int i = threadIdx.x; i < kBins0; i += kRowThreads)
+            sh.hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = (int64_t)threadIdx.x * 4; i < ns; i += (int64_t)kRowThreads * 4) {
+            uint32_t key[4];
+            int64_t pos[4];
+            bool ok[4];
+            src.get4(i, key, pos, ok);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (pass == 0)
+                    hist_add_wave(sh.hist, key[e] >> 21, ok[e]);
+                else if (ok[e] && (key[e] >> 21) == b)
+                    atomicAdd(&sh.hist[(key[e] >> 10) & (kBins0 - 1)], 1u);
+            }
+        }
+        __syncthreads();
+        if (pass == 0)
+            find_digit<kRowThreads>(sh, kBins0, (uint32_t)tgt, b, above);
+        else
+            find_digit<kRowThreads>(sh, kBins0, (uint32_t)tgt - above, d1, above1);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        bound[t] = (b << 21) | (d1 << 10);
+}
+
+// grid: T; block: kRowThreads. Query t's slices are those of the token
+// chunks its n_t rows reach; idx row t is written unless the query is marked.
+__global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(const uint64_t *__restrict__ slices,
+                                                                     const uint32_t *__restrict__ counts,
+                                                                     int32_t nchunks, int64_t chunk, int32_t cap,
+                                                                     const int32_t *__restrict__ n, int32_t k,
+                                                                     int32_t *__restrict__ idx,
+                                                                     uint32_t *__restrict__ need)
+{
+    __shared__ Shared sh;
+    __shared__ __align__(16) uint64_t list[kRowListCap];
+    __shared__ uint32_t offs[kPfSelMaxChunks + 1];
+    __shared__ uint32_t bad;
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nt = n[t];
+    int32_t *out = idx + (int64_t)t * k;
+    if (nt <= k) {
+        write_all<kRowThreads>(out, nt, k);
+        if (tid == 0)
+            need[t] = 0u;
+        return;
+    }
+    const int64_t nch = (nt + chunk - 1) / chunk;
+    if (nch > kPfSelMaxChunks) {
+        if (tid == 0)
+            need[t] = 1u;
+        return;
+    }
+    if (tid == 0)
+        bad = 0u;
+    __syncthreads();
+    // chunk counts, their running offsets and the total
+    uint32_t total = 0;
+    for (int64_t j0 = 0; j0 < nch; j0 += kRowThreads) {
+        const int64_t j = j0 + tid;
+        const uint32_t c = j < nch ? counts[(int64_t)t * nchunks + j] : 0u;
+        if (c > (uint32_t)cap)
+            bad = 1u;
+        uint32_t tot;
+        const uint32_t incl = block_scan<kRowThreads>(c, sh.waves, &tot);
+        if (j < nch)
+            offs[j + 1] = total + incl;
+        total += tot;
+    }
+    if (tid == 0)
+        offs[0] = 0u;
+    __syncthreads();
+    if (bad || total < (uint32_t)k || total > (uint32_t)kRowListCap) {
+        if (tid == 0)
+            need[t] = 1u;
+        return;
+    }
+    // gather the slices into one position-ordered list
+    const uint64_t *sl = slices + (int64_t)t * nchunks * cap;
+    for (uint32_t f = tid; f < total; f += kRowThreads) {
+        int lo = 0, hi = (int)nch - 1;                // chunk j with offs[j] <= f < offs[j + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (offs[mid] <= f)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        list[f] = sl[(int64_t)lo * cap + (f - offs[lo])];
+    }
+    __syncthreads();
+    finish_select<kRowThreads>(ListSrc{list, total}, sh, 0, 0u, 0u, (uint32_t)k, k, out);
+    if (tid == 0)
+        need[t] = 0u;
 }
 
 // grid-stride fill of the first-digit histograms with zeros (a kernel, not a
@@ -626,14 +767,41 @@ hipError_t launch_topk_collect(const float *scores, int64_t ld, const int32_t *n
     return hipGetLastError();
 }
 
+hipError_t launch_prefill_bound(const float *sample, int64_t ld, const int32_t *n, int32_t T, int32_t k,
+                                uint32_t *bound, bool none, hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    if (!trace_skip("prefill_bound_kernel"))
+        hipLaunchKernelGGL(prefill_bound_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, sample, ld, n, k,
+                           bound, (int32_t)none);
+    trace_launch(stream, "prefill_bound_kernel");
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_select(const uint64_t *slices, const uint32_t *counts, int32_t nchunks, int64_t chunk,
+                                 int32_t cap, const int32_t *n, int32_t T, int32_t k, int32_t *idx, uint32_t *need,
+                                 hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    if (!trace_skip("prefill_select_kernel"))
+        hipLaunchKernelGGL(prefill_select_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, slices, counts,
+                           nchunks, chunk, cap, n, k, idx, need);
+    trace_launch(stream, "prefill_select_kernel");
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_t T, int64_t max_n, int32_t k,
-                       int32_t *idx, void *ws, bool hist_ready, hipStream_t stream)
+                       int32_t *idx, void *ws, bool hist_ready, hipStream_t stream, const uint32_t *need)
 {
     if (T == 0)
         return hipSuccess;
     const TopkLayout L = topk_layout(T, max_n);
     char *base = static_cast<char *>(ws);
     uint32_t *hist0 = reinterpret_cast<uint32_t *>(base + L.hist_off);
+    if (L.split && need)
+        return hipErrorInvalidValue;              // gating is a row-path feature
     if (L.split) {
         uint32_t *counts = reinterpret_cast<uint32_t *>(base + L.counts_off);
         uint64_t *regions = reinterpret_cast<uint64_t *>(base + L.regions_off);
@@ -653,7 +821,7 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
     } else {
         if (!trace_skip("topk_row_kernel"))
             hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)T), dim3(kRowThreads), 0, stream, scores, ld, n, k, idx,
-                           hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off));
+                           hist_ready ? hist0 : nullptr, reinterpret_cast<uint64_t *>(base + L.regions_off), need);
         trace_launch(stream, "topk_row_kernel");
     }
     return hipGetLastError();
