@@ -85,7 +85,7 @@ __device__ __forceinline__ void load_run(const uint8_t *p, v8i (&frag)[IdxGeom<D
 constexpr int kIdxWaves = 4;
 constexpr int kIdxThreads = kIdxWaves * 64;
 constexpr int kIdxStep = kIdxWaves * 32 * 2;                  // tokens per WG step of two groups
-constexpr int kIdxMaxChunk = 512;                              // tokens per WG, upper bound
+constexpr int kIdxMaxChunk = 1024;                             // tokens per WG, upper bound
 constexpr int64_t kIdxResident = 2 * 256;                      // resident WGs: 2 per CU x 256 CUs
 
 // One wave step's key fragments: U groups of 32 tokens, each lane holding its
