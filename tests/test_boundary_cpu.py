@@ -300,3 +300,45 @@ def test_write_cache_validation(ic):
     assert f(tk(T=0, row=None, pos=None), *key, *lat, None) == ic.IC_OK                        # nothing to do
     # a key without rotation reads no table
     assert f(tk(T=3, rope=None, n_pos=0, key_rope=0, row=FAKE + 1), *key, None, 0, None, None) == ic.IC_ERR_ALIGN
+
+
+def test_prefill_collection_workspace(ic, monkeypatch):
+    """Causal prefill of at least 256 queries over rows of at least 65,536
+    tokens selects from a bounded collection of the scores: its workspace
+    adds the sample scores, bounds, survivor slices and marks to the score
+    rows (kept for queries the collection cannot serve). Shorter rows, fewer
+    queries, queries that do not share one sequence, and IC_PREFILL_TOPK=scores
+    keep the plain layout; IC_PREFILL_TOPK=collect or =fallback takes the
+    collection at any length."""
+    d = ic.dims(64, 128, 2048, 128, 576, 512)
+    size = lambda qs: ic._lib.ic_layer_stack_workspace_size(ctypes.byref(qs), ctypes.byref(d))
+
+    def prefill(T, n):
+        return ic.ic_queries(FAKE, FAKE, T, 1, n, n)
+
+    monkeypatch.delenv("IC_PREFILL_TOPK", raising=False)
+    long_, short = prefill(4096, 1 << 20), prefill(4096, 65535)
+    plain = {}
+    monkeypatch.setenv("IC_PREFILL_TOPK", "scores")
+    for name, qs in (("long", long_), ("short", short)):
+        plain[name] = size(qs)
+    monkeypatch.delenv("IC_PREFILL_TOPK")
+    assert size(short) == plain["short"]
+    extra = size(long_) - plain["long"]
+    T, n = 4096, 1 << 20
+    sample = T * ((n + 63) // 64) * 4              # one key in 64, fp32
+    assert extra > sample + 2 * T * 4              # sample scores, bounds, marks and the slices
+    # slices: per chunk twice its expected share of the survivors plus 64,
+    # rounded to 64 entries: a few times the ~2k + 1024 expected per query
+    assert extra < sample + T * 8 * (2 * 2048 + 16 * 64) * 8
+    monkeypatch.setenv("IC_PREFILL_TOPK", "scores")
+    few_plain = size(prefill(255, 1 << 20))
+    own = ic.ic_queries(FAKE, FAKE, 4096, 0, 1 << 20, 4096 << 20)   # every query its own cache
+    own_plain = size(own)
+    monkeypatch.setenv("IC_PREFILL_TOPK", "collect")
+    assert size(prefill(255, 1 << 20)) == few_plain   # fewer than 256 queries: never collects
+    assert size(own) == own_plain                      # no shared sequence: never collects
+    forced = size(short)
+    assert forced > plain["short"]                     # collects at any length when asked
+    monkeypatch.setenv("IC_PREFILL_TOPK", "fallback")
+    assert size(short) == forced
