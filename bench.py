@@ -217,7 +217,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode_128k",
-                    choices=["decode_128k", "ragged_64", "stack_78", "prefill_1m", "mtp_verify", "tiny_2layer"])
+                    choices=["decode_128k", "ragged_64", "stack_78", "prefill_1m", "mtp_verify", "tiny_2layer",
+                             "decode_128k_recency"])
     ap.add_argument("--sets", type=int, default=None, help="rotating input sets (default: enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

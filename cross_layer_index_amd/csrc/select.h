@@ -229,6 +229,40 @@ struct GListSrc {
     }
 };
 
+// The split phase's slices in global memory as one list: slice s (P of them,
+// each in position order, the slices in chunk order) holds off[s + 1] - off[s]
+// entries from reg + s * stride; off (P + 1 words) is in LDS.
+struct SliceSrc {
+    static constexpr bool kLds = false;
+    const uint64_t *reg;
+    int64_t stride;
+    const uint32_t *off;
+    int32_t P;
+    int64_t n;
+    __device__ void get4(int64_t i, uint32_t (&key)[4], int64_t (&pos)[4], bool (&ok)[4]) const
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t j = (uint32_t)(i + e);
+            ok[e] = i + e < n;
+            uint64_t v = 0ull;
+            if (ok[e]) {
+                int lo = 0, hi = P - 1;               // the slice s with off[s] <= j < off[s + 1]
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (off[mid] <= j)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                v = reg[(int64_t)lo * stride + (j - off[lo])];
+            }
+            key[e] = (uint32_t)(v >> 32);
+            pos[e] = (int64_t)(uint32_t)v;
+        }
+    }
+};
+
 // Calls f(key, live) once for every entry of `src`, in no particular order,
 // with every lane of the wave taking part in each call (f may use ballots).
 // An LDS list is read interleaved (lane i takes entry i, i + NT, ...), which
@@ -398,19 +432,25 @@ __device__ void finish_select(const Src &src, Shared &sh, int first, uint32_t pr
 // ordered by (r, tid), so one block scan per round orders the output. load()
 // issues the loads before the counts are known (clamped, unconditional);
 // select() calls emit(slot, position) for every selected key (slot in
-// [0, k)). A slice longer than C, or fewer than k keys at the bound, takes the
-// digits over the whole row instead. The caller handles rows of at most k keys.
+// [0, k)). A slice longer than C takes the digits over the slices in global
+// memory (every key at or above the bound is there, in position order); fewer
+// than k keys at the bound take them over the whole row. The caller handles
+// rows of at most k keys.
 template <int NT, int E>
 struct SplitSel {
     static_assert(E % 4 == 0, "groups of four");
     static constexpr int R = E / 4;
     uint32_t key[E], pos[E];
     uint32_t C;
+    const uint64_t *reg;
+    int64_t stride;
 
     // (both members inline into the caller: called, they would keep the
     // arrays in memory behind `this`)
-    __device__ __forceinline__ void load(const uint64_t *reg_t, int64_t stride, int32_t P)
+    __device__ __forceinline__ void load(const uint64_t *reg_t, int64_t stride_, int32_t P)
     {
+        reg = reg_t;
+        stride = stride_;
         C = min((uint32_t)(NT * E) / (uint32_t)P, (uint32_t)stride) & ~3u;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -425,8 +465,8 @@ struct SplitSel {
         }
     }
 
-    // cnt: P + 1 + R * NT / 64 words of LDS (the slice counts, an overflow
-    // flag, the scan's wave totals)
+    // cnt: P + 1 + R * NT / 64 + P + 1 words of LDS (the slice counts, an
+    // overflow flag, the scan's wave totals, the slice offsets)
     // Only slots in [s0, s1) are emitted (a group whose slots lie outside
     // skips the per-key work).
     template <class Emit>
@@ -444,12 +484,24 @@ struct SplitSel {
                 cnt[P] = 1;
         }
         uint32_t total;
-        block_scan<NT, LB>(c0, sh.waves, &total);     // its barriers publish cnt
-        if (total < (uint32_t)k || cnt[P] != 0) {
-            select_emit<NT, LB>(row, sh, 0, 0u, 0u, (uint32_t)k, k, [&](uint32_t slot, int32_t p) {
-                if (slot >= s0 && slot < s1)
-                    emit(slot, p);
-            });
+        const uint32_t incl = block_scan<NT, LB>(c0, sh.waves, &total);     // its barriers publish cnt
+        auto in_split = [&](uint32_t slot, int32_t p) {
+            if (slot >= s0 && slot < s1)
+                emit(slot, p);
+        };
+        if (total < (uint32_t)k) {
+            select_emit<NT, LB>(row, sh, 0, 0u, 0u, (uint32_t)k, k, in_split);
+            return;
+        }
+        if (cnt[P] != 0) {
+            uint32_t *off = cnt + P + 1 + R * NT / 64;
+            if (tid < P)
+                off[tid + 1] = incl;
+            if (tid == 0)
+                off[0] = 0u;
+            wg_barrier<LB>();
+            select_emit<NT, LB>(SliceSrc{reg, stride, off, P, (int64_t)total}, sh, 0, 0u, 0u, (uint32_t)k, k,
+                                in_split);
             return;
         }
         // which entries hold keys (a group of four lies in one slice)

@@ -299,9 +299,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // this split's rows are the slots [j_begin, j_end) of the query's
         // selection (position order); the selection's LDS (histograms, slice
         // counts) borrows the score-exchange buffer, unused until the tile loop
-        // Shared, then P + 1 slice counts (P <= kMlaThreads) and the scan's
-        // wave totals
-        static_assert(sizeof(Shared) + 4 * (kMlaThreads + 1 + (kSelPerThread / 4) * kWaves) <= sizeof(sx),
+        // Shared, then P + 1 slice counts (P <= kMlaThreads), the scan's wave
+        // totals and P + 1 slice offsets
+        static_assert(sizeof(Shared) + 4 * (2 * (kMlaThreads + 1) + (kSelPerThread / 4) * kWaves) <= sizeof(sx),
                       "the selection's LDS fits the exchange buffer");
         Shared &sh = *reinterpret_cast<Shared *>(&sx[0][0][0][0]);
         uint32_t *cnt = reinterpret_cast<uint32_t *>(&sh + 1);

@@ -69,6 +69,7 @@ class Workload:
     prefill_first_pos: Optional[int] = None  # causal prefill: p_t = first + t
     prefill_rows: Optional[int] = None  # rows of the one shared cache (prefill)
     group: int = 1                      # consecutive queries sharing one sequence (draft/verify)
+    recency: bool = False               # indexer scores that rise with position (recent tokens win)
     seq_lengths: Optional[List[int]] = None  # with group > 1: rows of each sequence
     description: str = ""
 
@@ -236,10 +237,24 @@ def layer_inputs(wl: Workload, layer: int, device="cpu", with_indexer=True, vari
     lo, hi = wl.qk_range
     wlo, whi = wl.w_range
     if with_indexer:
-        q_idx = _int_fp8((wl.T, wl.H_I, wl.D_I), lo, hi, _gen(device, sub_seed(s, layer, _TID_QI)), device)
+        q_idx = _int_fp8((wl.T, wl.H_I, wl.D_I), 0 if wl.recency else lo, hi,
+                         _gen(device, sub_seed(s, layer, _TID_QI)), device)
         w = torch.randint(wlo, whi + 1, (wl.T, wl.H_I), generator=_gen(device, sub_seed(s, layer, _TID_W)),
                           device=device, dtype=torch.int32).to(torch.float32)
-        k_idx = _int_fp8((rows, wl.D_I), lo, hi, _gen(device, sub_seed(s, layer, _TID_KI)), device)
+        if wl.recency:
+            # non-negative q (above) and key codes raised by floor(9 s / n) at
+            # position s of an n-row sequence, clamped to the range: every
+            # head's dot, and so the score, grows with position on average
+            assert not wl.same_seq and wl.group == 1, "recency draws are for decode workloads"
+            v = torch.randint(lo, hi + 1, (rows, wl.D_I), generator=_gen(device, sub_seed(s, layer, _TID_KI)),
+                              device=device, dtype=torch.int32)
+            n = wl.n_valid().to(torch.int64)
+            pos = torch.arange(rows, dtype=torch.int64) - torch.repeat_interleave(wl.base(), n)
+            trend = (9 * pos // torch.repeat_interleave(n, n)).to(device=device, dtype=torch.int32)
+            v = (v + trend[:, None]).clamp_(lo, hi)
+            k_idx = v.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            k_idx = _int_fp8((rows, wl.D_I), lo, hi, _gen(device, sub_seed(s, layer, _TID_KI)), device)
     else:
         q_idx = w = k_idx = None
     q = _randn_bf16((wl.T, wl.H, wl.D_qk), _gen(device, sub_seed(s, layer, _TID_Q)), device)
@@ -290,6 +305,11 @@ WORKLOADS = {
         name="mtp_verify", seed=6, n_layers=1, full_layers=[0], T=32, H_I=64, D_I=128, k=2048,
         H=128, D_qk=576, D_v=512, group=4, seq_lengths=[131072] * 8,
         description="draft/verify decode: 8 sequences x 4 queries each over one shared cache, L=131072"),
+    "decode_128k_recency": Workload(
+        name="decode_128k_recency", seed=12, n_layers=1, full_layers=[0], T=1, H_I=64, D_I=128, k=2048,
+        H=128, D_qk=576, D_v=512, lengths=[131072], recency=True,
+        description="decode_128k with indexer scores rising with position: the top-k crowds into the last "
+                    "chunk of the row (a slice of the split top-k holds far more than its share)"),
     "edge_lengths": Workload(
         name="edge_lengths", seed=11, n_layers=1, full_layers=[0], T=9, H_I=64, D_I=128, k=2048,
         H=128, D_qk=576, D_v=512, lengths=[0, 1, 63, 64, 65, 2047, 2048, 2049, 4095],

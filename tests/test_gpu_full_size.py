@@ -111,6 +111,14 @@ def test_decode_128k_full(gpu, orc):
     run_case(gpu, orc, wl, [0], device_gen=False)
 
 
+def test_decode_128k_recency_full(gpu, orc):
+    """Scores rising with position: the top-k lies in the row's last chunks,
+    so a slice of the split top-k holds more keys than the selecting sparse
+    MLA keeps in registers and the selection runs over the slices."""
+    wl = W.WORKLOADS["decode_128k_recency"]
+    run_case(gpu, orc, wl, [0], device_gen=False)
+
+
 def test_ragged_64_full(gpu, orc):
     wl = W.WORKLOADS["ragged_64"]
     n = wl.n_valid().numpy()
