@@ -80,15 +80,15 @@ def indexer_flops(n: int, H_I: int, D_I: int) -> int:
 # source files whose text a kernel's counters were taken on
 KERNEL_SOURCES = {
     "indexer_decode_kernel": ["indexer.hip", "radix_key.h"],
-    "indexer_prefill_kernel": ["indexer.hip"],
-    "sparse_mla_kernel": ["sparse_mla.hip", "select.h"],
-    "sparse_mla_kernel<selecting>": ["sparse_mla.hip", "select.h"],
+    "indexer_prefill_kernel": ["indexer.hip", "lds_dma.h"],
+    "sparse_mla_kernel": ["sparse_mla.hip", "select.h", "lds_dma.h"],
+    "sparse_mla_kernel<selecting>": ["sparse_mla.hip", "select.h", "lds_dma.h"],
     "mla_combine_kernel": ["sparse_mla.hip"],
     "topk_collect_kernel": ["topk.hip", "select.h", "radix_key.h"],
     "topk_finish_kernel": ["topk.hip", "select.h", "radix_key.h"],
     "topk_row_kernel": ["topk.hip", "select.h", "radix_key.h"],
-    "indexer_prefill_sample": ["indexer.hip"],
-    "indexer_prefill_collect": ["indexer.hip", "radix_key.h"],
+    "indexer_prefill_sample": ["indexer.hip", "lds_dma.h"],
+    "indexer_prefill_collect": ["indexer.hip", "radix_key.h", "lds_dma.h"],
     "prefill_bound_kernel": ["topk.hip", "select.h", "radix_key.h"],
     "prefill_select_kernel": ["topk.hip", "select.h", "radix_key.h"],
 }

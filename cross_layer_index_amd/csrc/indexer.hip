@@ -19,6 +19,7 @@
 //   Accumulator element r of lane l is (row 8*(r/4) + 4*(l/32) + r%4,
 //   column l % 32).
 #include "kernels.h"
+#include "lds_dma.h"
 #include "radix_key.h"
 
 namespace ic {
@@ -402,7 +403,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
     }
 
     // fills of this wave's group: row 32*wave + lane%32 of the tile (clamped
-    // to the group's extent), bytes 64*(lane/32) + 16*v for slab v
+    // to the group's extent), bytes 64*(lane/32) + 16*v for slab v; four fill
+    // instructions per wave per tile, by 32-bit offsets from the sequence's
+    // first key row (the rows of one sequence span less than 4 GiB)
     const int64_t frow = 32 * wave + j;
     const int fcol = 64 * g;
     auto issue = [&](uint8_t *buf, int64_t tile) {
@@ -410,11 +413,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
         row = row < s_end ? row : s_end - 1;
         if (MODE == kPfSample)
             row *= kPfSampleStride;
-        const uint8_t *src = krows + row * kPfDI + fcol;
-        uint8_t *dst = buf + wave * kPfGroupBytes;
+        const uint32_t off = (uint32_t)(row * kPfDI + fcol);
+        const uint32_t dst = (uint32_t)(uintptr_t)(lds_void *)buf + wave * kPfGroupBytes;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            __builtin_amdgcn_global_load_lds(src + 16 * v, (lds_void *)(dst + v * kPfSlab), 16, 0, 0);
+            lds_fill16(krows, off + 16 * v, dst + v * kPfSlab);
     };
 
     auto bfrag = [&](const uint8_t *tb, int gi, v8i (&b)[G::KS]) {
@@ -488,18 +491,25 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(
         }
     };
 
-    // ring of three tiles: tile it+1 is in flight while tile it is scored and
-    // tile it+2 is issued at the top of iteration it. The score stores share
-    // the vector-memory counter with the fills (and may complete out of
-    // order with them), so the wait before a tile is a full one.
+    // ring of three tiles: tile it+2 is issued at the top of iteration it and
+    // tiles it+1 and it+2 stay in flight while tile it is scored. The score
+    // stores share the vector-memory counter with the fills, but loads
+    // complete in order among themselves: with at most four operations
+    // outstanding, and tile it+1's four fills issued after tile it's, tile
+    // it's fills are complete whatever the stores do. The barrier then orders
+    // LDS only (a full one would also wait for the fills in flight).
     const int ntiles = (int)((s_end - s_begin + kPfTile - 1) / kPfTile);
     issue(tile0, s_begin);
     if (ntiles > 1)
         issue(tile1, s_begin + kPfTile);
     // the ring unrolled by three so that every access names its buffer
     auto step = [&](int it, uint8_t *cur, uint8_t *ahead) {
-        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));    // vmcnt(0)
-        __syncthreads();            // tile it is in LDS for every wave; `ahead` is free
+        if (it + 1 < ntiles)
+            wait_vmcnt<4>();
+        else
+            wait_vmcnt<0>();
+        // tile it is in LDS for every wave; `ahead` is free
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (it + 2 < ntiles)
             issue(ahead, s_begin + (int64_t)(it + 2) * kPfTile);
         compute(cur, s_begin + (int64_t)it * kPfTile);

@@ -30,6 +30,7 @@
 #include <cstring>
 
 #include "kernels.h"
+#include "lds_dma.h"
 #include "select.h"
 
 namespace ic {
@@ -163,13 +164,6 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at max)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 // grid: splits * ceil(H/64) * T workgroups (1-D; the work unit comes from the
 // linear id, see below); block: 512 = 4 head groups x 2 halves.
@@ -697,29 +691,6 @@ constexpr float kHeadroom = 32.0f;                         // log2 of the larges
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// One 64-lane LDS fill (global_load_lds, 16 bytes a lane): lane l's bytes
-// base + voff land at LDS byte address lds + 16 l. Written as inline asm so
-// that the compiler does not track it: with four buffers in flight its own
-// alias bookkeeping for such fills falls back to waiting for all of them
-// before a read of any buffer. The fill has no register result; the waits
-// for it are the explicit ones in the tile loop (and any wait the compiler
-// places for its own loads only waits longer). M0 is written in the same
-// block, one wait state before its use.
-__device__ __forceinline__ void lds_fill16(const void *base, uint32_t voff, uint32_t lds)
-{
-    // base and lds are the same in every lane (a wave's fill has one source
-    // base and one LDS span); say so to the compiler, which keeps them in
-    // scalar registers, M0 for the LDS address
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint64_t bs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
-                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
-    asm volatile("s_nop 0\n\t"
-                 "global_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(bs), "{m0}"(__builtin_amdgcn_readfirstlane((int)lds))
-                 : "memory");
-}
 
 __device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8 &a, const bf16x8 &b, const v16f &c)
 {
