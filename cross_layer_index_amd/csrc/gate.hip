@@ -9,7 +9,10 @@
 // wrong space.)
 //
 // A workgroup (8 waves) owns one head, a run of 16-query blocks and up to
-// 128 output columns, each wave one 16-column tile. v_mfma_f32_16x16x32_bf16
+// 128 output columns, each wave one 16-column tile. The gate values and the
+// results of a block travel as whole 16-byte chunks of their rows through LDS
+// (loaded with the block's o, stored after it by the workgroup together),
+// rather than as two bytes a lane. v_mfma_f32_16x16x32_bf16
 // with queries on M and output columns on N: A lane l holds
 // o[t0 + l%16][h][32*ks + 8*(l/16) .. +8], B lane l holds
 // wv_b[h][e + l%16][32*ks + 8*(l/16) .. +8] (the contraction runs along the
@@ -52,6 +55,10 @@ struct GateGeom {
     static constexpr int CHUNKS = kGateRows * CH;              // per block
     static constexpr int PER = (CHUNKS + NT - 1) / NT;         // chunks per thread
     static constexpr int COLS = NT / 64 * 16;                  // columns per workgroup
+    static constexpr int GROWB = COLS * 2 + 16;                // LDS bytes per gate / output row
+    static constexpr int GCH = COLS * 2 / 16;                  // 16-byte chunks per gate / output row
+    static constexpr int GCHUNKS = kGateRows * GCH;            // per block (at most one per thread)
+    static_assert(GCHUNKS <= NT, "one gate chunk per thread");
 };
 
 // grid: (H * ceil(D_o / COLS), query chunks); NT threads (NT/64 waves, one
@@ -67,11 +74,16 @@ __global__ __launch_bounds__(NT) void gated_output_kernel(const uint16_t *__rest
     constexpr int wcols = GG::COLS;
     __shared__ __attribute__((aligned(16))) unsigned char ob0[kGateRows * GG::ROWB];
     __shared__ __attribute__((aligned(16))) unsigned char ob1[kGateRows * GG::ROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char gb0[kGateRows * GG::GROWB];   // gate values
+    __shared__ __attribute__((aligned(16))) unsigned char gb1[kGateRows * GG::GROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char rb0[kGateRows * GG::GROWB];   // results
+    __shared__ __attribute__((aligned(16))) unsigned char rb1[kGateRows * GG::GROWB];
     const int groups = (D_o + wcols - 1) / wcols;
     const int h = blockIdx.x / groups;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
     const int lane = threadIdx.x & 63;
-    const int e0 = (blockIdx.x % groups) * wcols + wave * 16;
+    const int eb = (blockIdx.x % groups) * wcols;             // the workgroup's first column
+    const int e0 = eb + wave * 16;
     const bool active = e0 < D_o;                 // D_o is a multiple of 16: whole tiles
     const int c = lane & 15;
     const int g = lane >> 4;
@@ -88,9 +100,19 @@ __global__ __launch_bounds__(NT) void gated_output_kernel(const uint16_t *__rest
             bv[ks] = *reinterpret_cast<const uint4 *>(brow + 32 * ks);
     }
 
-    // o block i: thread chunk q = row q / CH, 16-byte chunk q % CH (zero past T)
+    // o block i: thread chunk q = row q / CH, 16-byte chunk q % CH (zero past
+    // T); gate chunk q = threadIdx.x: row q / GCH, chunk q % GCH
     uint4 stg[GG::PER];
+    uint4 gstg;
+    const int gq = threadIdx.x;
+    const int gcol = eb + 8 * (gq % GG::GCH);
+    const bool gown = gq < GG::GCHUNKS && gcol < D_o;   // D_o is a multiple of 8: whole chunks
     auto fetch = [&](int i) {
+        {
+            const int t = kGateRows * (tb0 + i) + gq / GG::GCH;
+            gstg = gown && t < T ? *reinterpret_cast<const uint4 *>(gate + ((int64_t)t * H + h) * D_o + gcol)
+                                 : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int p = 0; p < GG::PER; ++p) {
             const int q = threadIdx.x + p * NT;
@@ -103,23 +125,25 @@ __global__ __launch_bounds__(NT) void gated_output_kernel(const uint16_t *__rest
             stg[p] = v;
         }
     };
-    auto stash = [&](unsigned char *buf) {
+    auto stash = [&](unsigned char *buf, unsigned char *gbuf) {
 #pragma unroll
         for (int p = 0; p < GG::PER; ++p) {
             const int q = threadIdx.x + p * NT;
             if (q < GG::CHUNKS)
                 *reinterpret_cast<uint4 *>(buf + (q / GG::CH) * GG::ROWB + 16 * (q % GG::CH)) = stg[p];
         }
+        if (gq < GG::GCHUNKS)
+            *reinterpret_cast<uint4 *>(gbuf + (gq / GG::GCH) * GG::GROWB + 16 * (gq % GG::GCH)) = gstg;
     };
-    // the gate values of this lane's four outputs of block i
-    auto load_gate = [&](int i, uint16_t (&gv)[4]) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = kGateRows * (tb0 + i) + 4 * g + r;
-            gv[r] = (active && t < T) ? gate[((int64_t)t * H + h) * D_o + e0 + c] : (uint16_t)0;
-        }
+    // the results of block i, rows of 16-byte chunks (chunks past D_o or
+    // rows past T are not stored)
+    auto store = [&](int i, const unsigned char *rbuf) {
+        const int t = kGateRows * (tb0 + i) + gq / GG::GCH;
+        if (gown && t < T)
+            *reinterpret_cast<uint4 *>(out + ((int64_t)t * H + h) * D_o + gcol) =
+                *reinterpret_cast<const uint4 *>(rbuf + (gq / GG::GCH) * GG::GROWB + 16 * (gq % GG::GCH));
     };
-    auto compute = [&](int i, const unsigned char *buf, const uint16_t (&gv)[4]) {
+    auto compute = [&](int i, const unsigned char *buf, const unsigned char *gbuf, unsigned char *rbuf) {
         if (!active)
             return;
         f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};   // two chains, summed at the end
@@ -133,38 +157,41 @@ __global__ __launch_bounds__(NT) void gated_output_kernel(const uint16_t *__rest
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = kGateRows * (tb0 + i) + 4 * g + r;
-            if (t < T) {
-                const float sg = 1.0f / (1.0f + __expf(-bf16_to_f32(gv[r])));
-                out[((int64_t)t * H + h) * D_o + e0 + c] = f32_to_bf16((acc[0][r] + acc[1][r]) * sg);
-            }
+            const int row = 4 * g + r;
+            const uint16_t gv = *reinterpret_cast<const uint16_t *>(gbuf + row * GG::GROWB + 2 * (e0 - eb + c));
+            const float sg = 1.0f / (1.0f + __expf(-bf16_to_f32(gv)));
+            *reinterpret_cast<uint16_t *>(rbuf + row * GG::GROWB + 2 * (e0 - eb + c)) =
+                f32_to_bf16((acc[0][r] + acc[1][r]) * sg);
         }
     };
 
-    uint16_t g0[4], g1[4];
     fetch(0);
-    load_gate(0, g0);
-    stash(ob0);
+    stash(ob0, gb0);
     if (nb > 1)
         fetch(1);
     __syncthreads();
-    // block i is in LDS and its successor's o in registers; after the
-    // multiply the successor goes to the other buffer and block i+2 is fetched
-    auto iter = [&](int i, const unsigned char *cur, unsigned char *nxt, uint16_t (&gc)[4], uint16_t (&gn)[4]) {
+    // block i (o and gate) is in LDS and its successor's in registers; the
+    // multiply leaves block i's results in its result buffer, the successor
+    // goes to the other buffers and block i+2 is fetched; after the barrier
+    // block i's results go out while block i+1 multiplies into the other
+    // result buffer
+    auto iter = [&](int i, const unsigned char *cur, unsigned char *nxt, const unsigned char *gcur,
+                    unsigned char *gnxt, unsigned char *rcur, const unsigned char *rprev) {
+        if (i > 0)
+            store(i - 1, rprev);
+        compute(i, cur, gcur, rcur);
         if (i + 1 < nb)
-            load_gate(i + 1, gn);
-        compute(i, cur, gc);
-        if (i + 1 < nb)
-            stash(nxt);
+            stash(nxt, gnxt);
         if (i + 2 < nb)
             fetch(i + 2);
         __syncthreads();
     };
     for (int i = 0; i < nb; i += 2) {
-        iter(i, ob0, ob1, g0, g1);
+        iter(i, ob0, ob1, gb0, gb1, rb0, rb1);
         if (i + 1 < nb)
-            iter(i + 1, ob1, ob0, g1, g0);
+            iter(i + 1, ob1, ob0, gb1, gb0, rb1, rb0);
     }
+    store(nb - 1, (nb - 1) & 1 ? rb1 : rb0);
 }
 
 }  // namespace
