@@ -131,7 +131,12 @@ ic_status ic_topk(const float *scores, int64_t ld, const ic_queries *qs, int32_t
  *   out [T, H, D_v] bf16 (round to nearest even) or fp32, per dims->out_dtype.
  * An all-empty selection gives zeros. Entries outside [0, n_valid[t]) are
  * treated as -1 on the device (they never address memory). QK^T and PV run on bf16 matrix cores
- * with fp32 accumulation and an fp32 online softmax; P is rounded to bf16. */
+ * with fp32 accumulation and an fp32 softmax; P is rounded to bf16 and the
+ * denominators sum the rounded values. Two kernel forms (64 heads per
+ * workgroup, or 128 for large grids with D_v = 512 and H a multiple of 128)
+ * are chosen by size; IC_MLA_FORM=narrow|wide in the environment overrides
+ * the choice. Long rows are split over workgroups whose partials a second
+ * kernel merges (the workspace holds them). */
 size_t ic_sparse_mla_workspace_size(const ic_queries *qs, const ic_dims *d);
 ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs,
                         const int32_t *idx, const float *sink, float scale, const ic_dims *d,
@@ -229,7 +234,16 @@ ic_status ic_reuse_map_last_full(int32_t n_layers, const uint8_t *is_full, int32
  *   indexer_passes (host, may be NULL): receives the number of full layers.
  * Validation of the map: reuse_map[0] == 0, and for l > 0 either
  * reuse_map[l] == l or reuse_map[l] < l with reuse_map[reuse_map[l]] equal to
- * reuse_map[l]. */
+ * reuse_map[l].
+ * A full layer of causal prefill (same_seq, at least 256 queries, max_n at
+ * least 65,536; indexer 64 x 128) takes its top-k from the scores at or
+ * above a per-query bound drawn from a strided sample of its keys instead of
+ * from whole score rows, with the score rows as the fallback for any query
+ * the collection cannot serve: the index sets are the same; the workspace
+ * size covers both. The environment variable IC_PREFILL_TOPK=scores|collect|
+ * fallback overrides that choice, and IC_MLA_FORM=narrow|wide the sparse-MLA
+ * form (both for testing and measurement; results are the same within the
+ * stated bounds). */
 size_t ic_layer_stack_workspace_size(const ic_queries *qs, const ic_dims *d);
 ic_status ic_layer_stack(int32_t n_layers, const ic_layer *layers, const int32_t *reuse_map,
                          const ic_queries *qs, const ic_dims *d, float scale,
