@@ -130,10 +130,17 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
     const int g = lane >> 5;
     const int j = lane & 31;
 
-    // the query's extent and first row (scalar loads) go out first; q
-    // fragments and weights, which do not depend on them, follow at once
+    // the query's extent and first row (scalar loads) first: a workgroup
+    // past the query's end (ragged batches launch the longest query's grid
+    // for every query) leaves before it issues any vector load, which would
+    // hold its slot until the data returned; the q fragments and weights go
+    // out together with the first key rows
     const int64_t nt = n[t];
     const int64_t bt = base[t];
+    asm volatile("" ::"s"(nt), "s"(bt));   // both loads complete here, not one after the other
+    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
+    if (s_begin >= nt)
+        return;
     v8i a[MT][G::KS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -149,11 +156,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_decode_kernel(
     float wv = 0.0f;
     if (threadIdx.x < MT * 32 && (int)threadIdx.x < H_I)
         wv = w[(int64_t)t * H_I + threadIdx.x];
-
-    asm volatile("" ::"s"(nt), "s"(bt));   // both loads complete here, not one after the other
-    const int64_t s_begin = (int64_t)blockIdx.x * chunk;
-    if (s_begin >= nt)
-        return;
     const int64_t s_end = min(nt, s_begin + chunk);
     const uint8_t *krows = k_idx + (bt * DI) + g * G::HALF;
     float *srow = scores + (int64_t)t * ld;
