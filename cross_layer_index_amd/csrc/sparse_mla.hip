@@ -1278,6 +1278,98 @@ __global__ __launch_bounds__(DV / 4) void mla_combine_kernel(const uint16_t *__r
     }
 }
 
+// The same merge for 512 value columns, one wave per head: lane l merges
+// columns 8l .. 8l + 7 (16 bytes of every split's partial row) and the wave
+// loads its head's (m, l, e0, e1) itself, so no workgroup barrier is needed:
+// each wave's split weights stay in its own LDS words, written and read back
+// by that wave alone. grid: (ceil(H / HPW), T); block: 64 * HPW threads.
+template <int CB, int HPW>
+__global__ __launch_bounds__(64 * HPW) void mla_combine512_kernel(const uint16_t *__restrict__ part_o,
+                                                                  const float *__restrict__ part_ml,
+                                                                  const float *__restrict__ sink, int32_t H,
+                                                                  int32_t splits, void *__restrict__ out,
+                                                                  int32_t out_f32)
+{
+    constexpr int DV = 512;
+    __shared__ float wgt[HPW][2][kMaxSplits];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.x * HPW + wave;
+    const int t = blockIdx.y;
+    if (h >= H)
+        return;                                   // the whole wave; no barrier follows
+    const int hf = lane >= 32;                    // columns 8 * lane lie in the second half
+    const int64_t pr0 = (int64_t)t * splits * H + h;           // row of split 0
+    const uint4 *p = reinterpret_cast<const uint4 *>(part_o + pr0 * DV) + lane;
+    const int64_t stride = (int64_t)H * DV / 8;               // uint4s between splits
+    uint4 x[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+        if (u < splits)
+            x[u] = p[(int64_t)u * stride];
+    constexpr int R = kMaxSplits / 64;
+    const float ms = sink[h] * kLog2e;
+    float4 ml[R];
+    float m = ms;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = lane + 64 * r;
+        ml[r] = s < splits ? *reinterpret_cast<const float4 *>(part_ml + (pr0 + (int64_t)s * H) * 4)
+                           : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+        m = fmaxf(m, ml[r].x);
+    }
+    m = wave_max<64>(m);
+    float d = lane == 0 ? exp2f(ms - m) : 0.0f;
+    float *wg = &wgt[wave][0][0];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int s = lane + 64 * r;
+        if (s < splits) {
+            const float wl = exp2f(ml[r].x - m) * ml[r].y;
+            wg[s] = ldexpf(wl, (int)ml[r].z);
+            wg[kMaxSplits + s] = ldexpf(wl, (int)ml[r].w);
+            d += wl;
+        }
+    }
+    const float inv = 1.0f / wave_sum<64>(d);
+    __builtin_amdgcn_wave_barrier();
+    const float *wh = wg + kMaxSplits * hf;
+    auto h2f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.0f;
+    for (int s0 = 0; s0 < splits; s0 += CB) {
+        if (s0 > 0) {
+#pragma unroll
+            for (int u = 0; u < CB; ++u)
+                if (s0 + u < splits)
+                    x[u] = p[(int64_t)(s0 + u) * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+            if (s0 + u < splits) {
+                const float wv = wh[s0 + u];
+                const uint32_t v4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = fmaf(h2f(v4[e] & 0xFFFFu), wv, acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(h2f(v4[e] >> 16), wv, acc[2 * e + 1]);
+                }
+            }
+    }
+    const int64_t oi = ((int64_t)t * H + h) * DV + 8 * lane;
+    if (out_f32) {
+        float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + oi);
+        o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    } else {
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + oi) =
+            make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                       pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
+    }
+}
+
 // Merges the wide form's split partials (register order, see its epilogue)
 // and adds the sink:
 //   out = sum_s 2^(m_s - m) l_s 2^e_s p_s / (2^(sink - m) + sum_s 2^(m_s - m) l_s)
@@ -1420,7 +1512,19 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
         hipLaunchKernelGGL((mla_combine_wide_kernel<512>), dim3((512 / 32) * (H / 32), T), dim3(64),
                            (size_t)plan.splits * 33 * sizeof(float), stream, part_o, part_ml, sink, H, plan.splits,
                            out, out_f32);
-    else if (plan.splits > kCombineBatchMax / 2)
+    else if (DV == 512) {
+        // four heads to a workgroup once that still leaves a workgroup per CU
+        const bool four = (int64_t)T * ((H + 3) / 4) >= kResidentWGs;
+        auto go = [&](auto kern, int hpw) {
+            hipLaunchKernelGGL(kern, dim3((H + hpw - 1) / hpw, T), dim3(64 * hpw), 0, stream, part_o, part_ml, sink, H,
+                               plan.splits, out, out_f32);
+        };
+        if (plan.splits > kCombineBatchMax / 2)
+            four ? go(mla_combine512_kernel<kCombineBatchMax, 4>, 4) : go(mla_combine512_kernel<kCombineBatchMax, 1>, 1);
+        else
+            four ? go(mla_combine512_kernel<kCombineBatchMax / 2, 4>, 4)
+                 : go(mla_combine512_kernel<kCombineBatchMax / 2, 1>, 1);
+    } else if (plan.splits > kCombineBatchMax / 2)
         hipLaunchKernelGGL((mla_combine_kernel<DV, kCombineBatchMax>), dim3(H, T), dim3(DV / 4), 0, stream, part_o,
                            part_ml, sink, H, plan.splits, out, out_f32);
     else
