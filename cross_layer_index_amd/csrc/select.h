@@ -184,6 +184,21 @@ struct RowSrc {
     }
 };
 
+// Four consecutive scores from one unconditional 16-byte load, the address
+// clamped into a row of capacity cap (a multiple of 4, at least 4; i a
+// multiple of 4); positions at or past cap come back not ok. A branch around
+// the load (RowSrc::get4) makes the compiler wait for each such load before
+// the next is issued; these go out back to back.
+__device__ __forceinline__ void row_get4u(const float *row, int64_t cap, int64_t i, uint32_t (&key)[4],
+                                          int64_t (&pos)[4], bool (&ok)[4])
+{
+    const float4 v = *reinterpret_cast<const float4 *>(row + min(i, cap - 4));
+    key[0] = ord_key(v.x), key[1] = ord_key(v.y), key[2] = ord_key(v.z), key[3] = ord_key(v.w);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        pos[e] = i + e, ok[e] = i + e < cap;
+}
+
 struct ListSrc {
     static constexpr bool kLds = true;
     const uint64_t *list;                          // 16-byte aligned

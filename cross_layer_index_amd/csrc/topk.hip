@@ -132,7 +132,8 @@ static_assert(kSplitSampleBlock % 4 == 0, "groups of four stay inside a sampled 
 
 // The sample's slots of this thread: geometry from `n_geo` (the longest row of
 // the call, known before the row's own length arrives), loads bounded by the
-// row's capacity `cap`; split_bound masks them by the row's length.
+// row's capacity `cap` (a multiple of 4, at least 4); split_bound masks them
+// by the row's length.
 template <int NT>
 struct SplitSample {
     static constexpr int G = kSplitSamples / (NT * 4);     // groups of four samples per thread
@@ -142,11 +143,10 @@ struct SplitSample {
     __device__ void load(const float *row, int64_t cap, int64_t n_geo)
     {
         const int64_t sb = (n_geo + kSplitSamples - 1) / kSplitSamples * kSplitSampleBlock;   // block spacing
-        const RowSrc src{row, cap};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t s = ((int64_t)threadIdx.x + (int64_t)NT * g) * 4;     // first sample slot
-            src.get4(s / kSplitSampleBlock * sb + s % kSplitSampleBlock, key[g], pos[g], ok[g]);
+            row_get4u(row, cap, s / kSplitSampleBlock * sb + s % kSplitSampleBlock, key[g], pos[g], ok[g]);
         }
     }
 };
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_collect_kernel(const float
     bool ok[kSplitRuns][4];
 #pragma unroll
     for (int r = 0; r < kSplitRuns; ++r)
-        RowSrc{row, ld}.get4(s + 4 * r, key[r], pos[r], ok[r]);
+        row_get4u(row, ld, s + 4 * r, key[r], pos[r], ok[r]);
     SplitSample<NT> sp;
     sp.load(row, ld, max_n);
     const int64_t nt = n[t];
@@ -754,15 +754,14 @@ hipError_t launch_topk_collect(const float *scores, int64_t ld, const int32_t *n
     const TopkLayout L = topk_layout(T, max_n);
     if (T == 0)
         return hipSuccess;
-    if (!L.split)
-        return hipErrorInvalidValue;
+    if (!L.split || ld < 4)
+        return hipErrorInvalidValue;              // (its loads need rows of at least 4 scores)
     char *base = static_cast<char *>(ws);
     if (!trace_skip("topk_collect_kernel"))
-        if (!trace_skip("topk_collect_kernel"))
-            hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream, scores,
-                       ld, n, max_n, k, reinterpret_cast<uint32_t *>(base + L.counts_off),
-                       reinterpret_cast<uint64_t *>(base + L.regions_off),
-                       reinterpret_cast<uint32_t *>(base + L.bounds_off));
+        hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream,
+                           scores, ld, n, max_n, k, reinterpret_cast<uint32_t *>(base + L.counts_off),
+                           reinterpret_cast<uint64_t *>(base + L.regions_off),
+                           reinterpret_cast<uint32_t *>(base + L.bounds_off));
     trace_launch(stream, "topk_collect_kernel");
     return hipGetLastError();
 }
@@ -806,7 +805,9 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n, int32_
         uint32_t *counts = reinterpret_cast<uint32_t *>(base + L.counts_off);
         uint64_t *regions = reinterpret_cast<uint64_t *>(base + L.regions_off);
         uint32_t *bounds = reinterpret_cast<uint32_t *>(base + L.bounds_off);
-        if (!trace_skip("topk_collect_kernel"))
+        // (ld < 4: every row is empty, the finishing kernel writes them
+        // without the collected keys; the collect kernel's loads need ld >= 4)
+        if (ld >= 4 && !trace_skip("topk_collect_kernel"))
             hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)L.P, (unsigned)T), dim3(kSplitThreads), 0, stream,
                            scores, ld, n, max_n, k, counts, regions, bounds);
         trace_launch(stream, "topk_collect_kernel");
