@@ -278,6 +278,12 @@ def mla_case(name):
         wl = W.scaled(W.WORKLOADS["decode_128k"], lengths=[5000])
         idx = rng.choice(5000, 2048, replace=False).astype(np.int32)[None]     # unsorted
         return wl, idx
+    if name == "decode_k8192":
+        # 8192 entries: 128 splits of 64 rows, so the combine takes its
+        # partials in several batches of loads
+        wl = W.scaled(W.WORKLOADS["decode_128k"], lengths=[10000], k=8192)
+        idx = rng.choice(10000, 8192, replace=False).astype(np.int32)[None]
+        return wl, idx
     if name == "batch_k64":
         wl = W.scaled(W.WORKLOADS["decode_128k"], T=8, k=64, lengths=[300, 64, 65, 1, 0, 100, 200, 90])
         idx = np.full((8, 64), -1, np.int32)
@@ -305,7 +311,7 @@ def mla_case(name):
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_split", "batch_k64", "padded_split", "many_queries"])
+@pytest.mark.parametrize("name", ["tiny", "decode_split", "decode_k8192", "batch_k64", "padded_split", "many_queries"])
 def test_sparse_mla_close(gpu, orc, name, mla_form):
     """fp32 output within 5e-3 of the fp64 oracle; the bf16 output of the same
     launch is its rounded image (and within 5e-3 where bf16 can be)."""
