@@ -253,6 +253,25 @@ def test_topk_exact(gpu, orc, name):
     check_topk_invariants(s, n, k, got)
 
 
+def test_topk_all_rows_empty_zero_stride(gpu):
+    """Split top-k over rows that hold no scores, with the zero row stride the
+    boundary allows then (ld = 0): the collection launch, whose loads need
+    rows of at least four scores, is skipped and every index row is all -1."""
+    import ctypes
+    T, k = 3, 16
+    buf = torch.zeros(16, dtype=torch.float32, device="cuda")       # never read
+    qs = gpu.make_queries(torch.zeros(T, dtype=torch.int64), torch.zeros(T, dtype=torch.int32), 0)
+    assert qs.max_n == 0
+    qc = qs.c()
+    need = gpu._lib.ic_topk_workspace_size(ctypes.byref(qc), k)
+    ws = gpu.workspace(need, buf.device)
+    idx = torch.full((T, k), 5, dtype=torch.int32, device="cuda")
+    gpu._check(gpu._lib.ic_topk(gpu._ptr(buf), 0, ctypes.byref(qc), k, gpu._ptr(idx), gpu._ptr(ws), ws.numel(),
+                                gpu._stream(None)))
+    torch.cuda.synchronize()
+    assert bool((idx == -1).all())
+
+
 # ---------------------------------------------------------------- sparse MLA --
 @pytest.fixture(params=["narrow", "wide"])
 def mla_form(request, monkeypatch):
