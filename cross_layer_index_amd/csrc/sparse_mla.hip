@@ -1291,6 +1291,7 @@ __global__ __launch_bounds__(64 * HPW) void mla_combine512_kernel(const uint16_t
                                                                   int32_t out_f32)
 {
     constexpr int DV = 512;
+    static_assert(kMaxSplits % CB == 0, "every batch of weights lies inside the array");
     __shared__ float wgt[HPW][2][kMaxSplits];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -1346,10 +1347,17 @@ __global__ __launch_bounds__(64 * HPW) void mla_combine512_kernel(const uint16_t
                 if (s0 + u < splits)
                     x[u] = p[(int64_t)(s0 + u) * stride];
         }
+        // the batch's weights in one go (inside the array whatever the split
+        // count: s0 + CB <= kMaxSplits), so the LDS reads are not waited for
+        // one by one behind the per-split branches
+        float wv4[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+            wv4[u] = wh[s0 + u];
 #pragma unroll
         for (int u = 0; u < CB; ++u)
             if (s0 + u < splits) {
-                const float wv = wh[s0 + u];
+                const float wv = wv4[u];
                 const uint32_t v4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1395,6 +1403,21 @@ __global__ __launch_bounds__(64) void mla_combine_wide_kernel(const uint16_t *__
     const int lane = threadIdx.x;
     const int hf = i >= NT / 2;
     const int64_t pr0 = (int64_t)t * splits * H;             // row of split 0, head 0
+    const uint4 *p = reinterpret_cast<const uint4 *>(part_o + (pr0 + 32 * wb) * DV) + (i * 2) * 64 + lane;
+    const int64_t stride = (int64_t)H * DV / 8;               // uint4s between splits
+    constexpr int CB = 8;                                     // splits in flight
+    uint4 x[CB][2];
+    auto load_batch = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+            if (s0 + u < splits) {
+                x[u][0] = p[(int64_t)(s0 + u) * stride];
+                x[u][1] = p[(int64_t)(s0 + u) * stride + 64];
+            }
+    };
+    // the first batch of partials does not depend on the weights: its loads
+    // go out first, so their round trip overlaps the (m, l) phase
+    load_batch(0);
     if (lane < 32) {
         // head 32 wb + lane: the maximum over the splits and the sink, then
         // the weights and the denominator
@@ -1417,22 +1440,14 @@ __global__ __launch_bounds__(64) void mla_combine_wide_kernel(const uint16_t *__
     __syncthreads();
     const int g = lane >> 5;
     auto head_of = [&](int r) { return 8 * (r >> 2) + 4 * g + (r & 3); };
-    const uint4 *p = reinterpret_cast<const uint4 *>(part_o + (pr0 + 32 * wb) * DV) + (i * 2) * 64 + lane;
-    const int64_t stride = (int64_t)H * DV / 8;               // uint4s between splits
     auto h2f = [](uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); };
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         acc[r] = 0.0f;
-    constexpr int CB = 8;                                     // splits in flight
     for (int s0 = 0; s0 < splits; s0 += CB) {
-        uint4 x[CB][2];
-#pragma unroll
-        for (int u = 0; u < CB; ++u)
-            if (s0 + u < splits) {
-                x[u][0] = p[(int64_t)(s0 + u) * stride];
-                x[u][1] = p[(int64_t)(s0 + u) * stride + 64];
-            }
+        if (s0 > 0)
+            load_batch(s0);
 #pragma unroll
         for (int u = 0; u < CB; ++u)
             if (s0 + u < splits) {
