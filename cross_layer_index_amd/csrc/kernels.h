@@ -100,6 +100,7 @@ struct MlaPlan {
     int32_t rows_per_split;  // multiple of the row tile
     size_t ws_bytes;         // partial results when splits > 1
     bool direct_parts;       // partials few enough to store straight from the registers
+    bool o_trans;            // narrow form: O held transposed (four value columns of one head per lane)
 };
 bool sparse_mla_supported(int32_t D_qk, int32_t D_v);
 // Largest index list one query may carry: the combine merges at most

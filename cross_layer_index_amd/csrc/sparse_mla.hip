@@ -89,6 +89,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Reductions over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48)
 // inside the VGPRs: v_permlane16_swap pairs rows (0,1) and (2,3),
@@ -182,7 +183,7 @@ struct SelArgs {
 };
 constexpr int kSelPerThread = 16;           // collected keys per thread (512 threads: 8192 per query)
 
-template <int DQK, int DV, bool SEL>
+template <int DQK, int DV, bool SEL, bool TR>
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const int64_t *__restrict__ base,
     const int32_t *__restrict__ n_valid, const int32_t *__restrict__ idx, int32_t k, int32_t H,
@@ -441,16 +442,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         // it by more than kSlack; tiles that do not raise any maximum skip the
         // O rescale.
         const bool grow = mt > m_run + kSlack;
-        float al[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        float alpha = 1.0f;                       // this lane's head hc
+        float al[4] = {1.0f, 1.0f, 1.0f, 1.0f};   // heads 4*g + r (O's rows, untransposed)
         const bool rescale = __any(grow);
         if (rescale) {
             const float m_new = grow ? mt : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
+            if constexpr (!TR) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                al[r] = __shfl(alpha, 4 * g + r);   // O rows are heads 4*g + r
+                for (int r = 0; r < 4; ++r)
+                    al[r] = __shfl(alpha, 4 * g + r);
+            }
         }
         float p[8];
 #pragma unroll
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             for (int i = 0; i < NTH; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    o[i][r] *= al[r];
+                    o[i][r] *= TR ? alpha : al[r];
         }
         // V operand by transposing reads of the row-major tile: per 16-lane
         // group, lane p addresses matrix row 16*b + 4*g + p/4 (tile row
@@ -489,7 +493,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
 #pragma unroll
             for (int i = 0; i < kPvBatch; ++i)
                 if (i0 + i < NTH)
-                    o[i0 + i] = mfma_bf16_16x16x32(pa, vb[i], o[i0 + i]);
+                    o[i0 + i] = TR ? mfma_bf16_16x16x32(vb[i], pa, o[i0 + i])
+                                   : mfma_bf16_16x16x32(pa, vb[i], o[i0 + i]);
         }
     };
 
@@ -558,6 +563,94 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
         softmax_pv(b == 0 ? tile0 : (b == 1 ? tile1 : tile2), last * kTile, sc0, sc1, last & 1);
     }
 
+    if constexpr (TR) {
+    // O is held transposed: element r of o[i] in lane (c, g) is value column
+    // 16*(nt0 + i) + 4*g + r of head hc, four consecutive columns per lane
+    auto pack_f16x4 = [](const f4 &v, float sc) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 x = {static_cast<_Float16>(v[0] * sc), static_cast<_Float16>(v[1] * sc),
+                      static_cast<_Float16>(v[2] * sc), static_cast<_Float16>(v[3] * sc)};
+        return __builtin_bit_cast(u32x2, x);
+    };
+    if (splits == 1) {
+        const float inv = 1.0f / l_run;           // the sink is in l_run
+        if (hc < H) {
+            const int64_t orow = ((int64_t)t * H + hc) * DV;
+#pragma unroll
+            for (int i = 0; i < NTH; ++i) {
+                const int v = 16 * (nt0 + i) + 4 * g;
+                if (out_f32)
+                    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + orow + v) =
+                        make_float4(o[i][0] * inv, o[i][1] * inv, o[i][2] * inv, o[i][3] * inv);
+                else
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(out) + orow + v) =
+                        make_uint2(pack_bf16x2(o[i][0] * inv, o[i][1] * inv), pack_bf16x2(o[i][2] * inv, o[i][3] * inv));
+            }
+        }
+    } else {
+        // The split's partial, normalised by its own denominator: a convex
+        // combination of value rows, stored as fp16 (2^-11 relative, finer
+        // than the bf16 output). Values are scaled by 2^-e per (head, half),
+        // e > 0 only when the half's largest magnitude reaches 2^14, so that
+        // none leaves the fp16 range; (m, l, e_half0, e_half1) go beside it.
+        // Partials go out with streaming stores: dirty L2 lines would
+        // otherwise be written back at the kernel boundary, on the critical
+        // path. A small set (direct_parts: one short round of workgroups,
+        // where the epilogue's latency counts) is stored from the registers,
+        // four columns to a store; a large one is first staged into whole rows.
+        const int64_t prow = ((int64_t)t * splits + split) * H;
+        const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NTH; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mx = fmaxf(mx, fabsf(o[i][r] * inv));
+        // the head's half spans the four 16-lane row groups; their maximum
+        // only where some value of the wave reaches the scaled range
+        // (otherwise every e is 0)
+        if (__any(!(mx < 16384.0f)))
+            mx = rows_max(mx);
+        const int e = mx >= 16384.0f ? ilogbf(mx) - 13 : 0;
+        const float scl = ldexpf(inv, -e);
+        if (g == 0 && hc < H)
+            part_ml[(prow + hc) * 4 + 2 + half] = (float)e;
+        if (direct_parts) {
+            // a small partial set: straight from the registers, 8 bytes a store
+            if (hc < H) {
+                u32x2 *po = reinterpret_cast<u32x2 *>(part_o + (prow + hc) * DV + 16 * nt0 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < NTH; ++i)
+                    __builtin_nontemporal_store(pack_f16x4(o[i], scl), po + 4 * i);
+            }
+        } else {
+            // A large one: the wave's 16 x DV/2 block goes through LDS (the tile
+            // buffers, free once every wave has left the tile loop) and leaves in
+            // whole rows, 16-byte stores, 32 lanes per 512-byte row.
+            constexpr int SROW = DV / 2 + 16;          // staging row stride (elements)
+            static_assert(4 * 16 * SROW <= TG::ELEMS, "staging fits a tile buffer");
+            lds_barrier();
+            uint16_t *stg = (half == 0 ? tile0 : tile1) + hgrp * 16 * SROW;
+#pragma unroll
+            for (int i = 0; i < NTH; ++i)
+                *reinterpret_cast<u32x2 *>(stg + c * SROW + 16 * i + 4 * g) = pack_f16x4(o[i], scl);
+            constexpr int RCH = DV / 16;               // 16-byte chunks per staged row
+#pragma unroll
+            for (int j = 0; j < DV / 64; ++j) {
+                const int q = lane + 64 * j;
+                const int row = q / RCH, ch = q - row * RCH;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + row * SROW + 8 * ch);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(part_o + (prow + h0 + row) * DV + (DV / 2) * half + 8 * ch);
+                if (h0 + row < H)
+                    __builtin_nontemporal_store(v, dst);
+            }
+        }
+        if (half == 0 && g == 0 && hc < H) {
+            part_ml[(prow + hc) * 4 + 0] = m_run;
+            part_ml[(prow + hc) * 4 + 1] = l_run;
+        }
+    }
+    } else {
     if (splits == 1) {
         float inv[4];
 #pragma unroll
@@ -663,6 +756,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(
             part_ml[(prow + hc) * 4 + 0] = m_run;
             part_ml[(prow + hc) * 4 + 1] = l_run;
         }
+    }
     }
 }
 
@@ -1513,9 +1607,15 @@ hipError_t launch_shape(const uint16_t *q, const uint16_t *kv, const int64_t *ba
                            stream, q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split,
                            plan.splits, out, out_f32, part_o, part_ml, n_units);
     } else {
-        hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, SEL>), dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream,
-                           q, kv, base, n_valid, idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits,
-                           out, out_f32, part_o, part_ml, (int32_t)plan.direct_parts, sa);
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(plan.splits * hg * T), dim3(kMlaThreads), 0, stream, q, kv, base, n_valid,
+                               idx, k, H, sink, scale * kLog2e, plan.rows_per_split, plan.splits, out, out_f32, part_o,
+                               part_ml, (int32_t)plan.direct_parts, sa);
+        };
+        if (plan.o_trans)
+            go(sparse_mla_kernel<DQK, DV, SEL, true>);
+        else
+            go(sparse_mla_kernel<DQK, DV, SEL, false>);
     }
     trace_launch(stream, SEL ? "sparse_mla_kernel<selecting>" : "sparse_mla_kernel");
     hipError_t e = hipGetLastError();
@@ -1613,6 +1713,15 @@ MlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t k, int32_t D_v)
     p.rows_per_split = (int32_t)rps;
     p.ws_bytes = s > 1 ? (size_t)T * s * H * ((size_t)D_v * 2 + 4 * sizeof(float)) : 0;
     p.direct_parts = p.ws_bytes <= kDirectPartsMax;
+    // The narrow form holds O transposed where its partials are staged
+    // through LDS (one 8-byte write per value tile instead of four 2-byte
+    // ones: stack_78 2.28 -> 2.19 ms); small sets stored straight from the
+    // registers keep the untransposed layout, whose 2-byte stores drain
+    // sooner (decode 36.2 us transposed, 34.7 us not). IC_MLA_OTRANS=0|1
+    // overrides (both layouts stay testable on every path).
+    p.o_trans = p.splits > 1 && !p.direct_parts;
+    if (const char *f = getenv("IC_MLA_OTRANS"))
+        p.o_trans = !strcmp(f, "1");
     return p;
 }
 

@@ -281,6 +281,17 @@ def mla_form(request, monkeypatch):
     return request.param
 
 
+@pytest.fixture(params=["0", "1"])
+def o_layout(request, monkeypatch, mla_form):
+    """Both layouts of the narrow form's O accumulators (untransposed: four
+    heads of one value column per lane; transposed: four value columns of one
+    head), forced on every path whatever the plan would pick."""
+    if mla_form == "wide" and request.param == "1":
+        pytest.skip("the layout is the narrow form's")
+    monkeypatch.setenv("IC_MLA_OTRANS", request.param)
+    return request.param
+
+
 def needs_form(form, H):
     if form == "wide" and H % 128:
         pytest.skip("the wide form takes whole groups of 128 heads")
@@ -331,7 +342,7 @@ def mla_case(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_split", "decode_k8192", "batch_k64", "padded_split", "many_queries"])
-def test_sparse_mla_close(gpu, orc, name, mla_form):
+def test_sparse_mla_close(gpu, orc, name, mla_form, o_layout):
     """fp32 output within 5e-3 of the fp64 oracle; the bf16 output of the same
     launch is its rounded image (and within 5e-3 where bf16 can be)."""
     wl, idx = mla_case(name)
@@ -343,13 +354,13 @@ def test_sparse_mla_close(gpu, orc, name, mla_form):
     ref = orc.sparse_mla(li.q, li.kv, wl.base(), idx, li.sink, wl.scale, wl.D_v)
     f32 = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v, out_f32=True).cpu().numpy()
     b16 = gpu.sparse_mla(d.q, d.kv, qs, i, d.sink, wl.scale, wl.D_v).float().cpu().numpy()
-    assert_close(f32, ref, f"sparse MLA {name} {mla_form} [fp32]")
+    assert_close(f32, ref, f"sparse MLA {name} {mla_form}/o{o_layout} [fp32]")
     assert_bf16_output(b16, f32, ref, f"sparse MLA {name} {mla_form}")
     for got in (f32, b16):
         assert np.all(got[idx.max(1) < 0] == 0)                                  # empty rows are zero
 
 
-def test_sparse_mla_large_values(gpu, orc, mla_form):
+def test_sparse_mla_large_values(gpu, orc, mla_form, o_layout):
     """Latent rows scaled by 1e5 (and q by 1e-5, so the scores stay as they
     were): the split partials, stored in fp16 with a per-(head, half)
     power-of-two scale, must stay in range; the fp32 output holds the bar
@@ -373,7 +384,7 @@ def test_sparse_mla_large_values(gpu, orc, mla_form):
 
 
 @pytest.mark.parametrize("name", ["decode_split", "many_queries"])
-def test_sparse_mla_logit_range(gpu, orc, name, mla_form):
+def test_sparse_mla_logit_range(gpu, orc, name, mla_form, o_layout):
     """q scaled by a power of two until the logits of a head spread over
     hundreds of units: later rows then beat the first rows' maximum by far
     (the narrow form rescales its sums; the wide form, whose probabilities
@@ -394,7 +405,7 @@ def test_sparse_mla_logit_range(gpu, orc, name, mla_form):
     f32 = gpu.sparse_mla(q.cuda(), li.kv.cuda(), qs, i, li.sink.cuda(), wl.scale, wl.D_v,
                          out_f32=True).cpu().numpy()
     assert np.isfinite(f32).all()
-    assert_close(f32, ref, f"sparse MLA {name} {mla_form} logits x{f:g} [fp32]")
+    assert_close(f32, ref, f"sparse MLA {name} {mla_form}/o{o_layout} logits x{f:g} [fp32]")
 
 
 def test_sparse_mla_deterministic(gpu, mla_form):
@@ -467,7 +478,7 @@ def run_stack(ic, wl, layers_dev, rmap, out_f32=False):
 
 @pytest.mark.parametrize("case", ["tiny", "small_5layer", "every6_13layer", "first_only_4layer", "ties_3layer",
                                   "clustered_2layer"])
-def test_layer_stack_small(gpu, orc, case, mla_form):
+def test_layer_stack_small(gpu, orc, case, mla_form, o_layout):
     if case == "tiny":
         wl = W.WORKLOADS["tiny_2layer"]
     elif case == "clustered_2layer":
@@ -508,7 +519,7 @@ def test_layer_stack_small(gpu, orc, case, mla_form):
     for l in range(wl.n_layers):
         got_idx = cache[slots[rmap[l]]].cpu().numpy()
         assert np.array_equal(got_idx, r_index[l])
-        assert_close(outs[l].cpu().numpy(), r_outs[l], f"layer stack {case} {mla_form} layer {l} [fp32]")
+        assert_close(outs[l].cpu().numpy(), r_outs[l], f"layer stack {case} {mla_form}/o{o_layout} layer {l} [fp32]")
 
 
 def test_sparse_mla_odd_k_steps_after_graph_replays(gpu, orc, monkeypatch):
