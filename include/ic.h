@@ -135,7 +135,9 @@ ic_status ic_topk(const float *scores, int64_t ld, const ic_queries *qs, int32_t
  * denominators sum the rounded values. Two kernel forms (64 heads per
  * workgroup, or 128 for large grids with D_v = 512 and H a multiple of 128)
  * are chosen by size; IC_MLA_FORM=narrow|wide in the environment overrides
- * the choice. Long rows are split over workgroups whose partials a second
+ * the choice, and IC_MLA_OTRANS=0|1 the accumulator layout of the narrow form
+ * (chosen by how its partials are stored; the results are the same within the
+ * stated bound). Long rows are split over workgroups whose partials a second
  * kernel merges (the workspace holds them). */
 size_t ic_sparse_mla_workspace_size(const ic_queries *qs, const ic_dims *d);
 ic_status ic_sparse_mla(const uint16_t *q, const uint16_t *kv, const ic_queries *qs,
