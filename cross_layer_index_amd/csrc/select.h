@@ -508,28 +508,64 @@ struct SplitSel {
             select_emit<NT, LB>(row, sh, 0, 0u, 0u, (uint32_t)k, k, in_split);
             return;
         }
-        if (cnt[P] != 0) {
+        uint32_t valid = 0;
+        if (__builtin_expect(cnt[P] != 0, 0)) {
             uint32_t *off = cnt + P + 1 + R * NT / 64;
             if (tid < P)
                 off[tid + 1] = incl;
             if (tid == 0)
                 off[0] = 0u;
             wg_barrier<LB>();
-            select_emit<NT, LB>(SliceSrc{reg, stride, off, P, (int64_t)total}, sh, 0, 0u, 0u, (uint32_t)k, k,
-                                in_split);
-            return;
-        }
-        // which entries hold keys (a group of four lies in one slice)
-        uint32_t valid = 0;
+            if (total > (uint32_t)(NT * E)) {
+                // more keys than the registers hold: digit passes over the
+                // slices in global memory
+                select_emit<NT, LB>(SliceSrc{reg, stride, off, P, (int64_t)total}, sh, 0, 0u, 0u, (uint32_t)k, k,
+                                    in_split);
+                return;
+            }
+            // A slice holds more than its share, but every key fits the
+            // registers: reload them by their rank in the concatenated slices
+            // (position order; rank f in register 4r + e of thread
+            // (f / 4) % NT, as below) and go on in registers. A group's first
+            // rank finds its slice by a binary search over the offsets, the
+            // next three step forward from it; ranks past the last key read
+            // the last key again, so every load is unconditional.
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t f = (uint32_t)(NT * 4 * r) + 4u * tid;
-            const uint32_t sl = f / C, j = f - sl * C;
-            const uint32_t have = sl < (uint32_t)P ? cnt[sl] : 0u;
+            for (int r = 0; r < R; ++r) {
+                const uint32_t f0 = min((uint32_t)(NT * 4 * r) + 4u * tid, total - 1u);
+                int lo = 0, hi = P - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (off[mid] <= f0)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (j + e < have)
-                    valid |= 1u << (4 * r + e);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t f = (uint32_t)(NT * 4 * r) + 4u * tid + (uint32_t)e;
+                    const uint32_t fc = min(f, total - 1u);
+                    while (lo + 1 < P && off[lo + 1] <= fc)
+                        ++lo;
+                    const uint64_t v = reg[(int64_t)lo * stride + (fc - off[lo])];
+                    key[4 * r + e] = (uint32_t)(v >> 32);
+                    pos[4 * r + e] = (uint32_t)v;
+                    if (f < total)
+                        valid |= 1u << (4 * r + e);
+                }
+            }
+        } else {
+            // which entries hold keys (a group of four lies in one slice)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t f = (uint32_t)(NT * 4 * r) + 4u * tid;
+                const uint32_t sl = f / C, j = f - sl * C;
+                const uint32_t have = sl < (uint32_t)P ? cnt[sl] : 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < have)
+                        valid |= 1u << (4 * r + e);
+            }
         }
         // the keys' top 22 bits relative to the bound's, the last bin taking
         // everything from 2047 up (the same pass as the finishing kernel's)

@@ -113,8 +113,9 @@ def test_decode_128k_full(gpu, orc):
 
 def test_decode_128k_recency_full(gpu, orc):
     """Scores rising with position: the top-k lies in the row's last chunks,
-    so a slice of the split top-k holds more keys than the selecting sparse
-    MLA keeps in registers and the selection runs over the slices."""
+    so a slice of the split top-k holds more keys than its share of the
+    selecting sparse MLA's registers and the keys are reloaded by their rank
+    over the slices."""
     wl = W.WORKLOADS["decode_128k_recency"]
     run_case(gpu, orc, wl, [0], device_gen=False)
 

@@ -486,12 +486,13 @@ def test_layer_stack_small(gpu, orc, case, mla_form, o_layout):
         # query's heads: those positions tie above every other score and all
         # fall in the first chunk of the split path, more than a workgroup's
         # share of one slice when the sparse MLA selects its own rows (then
-        # the selection runs over the whole row)
+        # the keys are reloaded into registers by their rank over the slices)
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=2, full_layers=[0], T=1, lengths=[20000])
     elif case == "ties_3layer":
         # every key row equal: a query's scores all tie, every key reaches the
         # bound and the lowest positions win (past 8192 keys the selection
-        # runs over the whole row; at 5000 the ties resolve from the list)
+        # runs over the slices in memory; at 5000 they are reloaded into
+        # registers by rank)
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=3, full_layers=[0, 2], T=3, lengths=[20000, 5000, 2049])
     elif case == "small_5layer":
         wl = W.scaled(W.WORKLOADS["decode_128k"], n_layers=5, full_layers=[0, 3], T=3, lengths=[3000, 2048, 100])
